@@ -1,0 +1,177 @@
+"""fp64 CPU oracle for row-wise softmax -- TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, the smoke check and the benchmark's CPU-baseline leg
+import this package.  The product path (``row_wise_online_amd``) never does.
+
+This module is a ctypes wrapper around ``liboracle.so`` (built from
+``oracle.c`` by ``oracle/build.py``) plus the comparison helpers the parity
+tests use.  See ``oracle.c`` for the cited definitions.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+F32 = 0
+BF16 = 1
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            from . import build as _b
+            _b.build()
+        lib = ctypes.CDLL(_LIB_PATH)
+        vp, i64, i32, dp = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                            ctypes.c_void_p)
+        lib.oracle_softmax.argtypes = [vp, i64, i64, i64, i32, dp, dp, dp, dp]
+        lib.oracle_softmax.restype = i32
+        lib.oracle_state.argtypes = [vp, i64, i64, i64, i32, dp, dp]
+        lib.oracle_state.restype = i32
+        lib.oracle_merge2.argtypes = [ctypes.c_double] * 4 + [
+            ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)]
+        lib.oracle_merge2.restype = None
+        lib.oracle_merge.argtypes = [dp, dp, i64, i64, i64, dp, dp, dp]
+        lib.oracle_merge.restype = i32
+        _lib = lib
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def _as_input(x):
+    """Return (array, dtype code).  fp32 arrays are fp32; bf16 inputs are
+    uint16 arrays holding the raw bf16 bit patterns."""
+    x = np.asarray(x)
+    if x.dtype == np.float32:
+        code = F32
+    elif x.dtype == np.uint16:
+        code = BF16
+    else:
+        raise TypeError("oracle input must be float32 or uint16 (bf16 bits)")
+    if x.ndim == 1:
+        x = x[None, :]
+    if x.ndim != 2 or x.strides[1] != x.itemsize:
+        raise ValueError("oracle input must be a 2-D array with unit column stride")
+    if x.strides[0] % x.itemsize:
+        raise ValueError("row stride must be a whole number of elements")
+    return x, code
+
+
+def softmax(x, want_y=True):
+    """Three-pass fp64 safe softmax of every row of ``x``.
+
+    Returns (y [M,N] fp64 or None, m [M], d [M], lse [M])."""
+    x, code = _as_input(x)
+    M, N = x.shape
+    ld = x.strides[0] // x.itemsize
+    y = np.empty((M, N), np.float64) if want_y else None
+    m = np.empty(M, np.float64)
+    d = np.empty(M, np.float64)
+    lse = np.empty(M, np.float64)
+    rc = _load().oracle_softmax(_ptr(x), ld, M, N, code, _ptr(y), _ptr(m),
+                                _ptr(d), _ptr(lse))
+    if rc != 0:
+        raise ValueError("oracle_softmax rejected its arguments")
+    return y, m, d, lse
+
+
+def state(x):
+    """The element-by-element online (m, d) fold of every row of ``x``."""
+    x, code = _as_input(x)
+    M, N = x.shape
+    ld = x.strides[0] // x.itemsize
+    m = np.empty(M, np.float64)
+    d = np.empty(M, np.float64)
+    rc = _load().oracle_state(_ptr(x), ld, M, N, code, _ptr(m), _ptr(d))
+    if rc != 0:
+        raise ValueError("oracle_state rejected its arguments")
+    return m, d
+
+
+def merge2(a, b):
+    """Merge two states a = (m_a, d_a), b = (m_b, d_b)."""
+    m = ctypes.c_double()
+    d = ctypes.c_double()
+    _load().oracle_merge2(float(a[0]), float(a[1]), float(b[0]), float(b[1]),
+                          ctypes.byref(m), ctypes.byref(d))
+    return m.value, d.value
+
+
+def merge(m_in, d_in):
+    """Left-fold merge of the K states of each row: m_in, d_in are [M,K]
+    (any float dtype; widened to fp64).  Returns (m, d, lse) fp64 [M]."""
+    m_in = np.ascontiguousarray(m_in, dtype=np.float64)
+    d_in = np.ascontiguousarray(d_in, dtype=np.float64)
+    if m_in.ndim == 1:
+        m_in, d_in = m_in[None, :], d_in[None, :]
+    M, K = m_in.shape
+    m = np.empty(M, np.float64)
+    d = np.empty(M, np.float64)
+    lse = np.empty(M, np.float64)
+    rc = _load().oracle_merge(_ptr(m_in), _ptr(d_in), K, M, K, _ptr(m),
+                              _ptr(d), _ptr(lse))
+    if rc != 0:
+        raise ValueError("oracle_merge rejected its arguments")
+    return m, d, lse
+
+
+# ---------------------------------------------------------------------------
+# Comparison helpers used by the parity tests.  They compare a result against
+# fp64 oracle values; they never compute a softmax themselves.
+# ---------------------------------------------------------------------------
+
+def bf16_bits_to_f64(bits):
+    """Exact widening of raw bf16 bit patterns (uint16) to fp64."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return b.view(np.float32).astype(np.float64)
+
+
+def round_f64_to_bf16_bits(v):
+    """Round fp64 values to the nearest bf16 (ties to even), returning raw
+    uint16 bit patterns.  Rounding is done once, directly from fp64 (no
+    intermediate fp32 rounding).  Finite values only; NaN maps to a quiet
+    NaN pattern and values beyond the bf16 range to +-inf."""
+    v = np.asarray(v, dtype=np.float64)
+    out = np.empty(v.shape, np.uint16)
+    flat_v = v.ravel()
+    flat_o = out.ravel()
+    sign = np.signbit(flat_v)
+    a = np.abs(flat_v)
+    nan = np.isnan(flat_v)
+    # bf16: 8 significant bits, min normal 2^-126, subnormal quantum 2^-133
+    _, e = np.frexp(np.where(a > 0, a, 1.0))    # a = f * 2^e, f in [0.5, 1)
+    e = np.maximum(e, -125)                      # subnormal range: fixed quantum
+    quantum = np.ldexp(1.0, e - 8)
+    q = np.rint(a / quantum) * quantum           # exact in fp64; rint is RNE
+    q32 = q.astype(np.float32)                   # exact: q has <= 8 bits
+    bits = (q32.view(np.uint32) >> 16).astype(np.uint16)
+    bits = np.where(q > 3.3895313892515355e38, np.uint16(0x7F80), bits)
+    bits = np.where(sign, bits | np.uint16(0x8000), bits)
+    bits = np.where(nan, np.uint16(0x7FC0), bits)
+    flat_o[:] = bits
+    return out
+
+
+def bf16_ulp_distance(a_bits, b_bits):
+    """Distance in representable bf16 steps between two raw bf16 patterns
+    (ordered-integer distance; +0 and -0 are the same point)."""
+    def ordered(b):
+        b = np.asarray(b, dtype=np.uint16).astype(np.int32)
+        mag = b & 0x7FFF
+        return np.where(b & 0x8000, -mag, mag)
+    return np.abs(ordered(a_bits) - ordered(b_bits))
+
+
+def f32_ulp(v):
+    """The fp32 unit in the last place at |v| (spacing to the next float)."""
+    v = np.abs(np.asarray(v, dtype=np.float32))
+    return np.spacing(v).astype(np.float64)

@@ -1,0 +1,181 @@
+/*
+ * Plain fp64 CPU oracle for row-wise softmax, its online (m, d) state and
+ * the state merge.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product library links, loads or
+ * calls this file; only the test suite, the smoke check and the benchmark's
+ * CPU-baseline leg use it.  It shares no code, header, table or constant
+ * with the HIP library: it has its own dtype codes and its own bf16 widening.
+ *
+ * Everything here is deliberately slow and literal: one row at a time, one
+ * element at a time, fp64 accumulation, libm exp/log, true division, no
+ * blocking, no reordering beyond what each cited definition states.  Build
+ * with -ffp-contract=off so that every expression rounds as written.
+ *
+ * Sources (the pages this implements):
+ *  [P1] "5.2 CUDA Online Softmax 实现优化" (AIInfraGuide): §1.1 three-pass
+ *       safe softmax; §2.1 the running-state recurrence and its derivation;
+ *       §2.2 the two-pass pseudo-code; §2.3 stability; §4.1 the merge of two
+ *       partial states.
+ *  [P3] "从原始Softmax到在线Softmax": section on deriving the stable form, which
+ *       defines log-sum-exp LSE = m + log sum e^(z-m).
+ *  [P4] "Softmax 数值稳定性与 IO-Aware Attention：从在线归一化到 FlashAttention":
+ *       §3 (three passes), §4 (running state), §4.1 (merge of two states,
+ *       associativity, the random-chunking check).
+ *  [P5] "FlashAttention：为什么加速推理的同时还能节省显存": the 3-pass
+ *       safe_softmax and the 2-pass online_safe_softmax listings (used as a
+ *       description of what is computed, not copied).
+ *
+ * Readings where the pages are silent (each also listed in the design notes):
+ *  - An element equal to -inf has weight e^(-inf) = 0; it changes neither
+ *    the max of a row that has a larger element nor the sum.  A row whose
+ *    elements are all -inf therefore has m = -inf, d = 0, LSE = -inf and
+ *    y = 0/0 = NaN.  The state (-inf, 0) is the identity of the merge: the
+ *    merge formula would produce 0 * e^(NaN) for two such states, so the
+ *    merge returns the identity directly when both maxima are -inf.
+ *  - The max ignores NaN (a NaN never compares greater); a NaN element makes
+ *    its term e^(NaN - m) = NaN, so d, y and LSE of that row are NaN.
+ *  - A +inf element makes m = +inf and its term e^(inf - inf) = NaN, so the
+ *    row is NaN (as for a NaN element).
+ *
+ * Parity pins for every function are in the test suite; none is unpinned.
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "oracle.h"
+
+/* ---- ingest: read one stored element exactly ------------------------------
+ * fp32 -> fp64 is exact.  A bf16 value is the upper 16 bits of the fp32 with
+ * the same sign and exponent, so widening is a 16-bit left shift (exact). */
+static double load_elem(const void *x, int dtype, int64_t idx)
+{
+    if (dtype == ORACLE_F32) {
+        return (double)((const float *)x)[idx];
+    } else {
+        uint32_t bits = (uint32_t)((const uint16_t *)x)[idx] << 16;
+        float f;
+        memcpy(&f, &bits, sizeof f);
+        return (double)f;
+    }
+}
+
+static int check_args(const void *x, int64_t ld, int64_t M, int64_t N, int dtype)
+{
+    if (M < 0 || N < 1) return ORACLE_EINVAL;
+    if (ld < N) return ORACLE_EINVAL;
+    if (dtype != ORACLE_F32 && dtype != ORACLE_BF16) return ORACLE_EINVAL;
+    if (M > 0 && x == NULL) return ORACLE_EINVAL;
+    return ORACLE_OK;
+}
+
+/* ---- the definition: three-pass safe softmax ------------------------------
+ * [P1] §1.1 and [P4] §3: m = max_j x_j, d = sum_j e^(x_j - m),
+ * y_j = e^(x_j - m) / d.  [P3] stable-form section: LSE = m + log d.
+ * Each pass is a separate loop over the row, in index order. */
+int oracle_softmax(const void *x, int64_t ld, int64_t M, int64_t N, int dtype,
+                   double *y, double *m_out, double *d_out, double *lse_out)
+{
+    int rc = check_args(x, ld, M, N, dtype);
+    if (rc != ORACLE_OK) return rc;
+    for (int64_t i = 0; i < M; ++i) {
+        const int64_t base = i * ld;
+
+        /* pass 1: the row max (NaN never compares greater, so it is skipped) */
+        double m = -INFINITY;
+        for (int64_t j = 0; j < N; ++j) {
+            double v = load_elem(x, dtype, base + j);
+            if (v > m) m = v;
+        }
+
+        /* pass 2: the sum of e^(x - m); a -inf element has weight 0 */
+        double d = 0.0;
+        for (int64_t j = 0; j < N; ++j) {
+            double v = load_elem(x, dtype, base + j);
+            double t = (v == -INFINITY) ? 0.0 : exp(v - m);
+            d = d + t;
+        }
+
+        /* pass 3: normalise with a true division */
+        if (y != NULL) {
+            for (int64_t j = 0; j < N; ++j) {
+                double v = load_elem(x, dtype, base + j);
+                double t = (v == -INFINITY) ? 0.0 : exp(v - m);
+                y[i * N + j] = t / d;
+            }
+        }
+        if (m_out) m_out[i] = m;
+        if (d_out) d_out[i] = d;
+        if (lse_out) lse_out[i] = m + log(d);
+    }
+    return ORACLE_OK;
+}
+
+/* ---- the merge of two partial states --------------------------------------
+ * [P1] §4.1 and [P4] §4.1: m = max(m_a, m_b),
+ * d = d_a e^(m_a - m) + d_b e^(m_b - m).  (-inf, 0) is the identity. */
+void oracle_merge2(double ma, double da, double mb, double db,
+                   double *m_out, double *d_out)
+{
+    double m = (mb > ma) ? mb : ma;
+    if (m == -INFINITY) {
+        /* both operands have max -inf: the sum of their weights is da + db
+         * (0 for identities, NaN if a NaN was folded in) */
+        *m_out = -INFINITY;
+        *d_out = da + db;
+        return;
+    }
+    *m_out = m;
+    *d_out = da * exp(ma - m) + db * exp(mb - m);
+}
+
+/* ---- the method's running state: one element at a time ---------------------
+ * [P1] §2.1/§2.2, [P4] §4, [P5] 2-pass listing: start from (-inf, 0); for
+ * each element x: m' = max(m, x), d = d e^(m - m') + e^(x - m'), m = m'.
+ * When the max does not change the correction factor is e^0 = 1 exactly
+ * ([P1] §2.1 remark), which also keeps (-inf, 0) intact.  A -inf element
+ * has zero weight and leaves the state unchanged. */
+int oracle_state(const void *x, int64_t ld, int64_t M, int64_t N, int dtype,
+                 double *m_out, double *d_out)
+{
+    int rc = check_args(x, ld, M, N, dtype);
+    if (rc != ORACLE_OK) return rc;
+    for (int64_t i = 0; i < M; ++i) {
+        double m = -INFINITY, d = 0.0;
+        for (int64_t j = 0; j < N; ++j) {
+            double v = load_elem(x, dtype, i * ld + j);
+            if (v == -INFINITY) continue;
+            double m_new = (v > m) ? v : m;
+            double corr = (m_new == m) ? 1.0 : exp(m - m_new);
+            d = d * corr + exp(v - m_new);
+            m = m_new;
+        }
+        if (m_out) m_out[i] = m;
+        if (d_out) d_out[i] = d;
+    }
+    return ORACLE_OK;
+}
+
+/* ---- the merge of K states per row (left fold of oracle_merge2) -----------
+ * Row i holds K states at m_in[i*ld + k], d_in[i*ld + k].  The fold starts
+ * from the identity and merges k = 0, 1, ..., K-1 in order ([P4] §4.1:
+ * merge repeatedly; the result does not depend on the grouping in exact
+ * arithmetic).  LSE = m + log d as in [P3]. */
+int oracle_merge(const double *m_in, const double *d_in, int64_t ld,
+                 int64_t M, int64_t K, double *m_out, double *d_out,
+                 double *lse_out)
+{
+    if (M < 0 || K < 1 || ld < K) return ORACLE_EINVAL;
+    if (M > 0 && (m_in == NULL || d_in == NULL)) return ORACLE_EINVAL;
+    for (int64_t i = 0; i < M; ++i) {
+        double m = -INFINITY, d = 0.0;
+        for (int64_t k = 0; k < K; ++k)
+            oracle_merge2(m, d, m_in[i * ld + k], d_in[i * ld + k], &m, &d);
+        if (m_out) m_out[i] = m;
+        if (d_out) d_out[i] = d;
+        if (lse_out) lse_out[i] = m + log(d);
+    }
+    return ORACLE_OK;
+}

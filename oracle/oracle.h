@@ -1,0 +1,38 @@
+/*
+ * fp64 CPU oracle -- TEST INFRASTRUCTURE ONLY (see oracle.c).
+ * Own dtype codes and status codes; nothing here is shared with the library.
+ */
+#ifndef ROW_SOFTMAX_ORACLE_H
+#define ROW_SOFTMAX_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { ORACLE_F32 = 0, ORACLE_BF16 = 1 };
+enum { ORACLE_OK = 0, ORACLE_EINVAL = 1 };
+
+/* Three-pass safe softmax of each of the M rows of x (row stride ld
+ * elements, N columns).  y (nullable) is dense fp64 [M][N]; m, d, lse
+ * (each nullable) are fp64 [M]. */
+int oracle_softmax(const void *x, int64_t ld, int64_t M, int64_t N, int dtype,
+                   double *y, double *m, double *d, double *lse);
+
+/* The online recurrence, element by element, per row: (m, d) fp64 [M]. */
+int oracle_state(const void *x, int64_t ld, int64_t M, int64_t N, int dtype,
+                 double *m, double *d);
+
+/* Merge of two states with the (-inf, 0) identity. */
+void oracle_merge2(double ma, double da, double mb, double db,
+                   double *m, double *d);
+
+/* Left-fold merge of K states per row (row stride ld). */
+int oracle_merge(const double *m_in, const double *d_in, int64_t ld,
+                 int64_t M, int64_t K, double *m, double *d, double *lse);
+
+#ifdef __cplusplus
+}
+#endif
+#endif
