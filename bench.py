@@ -1,0 +1,252 @@
+#!/usr/bin/env python3
+"""Throughput of the row-wise online softmax forward on one MI355X.
+
+A step is one ``os_softmax_fwd`` call (the whole hot path: pass 1, the
+state merges, pass 2) over one seeded synthetic input already resident in
+HBM.  Inputs rotate over enough buffer sets (>= 1 GiB) that every step reads
+from HBM rather than from the 256 MB Infinity Cache.  The timed region is
+bracketed by device synchronisation and HIP events on the stream the
+kernels are launched on.
+
+Prints one JSON line on stdout (rank 0, N = 1).  ``value`` is algorithmic
+GB/s: the bytes the path must move (x read once per read pass, y written
+once, row statistics written) divided by the step time.
+
+``--all`` also prints one JSON line per workload to stderr.
+"""
+import argparse
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = ("achieved HBM GB/s (% of peak) + rows/s, online softmax fwd fp32 "
+          "4096×4096")
+PEAK_GBS = 8000.0           # MI355X HBM3E, published peak
+ROTATE_BYTES = 1 << 30      # rotating working set, 4x the Infinity Cache
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "row_wise_online_amd",
+                                           "csrc", "*"))):
+        with open(p, "rb") as f:
+            h.update(os.path.basename(p).encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(w, path, n_stats):
+    """Bytes the path must move for one step of workload w."""
+    import row_wise_online_amd as rw
+    xy = w.M * w.N * w.esize
+    reads = 1 if path == "resident" else 2
+    b = reads * xy + xy + 4 * w.M * n_stats
+    if path == "split":
+        b += 2 * rw.workspace_bytes(w.M, w.N, w.dtype, "split")  # states w+r
+    return b
+
+
+def measure(w, steps, warmup, path="auto", rotate=True):
+    import torch
+    import row_wise_online_amd as rw
+    from row_wise_online_amd import workloads as wl
+
+    x_host = wl.generate(w.name)
+    tdt = torch.float32 if w.dtype == "f32" else torch.bfloat16
+    if w.dtype == "f32":
+        x0 = torch.from_numpy(x_host).cuda()
+    else:
+        import numpy as np
+        x0 = torch.from_numpy(x_host.view(np.int16)).view(tdt).cuda()
+    per_set = 2 * w.M * w.N * w.esize
+    R = max(2, -(-ROTATE_BYTES // per_set)) if rotate else 1
+    xs = [x0] + [x0.clone() for _ in range(R - 1)]
+    ys = [torch.empty_like(x0) for _ in range(R)]
+    want = set(w.outputs)
+    stat = lambda k: torch.empty(w.M, device="cuda") if k in want else None
+    m, d, lse = stat("m"), stat("d"), stat("lse")
+    ws_bytes = rw.workspace_bytes(w.M, w.N, w.dtype, path)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+
+    def step(i):
+        rw.softmax_fwd(xs[i % R], ys[i % R], m=m, d=d, lse=lse, ws=ws,
+                       path=path)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        step(i)
+    end.record()
+    end.synchronize()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    del xs, ys
+    return ms, R
+
+
+def copy_ceiling(nbytes, steps=50):
+    """GB/s of a plain device copy of nbytes (read + write), rotating."""
+    import torch
+    n = nbytes // 4
+    R = max(2, -(-ROTATE_BYTES // (2 * nbytes)))
+    src = [torch.ones(n, device="cuda") for _ in range(R)]
+    dst = [torch.empty(n, device="cuda") for _ in range(R)]
+    for i in range(5):
+        dst[i % R].copy_(src[i % R])
+    torch.cuda.synchronize()
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    s.record()
+    for i in range(steps):
+        dst[i % R].copy_(src[i % R])
+    e.record()
+    e.synchronize()
+    ms = s.elapsed_time(e) / steps
+    return 2 * nbytes / (ms * 1e-3) / 1e9
+
+
+def cpu_baseline(w, n_stats, budget_s):
+    """The fp64 oracle, as it is, on this host: whole input matrices of the
+    workload, repeated until about budget_s seconds have passed."""
+    import oracle
+    from row_wise_online_amd import workloads as wl
+    x = wl.generate(w.name)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.softmax(x)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or reps >= 64:
+            break
+    per = el / reps
+    b = 2 * w.M * w.N * w.esize + 4 * w.M * n_stats
+    return {"value": round(b / per / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "rows_per_s": round(w.M / per, 1),
+            "sample": f"{reps} x full {w.M}x{w.N} {w.dtype} matrix, fp64 "
+                      f"three-pass oracle (y, m, d, lse), 1 thread, "
+                      f"{el:.1f} s"}
+
+
+def traffic_record(workload):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they
+    were taken on the current kernel sources."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        rec = json.load(f).get(workload)
+    if not rec or rec.get("kernel_hash") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def run_workload(name, steps, warmup, path="auto", want_cpu=True,
+                 cpu_budget=10.0):
+    import row_wise_online_amd as rw
+    from row_wise_online_amd import workloads as wl
+    w = wl.WORKLOADS[name]
+    resolved = rw.select_path(w.M, w.N, w.dtype) if path == "auto" else path
+    n_stats = len(set(w.outputs) & {"m", "d", "lse"})
+    ms, R = measure(w, steps, warmup, path)
+    warm_ms, _ = measure(w, max(10, steps // 4), 3, path, rotate=False)
+    nbytes = algorithmic_bytes(w, resolved, n_stats)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    eff = (2 * w.M * w.N * w.esize + 4 * w.M * n_stats) / (ms * 1e-3) / 1e9
+    rec = {
+        "metric": METRIC if name == "c2" else
+        f"achieved HBM GB/s (% of peak) + rows/s, online softmax fwd "
+        f"{w.dtype} {w.M}x{w.N}",
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if w.dtype == "f32" else "bf16",
+        "data": "synthetic (seeded numpy PCG64 normals, HBM-resident, "
+                f"{R} rotating buffer sets)",
+        "config": {"workload": w.desc, "M": w.M, "N": w.N,
+                   "outputs": list(w.outputs), "path": resolved},
+        "pct_of_peak": round(100.0 * gbs / PEAK_GBS, 2),
+        "rows_per_s": round(w.M / (ms * 1e-3), 1),
+        "effective_single_read_GBps": round(eff, 1),
+        "warm_cache_GBps": round(nbytes / (warm_ms * 1e-3) / 1e9, 1),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(gbs, 1),
+            "peak": PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(gbs / PEAK_GBS, 4),
+            "traffic": traffic_record(name),
+            "algorithmic_bytes_per_launch": nbytes,
+            "kernel_launches_per_step": 1 if resolved != "split" else 3,
+        },
+        "kernel_source": kernel_source_hash(),
+    }
+    rec["copy_ceiling_GBps"] = round(
+        copy_ceiling(w.M * w.N * w.esize), 1)
+    if want_cpu:
+        rec["cpu_baseline"] = cpu_baseline(w, n_stats, cpu_budget)
+    return rec
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--workload", default="c2",
+                    choices=["c1", "c2", "c3", "c4", "c5"])
+    ap.add_argument("--path", default="auto",
+                    choices=["auto", "resident", "stream", "split"])
+    ap.add_argument("--all", action="store_true",
+                    help="also report every workload on stderr")
+    ap.add_argument("--no-cpu", action="store_true",
+                    help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-budget", type=float, default=10.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this build measures the "
+              "single-GPU hot path (rows shard across GPUs with no "
+              "communication, see the design notes); use --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import row_wise_online_amd as rw
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    rw.load()
+
+    if args.all:
+        for name in ["c1", "c2", "c3", "c4", "c5"]:
+            print(f"[bench] workload {name}", file=sys.stderr, flush=True)
+            r = run_workload(name, args.steps, args.warmup, "auto",
+                             want_cpu=False)
+            print(json.dumps(r), file=sys.stderr, flush=True)
+    print(f"[bench] headline workload {args.workload}", file=sys.stderr,
+          flush=True)
+    rec = run_workload(args.workload, args.steps, args.warmup, args.path,
+                       want_cpu=not args.no_cpu, cpu_budget=args.cpu_budget)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

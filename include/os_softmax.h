@@ -1,0 +1,160 @@
+/*
+ * os_softmax -- row-wise online softmax for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI.  Every entry point takes plain device pointers, 64-bit sizes and a
+ * hipStream_t; nothing here allocates device memory or keeps a pointer after
+ * it returns.  All compute runs in the library's HIP kernels.
+ *
+ * What is computed (per row i of x[M,N]):
+ *   m_i   = max_j x_ij                               (the running max)
+ *   d_i   = sum_j e^(x_ij - m_i)                     (the normaliser)
+ *   y_ij  = e^(x_ij - m_i) / d_i
+ *   lse_i = m_i + log d_i
+ * The pass that produces (m, d) keeps a running state and combines partial
+ * states with the associative merge
+ *   m = max(m_a, m_b),  d = d_a e^(m_a - m) + d_b e^(m_b - m),
+ * as derived in "5.2 CUDA Online Softmax 实现优化" (AIInfraGuide), §2.1
+ * (recurrence), §2.2 (two passes), §4.1 (merge); the same state and merge
+ * appear in "Softmax 数值稳定性与 IO-Aware Attention：从在线归一化到
+ * FlashAttention" §4 and §4.1.  log-sum-exp as defined in "从原始Softmax到在线
+ * Softmax" (section deriving the stable form).
+ *
+ * Conventions shared by all entry points
+ *  - Layout: x and y are row-major; element (i, j) sits at base + i*ld + j
+ *    (ld in elements, ld >= N).  Statistics are fp32.
+ *  - dtype: OS_F32 (x, y are float) or OS_BF16 (x, y are bfloat16 bit
+ *    patterns, 2 bytes each; arithmetic is fp32, y is rounded to nearest
+ *    even).  y always has the dtype of x.
+ *  - Asynchrony: every call enqueues work on `stream` and returns; outputs
+ *    are valid once the stream reaches that point.  Multi-kernel paths are
+ *    ordered by the stream alone (no host sync, no atomics).
+ *  - Validation happens on the host, before any HIP call; an invalid call
+ *    enqueues nothing.  M == 0 is a valid no-op.
+ *  - HIP errors: a failed launch returns OS_ERR_HIP (from hipGetLastError,
+ *    which may also report an earlier, unrelated error left on the thread).
+ *  - Alignment is never an error: 16-byte vector memory operations are used
+ *    when both bases and both row pitches are 16-byte aligned, element
+ *    operations otherwise.
+ *  - Aliasing: y == x with ld_y == ld_x (in place) is allowed; any other
+ *    overlap between inputs and outputs is undefined.
+ *  - Determinism: the work partition is a pure function of (M, N, dtype,
+ *    path, alignment class) and no atomics are used, so repeated calls give
+ *    bit-identical results.  Different paths round differently (within the
+ *    documented accuracy).
+ *  - Special values: an element -inf has weight 0; a row of only -inf gives
+ *    m = -inf, d = 0, lse = -inf, y = NaN.  A NaN element makes d, lse and
+ *    the row of y NaN (m is the max of the other elements); a +inf element
+ *    gives m = +inf and a NaN row.
+ */
+#ifndef OS_SOFTMAX_H
+#define OS_SOFTMAX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    OS_OK = 0,
+    OS_ERR_NULL = 1,        /* a required pointer is NULL */
+    OS_ERR_SHAPE = 2,       /* M < 0 or M > 2^31-1, N < 1 or N > 2^30, K < 1 */
+    OS_ERR_STRIDE = 3,      /* ld < N (or ld_in < K), inc_out < 1 */
+    OS_ERR_DTYPE = 4,       /* unknown dtype */
+    OS_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required */
+    OS_ERR_PATH = 6,        /* unknown path value */
+    OS_ERR_UNSUPPORTED = 7, /* forced path cannot take this shape */
+    OS_ERR_HIP = 8          /* a HIP launch reported an error */
+} os_status;
+
+typedef enum { OS_F32 = 0, OS_BF16 = 1 } os_dtype;
+
+/* Execution paths.
+ *  RESIDENT: each row is loaded once into registers, reduced, and
+ *            normalised from registers (one read + one write of x).  Rows of
+ *            up to 32768 elements.  ("5.2 CUDA Online Softmax 实现优化" §6,
+ *            register-cached one-read version.)
+ *  STREAM:   one workgroup per row; pass 1 streams the row folding (m, d),
+ *            pass 2 re-reads it and writes y (two reads + one write).  Any N.
+ *  SPLIT:    several workgroups per row: a partial-state kernel, the
+ *            state-merge kernel, and a normalise kernel (§7.1 of the same
+ *            page names this two-stage scheme for few, very long rows).
+ *  AUTO:     choose by shape (os_softmax_select_path). */
+typedef enum {
+    OS_PATH_AUTO = 0,
+    OS_PATH_RESIDENT = 1,
+    OS_PATH_STREAM = 2,
+    OS_PATH_SPLIT = 3
+} os_path;
+
+/* Softmax forward.
+ *  x        [M, ld_x] input, dtype dt (read only).
+ *  y        [M, ld_y] output, dtype dt.
+ *  m_out, d_out, lse_out  nullable fp32 [M]: the row's (m, d) as defined
+ *           above (m is exactly the row max) and m + log d.
+ *  ws       device workspace of at least os_softmax_workspace_bytes(M, N,
+ *           dt, OS_PATH_AUTO) bytes, 256-byte aligned; may be NULL when that
+ *           size is 0.  The library only uses it during the enqueued work.
+ *  Returns OS_OK or the first validation error (nothing is enqueued then). */
+os_status os_softmax_fwd(const void *x, int64_t ld_x, void *y, int64_t ld_y,
+                         int64_t M, int64_t N, os_dtype dt,
+                         float *m_out, float *d_out, float *lse_out,
+                         void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* os_softmax_fwd on a caller-chosen path (AUTO behaves as os_softmax_fwd).
+ * OS_ERR_UNSUPPORTED if the path cannot take the shape (RESIDENT with
+ * N > 32768).  The workspace must cover os_softmax_workspace_bytes(M, N, dt,
+ * path). */
+os_status os_softmax_fwd_path(const void *x, int64_t ld_x, void *y,
+                              int64_t ld_y, int64_t M, int64_t N,
+                              os_dtype dt, float *m_out, float *d_out,
+                              float *lse_out, void *ws, size_t ws_bytes,
+                              os_path path, hipStream_t stream);
+
+/* Pass 1 only: the (m, d) state of each row, written to m_out[i*inc_out]
+ * and d_out[i*inc_out] (both required, fp32), and optionally
+ * lse_out[i*inc_out].  Called on a column window (x advanced by a column
+ * offset, N the window width) it gives that window's partial state, which
+ * os_state_merge combines with other windows' states ("Softmax 数值稳定性与
+ * IO-Aware Attention" §4.1: chunk a row, take each chunk's state, merge). */
+os_status os_softmax_stats(const void *x, int64_t ld_x, int64_t M, int64_t N,
+                           os_dtype dt, float *m_out, float *d_out,
+                           int64_t inc_out, float *lse_out, void *ws,
+                           size_t ws_bytes, hipStream_t stream);
+
+/* os_softmax_stats on a chosen path: STREAM (one workgroup per row) or SPLIT
+ * (several per row, then the merge kernel); RESIDENT is treated as STREAM,
+ * since pass 1 alone keeps nothing resident. */
+os_status os_softmax_stats_path(const void *x, int64_t ld_x, int64_t M,
+                                int64_t N, os_dtype dt, float *m_out,
+                                float *d_out, int64_t inc_out, float *lse_out,
+                                void *ws, size_t ws_bytes, os_path path,
+                                hipStream_t stream);
+
+/* Merge K partial states per row ("5.2 CUDA Online Softmax 实现优化" §4.1):
+ * row i's states are (m_in[i*ld_in + k], d_in[i*ld_in + k]), k < K, fp32.
+ * (-inf, 0) is an exact identity.  Writes m_out[i], d_out[i] (required) and
+ * lse_out[i] (nullable).  Outputs must not overlap the inputs. */
+os_status os_state_merge(const float *m_in, const float *d_in, int64_t ld_in,
+                         int64_t M, int64_t K, float *m_out, float *d_out,
+                         float *lse_out, hipStream_t stream);
+
+/* Workspace bytes that os_softmax_fwd(_path) and os_softmax_stats(_path)
+ * need for this shape and path (0 unless the split path is taken).  A pure
+ * function of its arguments; returns 0 for invalid arguments. */
+size_t os_softmax_workspace_bytes(int64_t M, int64_t N, os_dtype dt,
+                                  os_path path);
+
+/* The path AUTO resolves to for os_softmax_fwd at this shape (host only). */
+os_path os_softmax_select_path(int64_t M, int64_t N, os_dtype dt);
+
+/* Static description of a status code (never NULL). */
+const char *os_status_string(os_status s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* OS_SOFTMAX_H */

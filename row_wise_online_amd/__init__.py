@@ -1,0 +1,163 @@
+"""Row-wise online softmax for AMD MI355X (gfx950) -- Python binding.
+
+Thin wrapper over the C ABI of ``libos_softmax.so`` (``include/os_softmax.h``):
+each function checks that its tensors are on the GPU with the layout the ABI
+expects, passes their device pointers and the current HIP stream, and raises
+``OsError`` on a non-OK status.  PyTorch supplies device memory and streams
+only; every step of the computation runs in the library's HIP kernels, and
+there is no fallback when the library is missing.
+
+Same names as the C ABI, without the ``os_`` prefix:
+
+* ``softmax_fwd(x, y=None, m=None, d=None, lse=None, ws=None, path="auto")``
+* ``softmax_stats(x, m, d, lse=None, inc=1, ws=None, path="auto")``
+* ``state_merge(m_in, d_in, m_out, d_out, lse_out=None)``
+* ``workspace_bytes(M, N, dtype, path="auto")``, ``select_path(M, N, dtype)``
+"""
+from . import _lib
+from ._lib import OsError, PATHS, PATH_NAMES  # noqa: F401
+
+__all__ = ["softmax_fwd", "softmax_stats", "state_merge", "workspace_bytes",
+           "select_path", "OsError", "load"]
+
+
+def load():
+    """Load the HIP library; raises ImportError if it has not been built."""
+    return _lib.load()
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(dtype):
+    torch = _torch()
+    if dtype == torch.float32:
+        return _lib.OS_F32
+    if dtype == torch.bfloat16:
+        return _lib.OS_BF16
+    raise TypeError(f"unsupported dtype {dtype}: float32 or bfloat16")
+
+
+def _dtype_code_any(dtype):
+    if isinstance(dtype, str):
+        return {"f32": _lib.OS_F32, "float32": _lib.OS_F32,
+                "bf16": _lib.OS_BF16, "bfloat16": _lib.OS_BF16}[dtype]
+    return _dtype_code(dtype)
+
+
+def _matrix(t, name):
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError(f"{name} must be 2-D with unit column stride")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    return t.data_ptr(), t.stride(0)
+
+
+def _vec(t, name, M, inc=1):
+    """Pointer of an fp32 GPU vector holding M values at stride inc: either a
+    view whose own stride is inc, or a dense vector with room for them."""
+    torch = _torch()
+    if t is None:
+        return None
+    if t.dtype != torch.float32 or not t.is_cuda:
+        raise ValueError(f"{name} must be a float32 GPU tensor")
+    if t.dim() != 1:
+        raise ValueError(f"{name} must be 1-D")
+    if t.stride(0) == inc and t.numel() >= M:
+        return t.data_ptr()
+    if t.stride(0) == 1 and t.numel() >= (M - 1) * inc + 1:
+        return t.data_ptr()
+    raise ValueError(f"{name} must hold {M} values at stride {inc}")
+
+
+def _stream(stream):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _path_code(path):
+    if isinstance(path, str):
+        return _lib.PATHS[path]
+    return int(path)
+
+
+def workspace_bytes(M, N, dtype, path="auto"):
+    return _lib.load().os_softmax_workspace_bytes(
+        M, N, _dtype_code_any(dtype), _path_code(path))
+
+
+def select_path(M, N, dtype):
+    return _lib.PATH_NAMES[_lib.load().os_softmax_select_path(
+        M, N, _dtype_code_any(dtype))]
+
+
+def _workspace(ws, need, device):
+    torch = _torch()
+    if need == 0:
+        return (ws.data_ptr() if ws is not None else None), (
+            ws.numel() if ws is not None else 0)
+    if ws is None:
+        ws = torch.empty(need, dtype=torch.uint8, device=device)
+    return ws.data_ptr(), ws.numel() * ws.element_size()
+
+
+def softmax_fwd(x, y=None, *, m=None, d=None, lse=None, ws=None,
+                path="auto", stream=None):
+    """y = softmax(x) along rows; optional fp32 row statistics m, d, lse."""
+    torch = _torch()
+    lib = _lib.load()
+    dt = _dtype_code(x.dtype)
+    if y is None:
+        y = torch.empty_like(x)
+    if y.dtype != x.dtype or y.shape != x.shape:
+        raise ValueError("y must have the dtype and shape of x")
+    xp, ldx = _matrix(x, "x")
+    yp, ldy = _matrix(y, "y")
+    M, N = x.shape
+    pc = _path_code(path)
+    need = lib.os_softmax_workspace_bytes(M, N, dt, pc)
+    wp, wb = _workspace(ws, need, x.device)
+    st = lib.os_softmax_fwd_path(xp, ldx, yp, ldy, M, N, dt,
+                                 _vec(m, "m", M), _vec(d, "d", M),
+                                 _vec(lse, "lse", M), wp, wb, pc,
+                                 _stream(stream))
+    _lib.check("os_softmax_fwd_path", st)
+    return y
+
+
+def softmax_stats(x, m, d, lse=None, *, inc=1, ws=None, path="auto",
+                  stream=None):
+    """Pass 1 only: each row's (m, d) (and lse) at index row * inc."""
+    lib = _lib.load()
+    dt = _dtype_code(x.dtype)
+    xp, ldx = _matrix(x, "x")
+    M, N = x.shape
+    pc = _path_code(path)
+    need = lib.os_softmax_workspace_bytes(M, N, dt, pc)
+    wp, wb = _workspace(ws, need, x.device)
+    st = lib.os_softmax_stats_path(xp, ldx, M, N, dt, _vec(m, "m", M, inc),
+                                   _vec(d, "d", M, inc),
+                                   inc, _vec(lse, "lse", M, inc), wp, wb, pc,
+                                   _stream(stream))
+    _lib.check("os_softmax_stats_path", st)
+
+
+def state_merge(m_in, d_in, m_out, d_out, lse_out=None, *, stream=None):
+    """Merge the K states of each row of m_in, d_in ([M, K], fp32)."""
+    torch = _torch()
+    lib = _lib.load()
+    for t, n in ((m_in, "m_in"), (d_in, "d_in")):
+        if t.dtype != torch.float32:
+            raise ValueError(f"{n} must be float32")
+    mp, ld = _matrix(m_in, "m_in")
+    dp, ld2 = _matrix(d_in, "d_in")
+    if ld != ld2 or m_in.shape != d_in.shape:
+        raise ValueError("m_in and d_in must have the same shape and stride")
+    M, K = m_in.shape
+    st = lib.os_state_merge(mp, dp, ld, M, K, _vec(m_out, "m_out", M),
+                            _vec(d_out, "d_out", M),
+                            _vec(lse_out, "lse_out", M), _stream(stream))
+    _lib.check("os_state_merge", st)

@@ -1,0 +1,194 @@
+// C ABI of the row-wise online softmax library: argument validation (on the
+// host, before any HIP call), path selection and launches.
+#include <stdint.h>
+
+#include "../../include/os_softmax.h"
+#include "launch.hpp"
+
+namespace {
+
+constexpr int64_t kMaxN = int64_t(1) << 30;  // keeps in-row int indexing exact
+constexpr int64_t kMaxM = (int64_t(1) << 31) - 1;
+
+// AUTO rule (pure function of the shape, tuned for 256 CUs):
+//  - rows that fit in registers go resident, unless they are long and so
+//    few that one workgroup per row would leave most CUs idle;
+//  - longer rows with many rows stream, one workgroup per row;
+//  - few long rows are split across workgroups.
+constexpr int64_t kManyRows = 512;
+constexpr int64_t kShortRow = 4096;
+
+os_path select_fwd(int64_t M, int64_t N) {
+    if (N <= os::kResidentMaxN && (M >= kManyRows || N <= kShortRow))
+        return OS_PATH_RESIDENT;
+    if (M >= kManyRows) return OS_PATH_STREAM;
+    return OS_PATH_SPLIT;
+}
+
+os_path select_stats(int64_t M, int64_t N) {
+    return (M >= kManyRows || N <= kShortRow) ? OS_PATH_STREAM : OS_PATH_SPLIT;
+}
+
+int esize(os_dtype dt) { return dt == OS_BF16 ? 2 : 4; }
+
+bool aligned16(const void *p, int64_t ld, os_dtype dt) {
+    return (reinterpret_cast<uintptr_t>(p) % 16 == 0) &&
+           ((ld * esize(dt)) % 16 == 0);
+}
+
+os_status check_shape(int64_t M, int64_t N, os_dtype dt) {
+    if (dt != OS_F32 && dt != OS_BF16) return OS_ERR_DTYPE;
+    if (M < 0 || M > kMaxM || N < 1 || N > kMaxN) return OS_ERR_SHAPE;
+    return OS_OK;
+}
+
+os_status finish() {
+    return hipGetLastError() == hipSuccess ? OS_OK : OS_ERR_HIP;
+}
+
+size_t workspace_for(int64_t M, int64_t N, os_path resolved) {
+    return (resolved == OS_PATH_SPLIT && M > 0) ? os::split_workspace_bytes(M, N)
+                                                : 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+os_path os_softmax_select_path(int64_t M, int64_t N, os_dtype dt) {
+    if (check_shape(M, N, dt) != OS_OK) return OS_PATH_AUTO;
+    return select_fwd(M, N);
+}
+
+size_t os_softmax_workspace_bytes(int64_t M, int64_t N, os_dtype dt,
+                                  os_path path) {
+    if (check_shape(M, N, dt) != OS_OK) return 0;
+    if (path < OS_PATH_AUTO || path > OS_PATH_SPLIT) return 0;
+    // one size covers the forward and the statistics call on this path
+    if (path == OS_PATH_AUTO) {
+        const size_t a = workspace_for(M, N, select_fwd(M, N));
+        const size_t b = workspace_for(M, N, select_stats(M, N));
+        return a > b ? a : b;
+    }
+    return workspace_for(M, N, path);
+}
+
+os_status os_softmax_fwd_path(const void *x, int64_t ld_x, void *y,
+                              int64_t ld_y, int64_t M, int64_t N,
+                              os_dtype dt, float *m_out, float *d_out,
+                              float *lse_out, void *ws, size_t ws_bytes,
+                              os_path path, hipStream_t stream) {
+    os_status s = check_shape(M, N, dt);
+    if (s != OS_OK) return s;
+    if (path < OS_PATH_AUTO || path > OS_PATH_SPLIT) return OS_ERR_PATH;
+    if (ld_x < N || ld_y < N) return OS_ERR_STRIDE;
+    if (M == 0) return OS_OK;
+    if (x == nullptr || y == nullptr) return OS_ERR_NULL;
+    const os_path p = (path == OS_PATH_AUTO) ? select_fwd(M, N) : path;
+    if (p == OS_PATH_RESIDENT && N > os::kResidentMaxN) return OS_ERR_UNSUPPORTED;
+    const size_t need = workspace_for(M, N, p);
+    if (need > 0 && (ws == nullptr || ws_bytes < need)) return OS_ERR_WORKSPACE;
+
+    os::FwdArgs a{};
+    a.x = x;
+    a.ldx = ld_x;
+    a.y = y;
+    a.ldy = ld_y;
+    a.M = M;
+    a.N = static_cast<int>(N);
+    a.m_out = m_out;
+    a.d_out = d_out;
+    a.inc_out = 1;
+    a.lse_out = lse_out;
+    a.dt = dt == OS_F32 ? os::Dt::F32 : os::Dt::BF16;
+    a.vec = aligned16(x, ld_x, dt) && aligned16(y, ld_y, dt);
+    a.stream = stream;
+    switch (p) {
+        case OS_PATH_RESIDENT: os::launch_resident(a); break;
+        case OS_PATH_STREAM: os::launch_stream(a); break;
+        default: os::launch_split(a, ws); break;
+    }
+    return finish();
+}
+
+os_status os_softmax_fwd(const void *x, int64_t ld_x, void *y, int64_t ld_y,
+                         int64_t M, int64_t N, os_dtype dt, float *m_out,
+                         float *d_out, float *lse_out, void *ws,
+                         size_t ws_bytes, hipStream_t stream) {
+    return os_softmax_fwd_path(x, ld_x, y, ld_y, M, N, dt, m_out, d_out,
+                               lse_out, ws, ws_bytes, OS_PATH_AUTO, stream);
+}
+
+os_status os_softmax_stats_path(const void *x, int64_t ld_x, int64_t M,
+                                int64_t N, os_dtype dt, float *m_out,
+                                float *d_out, int64_t inc_out, float *lse_out,
+                                void *ws, size_t ws_bytes, os_path path,
+                                hipStream_t stream) {
+    os_status s = check_shape(M, N, dt);
+    if (s != OS_OK) return s;
+    if (path < OS_PATH_AUTO || path > OS_PATH_SPLIT) return OS_ERR_PATH;
+    if (ld_x < N || inc_out < 1) return OS_ERR_STRIDE;
+    if (M == 0) return OS_OK;
+    if (x == nullptr || m_out == nullptr || d_out == nullptr) return OS_ERR_NULL;
+    os_path p = (path == OS_PATH_AUTO) ? select_stats(M, N) : path;
+    if (p == OS_PATH_RESIDENT) p = OS_PATH_STREAM;
+    const size_t need = workspace_for(M, N, p);
+    if (need > 0 && (ws == nullptr || ws_bytes < need)) return OS_ERR_WORKSPACE;
+
+    os::FwdArgs a{};
+    a.x = x;
+    a.ldx = ld_x;
+    a.y = nullptr;
+    a.ldy = 0;
+    a.M = M;
+    a.N = static_cast<int>(N);
+    a.m_out = m_out;
+    a.d_out = d_out;
+    a.inc_out = inc_out;
+    a.lse_out = lse_out;
+    a.dt = dt == OS_F32 ? os::Dt::F32 : os::Dt::BF16;
+    a.vec = aligned16(x, ld_x, dt);
+    a.stream = stream;
+    if (p == OS_PATH_STREAM) os::launch_stream(a);
+    else os::launch_split(a, ws);
+    return finish();
+}
+
+os_status os_softmax_stats(const void *x, int64_t ld_x, int64_t M, int64_t N,
+                           os_dtype dt, float *m_out, float *d_out,
+                           int64_t inc_out, float *lse_out, void *ws,
+                           size_t ws_bytes, hipStream_t stream) {
+    return os_softmax_stats_path(x, ld_x, M, N, dt, m_out, d_out, inc_out,
+                                 lse_out, ws, ws_bytes, OS_PATH_AUTO, stream);
+}
+
+os_status os_state_merge(const float *m_in, const float *d_in, int64_t ld_in,
+                         int64_t M, int64_t K, float *m_out, float *d_out,
+                         float *lse_out, hipStream_t stream) {
+    if (M < 0 || M > kMaxM || K < 1 || K > kMaxN) return OS_ERR_SHAPE;
+    if (ld_in < K) return OS_ERR_STRIDE;
+    if (M == 0) return OS_OK;
+    if (m_in == nullptr || d_in == nullptr || m_out == nullptr ||
+        d_out == nullptr)
+        return OS_ERR_NULL;
+    os::launch_state_merge(m_in, d_in, ld_in, M, static_cast<int>(K), m_out,
+                           d_out, 1, nullptr, nullptr, lse_out, 1, stream);
+    return finish();
+}
+
+const char *os_status_string(os_status s) {
+    switch (s) {
+        case OS_OK: return "OS_OK: success";
+        case OS_ERR_NULL: return "OS_ERR_NULL: a required pointer is NULL";
+        case OS_ERR_SHAPE: return "OS_ERR_SHAPE: M, N or K out of range";
+        case OS_ERR_STRIDE: return "OS_ERR_STRIDE: row stride smaller than the row, or inc_out < 1";
+        case OS_ERR_DTYPE: return "OS_ERR_DTYPE: unknown dtype";
+        case OS_ERR_WORKSPACE: return "OS_ERR_WORKSPACE: workspace missing or too small";
+        case OS_ERR_PATH: return "OS_ERR_PATH: unknown path";
+        case OS_ERR_UNSUPPORTED: return "OS_ERR_UNSUPPORTED: the forced path cannot take this shape";
+        case OS_ERR_HIP: return "OS_ERR_HIP: a HIP launch failed";
+    }
+    return "unknown os_status";
+}
+
+}  // extern "C"

@@ -1,0 +1,154 @@
+// Element types, 16-byte vector memory access and the exp helper shared by
+// the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace os {
+
+constexpr int kWave = 64;                    // CDNA wavefront width
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kNegInf = -__builtin_huge_valf();
+
+// e^t for t = x - m, computed as 2^(t * log2 e).  The subtraction x - m is
+// done first by the caller (exact when x is near m), then scaled; folding
+// -m * log2 e into an fma would lose the low bits of large maxima.
+// __builtin_exp2f lowers to v_exp_f32 with a range fix-up that keeps
+// results in the fp32 subnormal range accurate.
+__device__ __forceinline__ float exp_shifted(float t) {
+    return __builtin_exp2f(t * kLog2e);
+}
+
+// The reference point used for exponents: the max itself, or 0 when the
+// max is -inf (a state holding only -inf / padding).  With it, padding and
+// -inf elements give e^(-inf) = 0, the identity state (-inf, 0) merges to
+// itself, and a NaN folded into d stays NaN.
+__device__ __forceinline__ float safe_ref(float m) {
+    return (m == kNegInf) ? 0.0f : m;
+}
+
+// ---- element types --------------------------------------------------------
+// Traits give: the stored type, E = elements per 16-byte vector, and the
+// conversions between a 16-byte vector and E fp32 values.
+
+struct F32 {
+    using elem_t = float;
+    static constexpr int E = 4;
+    __device__ __forceinline__ static float to_f32(float v) { return v; }
+    __device__ __forceinline__ static float from_f32(float v) { return v; }
+    __device__ __forceinline__ static void unpack(const uint4 &u, float *f) {
+        f[0] = __uint_as_float(u.x);
+        f[1] = __uint_as_float(u.y);
+        f[2] = __uint_as_float(u.z);
+        f[3] = __uint_as_float(u.w);
+    }
+    __device__ __forceinline__ static uint4 pack(const float *f) {
+        return make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]),
+                          __float_as_uint(f[2]), __float_as_uint(f[3]));
+    }
+};
+
+// bf16 stored as its 16-bit pattern.  Widening is exact (the pattern is the
+// top half of the fp32 with the same value); narrowing rounds to nearest
+// even (v_cvt_pk_bf16_f32 on gfx950).
+struct BF16 {
+    using elem_t = uint16_t;
+    static constexpr int E = 8;
+    __device__ __forceinline__ static float to_f32(uint16_t b) {
+        return __uint_as_float(static_cast<uint32_t>(b) << 16);
+    }
+    __device__ __forceinline__ static uint16_t from_f32(float v) {
+        return __builtin_bit_cast(uint16_t, static_cast<__bf16>(v));
+    }
+    __device__ __forceinline__ static uint32_t pack2(float lo, float hi) {
+        typedef float f2 __attribute__((ext_vector_type(2)));
+        typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+        f2 v = {lo, hi};
+        b2 r = __builtin_convertvector(v, b2);
+        return __builtin_bit_cast(uint32_t, r);
+    }
+    __device__ __forceinline__ static void unpack(const uint4 &u, float *f) {
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            f[2 * i] = __uint_as_float(w[i] << 16);
+            f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+        }
+    }
+    __device__ __forceinline__ static uint4 pack(const float *f) {
+        return make_uint4(pack2(f[0], f[1]), pack2(f[2], f[3]),
+                          pack2(f[4], f[5]), pack2(f[6], f[7]));
+    }
+};
+
+// ---- memory access --------------------------------------------------------
+// A "slot" is the unit one lane moves per memory instruction: a 16-byte
+// vector (VEC = true, E elements) or one element (VEC = false).  Slots of a
+// row are numbered 0, 1, ...; slot s covers elements [s*W, s*W + W) with
+// W = E or 1.  A slot that runs past N is loaded element by element with
+// -inf fill, and stored element by element.
+
+template <class Tr, bool VEC>
+struct Slot {
+    static constexpr int W = VEC ? Tr::E : 1;
+    using elem_t = typename Tr::elem_t;
+
+    // Load slot s of a row into f[0..W), -inf beyond column N.
+    __device__ __forceinline__ static void load(const elem_t *row, int s,
+                                                int N, float *f) {
+        const int j0 = s * W;
+        if constexpr (VEC) {
+            if (j0 + W <= N) {
+                uint4 u = *reinterpret_cast<const uint4 *>(row + j0);
+                Tr::unpack(u, f);
+            } else {
+#pragma unroll
+                for (int e = 0; e < W; ++e)
+                    f[e] = (j0 + e < N) ? Tr::to_f32(row[j0 + e]) : kNegInf;
+            }
+        } else {
+            f[0] = (j0 < N) ? Tr::to_f32(row[j0]) : kNegInf;
+        }
+    }
+
+    // Load a slot known to lie entirely inside the row.
+    __device__ __forceinline__ static void load_full(const elem_t *row, int s,
+                                                     float *f) {
+        const int j0 = s * W;
+        if constexpr (VEC) {
+            uint4 u = *reinterpret_cast<const uint4 *>(row + j0);
+            Tr::unpack(u, f);
+        } else {
+            f[0] = Tr::to_f32(row[j0]);
+        }
+    }
+
+    __device__ __forceinline__ static void store(elem_t *row, int s, int N,
+                                                 const float *f) {
+        const int j0 = s * W;
+        if constexpr (VEC) {
+            if (j0 + W <= N) {
+                *reinterpret_cast<uint4 *>(row + j0) = Tr::pack(f);
+            } else {
+#pragma unroll
+                for (int e = 0; e < W; ++e)
+                    if (j0 + e < N) row[j0 + e] = Tr::from_f32(f[e]);
+            }
+        } else {
+            if (j0 < N) row[j0] = Tr::from_f32(f[0]);
+        }
+    }
+
+    __device__ __forceinline__ static void store_full(elem_t *row, int s,
+                                                      const float *f) {
+        const int j0 = s * W;
+        if constexpr (VEC) {
+            *reinterpret_cast<uint4 *>(row + j0) = Tr::pack(f);
+        } else {
+            row[j0] = Tr::from_f32(f[0]);
+        }
+    }
+};
+
+}  // namespace os

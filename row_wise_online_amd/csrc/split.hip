@@ -1,0 +1,98 @@
+// Split-row path (partial states -> state merge -> normalise) and the
+// state-merge launcher.
+#include "kernels.hpp"
+#include "launch.hpp"
+
+namespace os {
+namespace {
+
+constexpr int kSplitWaves = 4;
+constexpr int kMergeRows = 4;          // rows (wavefronts) per merge workgroup
+constexpr int64_t kTargetWgs = 2048;   // 8 workgroups per CU on 256 CUs
+constexpr int64_t kChunkAlign = 4096;  // chunk length granularity (elements)
+
+template <class Tr, bool VEC>
+constexpr int tile_slots() {
+    return VEC ? 32 / Tr::E : 16;
+}
+
+size_t align256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
+
+struct WsLayout {
+    float *part_m, *part_d, *row_m, *row_d;
+};
+
+WsLayout layout(void *ws, int64_t M, int P) {
+    char *p = static_cast<char *>(ws);
+    const size_t part = align256(sizeof(float) * static_cast<size_t>(M) * P);
+    const size_t rows = align256(sizeof(float) * static_cast<size_t>(M));
+    WsLayout l;
+    l.part_m = reinterpret_cast<float *>(p);
+    l.part_d = reinterpret_cast<float *>(p + part);
+    l.row_m = reinterpret_cast<float *>(p + 2 * part);
+    l.row_d = reinterpret_cast<float *>(p + 2 * part + rows);
+    return l;
+}
+
+template <class Tr, bool VEC>
+void run(const FwdArgs &a, void *ws) {
+    using E = typename Tr::elem_t;
+    constexpr int U = tile_slots<Tr, VEC>();
+    const SplitPlan plan = split_plan(a.M, a.N);
+    const WsLayout l = layout(ws, a.M, plan.P);
+    const dim3 grid(static_cast<unsigned>(a.M * plan.P));
+    const dim3 block(kWave * kSplitWaves);
+    const E *x = static_cast<const E *>(a.x);
+
+    split_partial_kernel<Tr, VEC, kSplitWaves, U><<<grid, block, 0, a.stream>>>(
+        x, a.ldx, a.N, plan.P, plan.C, l.part_m, l.part_d);
+
+    // Row states go to the workspace (read by the normalise kernel) and to
+    // whichever of the caller's m / d / lse are given, in one merge launch.
+    launch_state_merge(l.part_m, l.part_d, plan.P, a.M, plan.P, l.row_m,
+                       l.row_d, 1, a.m_out, a.d_out, a.lse_out, a.inc_out,
+                       a.stream);
+
+    if (a.y) {
+        split_normalize_kernel<Tr, VEC, kSplitWaves, U><<<grid, block, 0, a.stream>>>(
+            x, a.ldx, static_cast<E *>(a.y), a.ldy, a.N, plan.P, plan.C,
+            l.row_m, l.row_d, 1);
+    }
+}
+
+}  // namespace
+
+SplitPlan split_plan(int64_t M, int64_t N) {
+    int64_t P = (kTargetWgs + M - 1) / M;
+    if (P < 1) P = 1;
+    int64_t C = (N + P - 1) / P;
+    C = (C + kChunkAlign - 1) / kChunkAlign * kChunkAlign;
+    P = (N + C - 1) / C;
+    return SplitPlan{static_cast<int>(P), static_cast<int>(C)};
+}
+
+size_t split_workspace_bytes(int64_t M, int64_t N) {
+    const SplitPlan plan = split_plan(M, N);
+    return 2 * align256(sizeof(float) * static_cast<size_t>(M) * plan.P) +
+           2 * align256(sizeof(float) * static_cast<size_t>(M));
+}
+
+void launch_split(const FwdArgs &a, void *ws) {
+    if (a.dt == Dt::F32) {
+        if (a.vec) run<F32, true>(a, ws); else run<F32, false>(a, ws);
+    } else {
+        if (a.vec) run<BF16, true>(a, ws); else run<BF16, false>(a, ws);
+    }
+}
+
+void launch_state_merge(const float *m_in, const float *d_in, int64_t ld,
+                        int64_t M, int K, float *m_a, float *d_a,
+                        int64_t inc_a, float *m_b, float *d_b, float *lse_b,
+                        int64_t inc_b, hipStream_t stream) {
+    const dim3 grid(static_cast<unsigned>((M + kMergeRows - 1) / kMergeRows));
+    const dim3 block(kWave * kMergeRows);
+    state_merge_kernel<kMergeRows><<<grid, block, 0, stream>>>(
+        m_in, d_in, ld, M, K, m_a, d_a, inc_a, m_b, d_b, lse_b, inc_b);
+}
+
+}  // namespace os

@@ -1,0 +1,339 @@
+"""GPU parity: the HIP library (through its C ABI) against the fp64 oracle.
+
+Every test calls the library via the ctypes binding on seeded inputs from
+row_wise_online_amd.workloads and compares with oracle values computed
+from the same stored bytes.  Shapes span several tiles and ragged tails;
+each path is forced on every shape it accepts, in fp32 and bf16, with
+16-byte-aligned and misaligned rows.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+import oracle  # noqa: E402
+import row_wise_online_amd as rw  # noqa: E402
+from row_wise_online_amd import workloads as wl  # noqa: E402
+
+from gpu_util import (check_d, check_lse, check_m, check_y, empty_like_rows,  # noqa: E402
+                      to_device, to_host)
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    rw.load()
+    yield
+    torch.cuda.synchronize()
+
+
+def _run_fwd(x_host, path="auto", ld_y=None, stats=True):
+    x = to_device(x_host)
+    M, N = x.shape
+    y = empty_like_rows(x, ld_y)
+    z = lambda: torch.full((M,), float("nan"), device="cuda")
+    m, d, lse = (z(), z(), z()) if stats else (None, None, None)
+    rw.softmax_fwd(x, y, m=m, d=d, lse=lse, path=path)
+    torch.cuda.synchronize()
+    out = to_host(y)
+    if stats:
+        return out, m.cpu().numpy(), d.cpu().numpy(), lse.cpu().numpy()
+    return out, None, None, None
+
+
+def _check_all(x_host, res, what):
+    y, m, d, lse = res
+    y_ref, m_ref, d_ref, l_ref = oracle.softmax(x_host)
+    check_y(y, y_ref, what)
+    if m is not None:
+        check_m(m, m_ref, what)
+        check_d(d, d_ref, what)
+        check_lse(lse, l_ref, what)
+
+
+# ---------------------------------------------------------------------------
+# Each path forced on shapes spanning tiles and ragged tails
+# ---------------------------------------------------------------------------
+
+SHAPES = [(3, 1), (5, 2), (7, 3), (4, 63), (4, 64), (4, 65), (9, 1000),
+          (3, 1023), (3, 1025), (5, 4096), (2, 4097), (2, 8191), (3, 16385),
+          (2, 32768)]
+LONG_SHAPES = [(3, 20000), (2, 70001), (1, 300000)]
+
+
+def _input(M, N, dtype, seed, misalign):
+    # misaligned rows: an odd row stride, so 16-byte vectors are illegal
+    ld = N + 1 if misalign else None
+    return wl.normal(M, N, scale=3.0, seed=seed, dtype=dtype, ld=ld)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("misalign", [False, True])
+@pytest.mark.parametrize("path", ["resident", "stream", "split"])
+def test_paths_on_shapes(path, dtype, misalign):
+    for i, (M, N) in enumerate(SHAPES + (LONG_SHAPES if path != "resident" else [])):
+        what = f"{path} {dtype} misalign={misalign} M={M} N={N}"
+        _say(what)
+        x = _input(M, N, dtype, seed=100 + i, misalign=misalign)
+        _check_all(x, _run_fwd(x, path), what)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_misaligned_base_column_window(dtype):
+    # x starts one element into each row: the base pointer is misaligned
+    full = wl.normal(6, 1500, scale=2.0, seed=7, dtype=dtype)
+    xw = full[:, 1:]
+    xd = to_device(full)[:, 1:]
+    for path in ("resident", "stream", "split"):
+        y = torch.empty((6, 1499), dtype=xd.dtype, device="cuda")
+        rw.softmax_fwd(xd, y, path=path)
+        torch.cuda.synchronize()
+        y_ref, *_ = oracle.softmax(np.ascontiguousarray(xw))
+        check_y(to_host(y), y_ref, f"window {path} {dtype}")
+
+
+def test_padded_output_stride():
+    x = wl.normal(5, 777, scale=2.0, seed=8)
+    for path in ("resident", "stream", "split"):
+        res = _run_fwd(x, path, ld_y=800)
+        _check_all(x, res, f"ld_y {path}")
+
+
+# ---------------------------------------------------------------------------
+# The five workloads at full size, on the path the library picks
+# ---------------------------------------------------------------------------
+
+SAMPLE_ROWS = {"c1": None, "c2": 48, "c3": 256, "c4": 12, "c5": 3}
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c5"])
+def test_workload_full_size(name):
+    w = wl.WORKLOADS[name]
+    _say(f"workload {name}: {w.desc} path={rw.select_path(w.M, w.N, w.dtype)}")
+    x_host = wl.generate(name)
+    x = to_device(x_host)
+    y = torch.empty_like(x)
+    m = torch.empty(w.M, device="cuda")
+    d = torch.empty(w.M, device="cuda")
+    lse = torch.empty(w.M, device="cuda")
+    rw.softmax_fwd(x, y, m=m, d=d, lse=lse)
+    torch.cuda.synchronize()
+
+    # properties over every row
+    ysum = y.double().sum(dim=1).cpu().numpy()
+    # each bf16 value is within one bf16 step (relative 2^-7) of the exact
+    # value, so a row sum is within 2^-7 of 1; fp32 values are far closer
+    tol = 2.0 ** -7 if w.dtype == "bf16" else 1e-4
+    assert np.all(np.abs(ysum - 1.0) < tol), f"{name}: row sums"
+    m_h = m.cpu().numpy()
+    assert np.array_equal(m_h, x.float().max(dim=1).values.cpu().numpy())
+    assert torch.isfinite(y).all()
+
+    # oracle statistics of every row (no y), oracle y of sampled rows
+    _, m_ref, d_ref, l_ref = oracle.softmax(x_host, want_y=False)
+    check_m(m_h, m_ref, name)
+    check_d(d.cpu().numpy(), d_ref, name)
+    check_lse(lse.cpu().numpy(), l_ref, name)
+    if name != "c4":
+        # the workloads whose LSE stays below 128 meet the plain 1e-5 bound
+        assert np.all(np.abs(lse.cpu().numpy() - l_ref) <= 1e-5)
+    k = SAMPLE_ROWS[name]
+    rows = np.arange(w.M) if k is None else np.sort(
+        np.random.default_rng(5).choice(w.M, size=k, replace=False))
+    xs = np.ascontiguousarray(x_host[rows])
+    y_ref, *_ = oracle.softmax(xs)
+    ys = to_host(y[torch.as_tensor(rows, device="cuda")])
+    err = check_y(ys, y_ref, name)
+    _say(f"  {name}: max abs err {err[0]:.3e}, max rel/ulp {err[1]}")
+    if name == "c5":
+        cols = wl.planted_columns("c5")
+        assert np.all(m_h == 20.0)
+        assert np.all(np.argmax(to_host(y[:, :]), axis=1) == cols)
+
+
+# ---------------------------------------------------------------------------
+# Statistics, column windows and the state merge
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("path", ["stream", "split"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_stats(path, dtype):
+    for (M, N), inc in [((5, 1000), 1), ((3, 70001), 3), ((600, 130), 2),
+                        ((2, 4096), 1)]:
+        x_h = wl.normal(M, N, scale=4.0, seed=N, dtype=dtype)
+        x = to_device(x_h)
+        buf = torch.full((3, M * inc), float("nan"), device="cuda")
+        rw.softmax_stats(x, buf[0], buf[1], buf[2], inc=inc, path=path)
+        torch.cuda.synchronize()
+        h = buf.cpu().numpy()[:, ::inc]
+        _, m_ref, d_ref, l_ref = oracle.softmax(x_h, want_y=False)
+        what = f"stats {path} {dtype} {M}x{N} inc={inc}"
+        check_m(h[0], m_ref, what)
+        check_d(h[1], d_ref, what)
+        check_lse(h[2], l_ref, what)
+        # untouched gaps between strided outputs
+        if inc > 1:
+            assert np.all(np.isnan(buf.cpu().numpy()[:, 1::inc]))
+
+
+def test_column_windows_merge_to_row_state():
+    # the state of each column window, merged, is the state of the row
+    M, N, Wn = 7, 50000, 6
+    x_h = wl.normal(M, N, scale=2.0, seed=9)
+    x = to_device(x_h)
+    edges = np.linspace(0, N, Wn + 1).astype(int)
+    ms = torch.empty((M, Wn), device="cuda")
+    ds = torch.empty((M, Wn), device="cuda")
+    for k in range(Wn):
+        a, b = edges[k], edges[k + 1]
+        rw.softmax_stats(x[:, a:b], ms[:, k], ds[:, k], inc=Wn)
+    mo = torch.empty(M, device="cuda")
+    do = torch.empty(M, device="cuda")
+    lo = torch.empty(M, device="cuda")
+    rw.state_merge(ms, ds, mo, do, lo)
+    torch.cuda.synchronize()
+    _, m_ref, d_ref, l_ref = oracle.softmax(x_h, want_y=False)
+    check_m(mo.cpu().numpy(), m_ref, "windows")
+    check_d(do.cpu().numpy(), d_ref, "windows")
+    check_lse(lo.cpu().numpy(), l_ref, "windows")
+
+
+@pytest.mark.parametrize("K", [1, 5, 64, 65, 1000])
+def test_state_merge_against_oracle(K):
+    rng = np.random.default_rng(K)
+    M = 37
+    m_in = rng.uniform(-100.0, 100.0, (M, K)).astype(np.float32)
+    d_in = rng.uniform(0.5, 1000.0, (M, K)).astype(np.float32)
+    ident = rng.random((M, K)) < 0.2        # identity states (-inf, 0)
+    m_in[ident] = -np.inf
+    d_in[ident] = 0.0
+    m_in[3, :] = -np.inf                    # a row of identities only
+    d_in[3, :] = 0.0
+    mo = torch.empty(M, device="cuda")
+    do = torch.empty(M, device="cuda")
+    lo = torch.empty(M, device="cuda")
+    rw.state_merge(torch.from_numpy(m_in).cuda(), torch.from_numpy(d_in).cuda(),
+                   mo, do, lo)
+    torch.cuda.synchronize()
+    m_ref, d_ref, l_ref = oracle.merge(m_in, d_in)
+    mh, dh, lh = mo.cpu().numpy(), do.cpu().numpy(), lo.cpu().numpy()
+    assert np.array_equal(mh.astype(np.float64), m_ref)
+    fin = np.isfinite(m_ref)
+    rel = np.abs(dh[fin] - d_ref[fin]) / d_ref[fin]
+    assert rel.max() <= 1e-5
+    assert dh[3] == 0.0 and mh[3] == -np.inf and lh[3] == -np.inf
+    assert np.all(np.abs(lh[fin] - l_ref[fin]) <= 1e-5 + oracle.f32_ulp(l_ref[fin]))
+
+
+def test_state_merge_strided_rows():
+    M, K, ld = 9, 13, 20
+    rng = np.random.default_rng(3)
+    m_full = rng.uniform(-5, 5, (M, ld)).astype(np.float32)
+    d_full = rng.uniform(1, 3, (M, ld)).astype(np.float32)
+    m_full[:, K:] = np.nan                   # padding must not be read
+    d_full[:, K:] = np.nan
+    mo = torch.empty(M, device="cuda")
+    do = torch.empty(M, device="cuda")
+    rw.state_merge(torch.from_numpy(m_full).cuda()[:, :K],
+                   torch.from_numpy(d_full).cuda()[:, :K], mo, do)
+    torch.cuda.synchronize()
+    m_ref, d_ref, _ = oracle.merge(m_full[:, :K], d_full[:, :K])
+    assert np.array_equal(mo.cpu().numpy().astype(np.float64), m_ref)
+    assert np.all(np.abs(do.cpu().numpy() - d_ref) / d_ref <= 1e-5)
+
+
+# ---------------------------------------------------------------------------
+# Edge cases
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("offset", [80.0, -80.0, 1e4, -1e4, 1e30, -1e30])
+@pytest.mark.parametrize("path", ["resident", "stream", "split"])
+def test_large_offsets(offset, path):
+    x = wl.normal(4, 3000, scale=3.0, offset=offset, seed=11)
+    res = _run_fwd(x, path)
+    assert np.all(np.isfinite(res[0]))
+    _check_all(x, res, f"offset {offset} {path}")
+
+
+@pytest.mark.parametrize("path", ["resident", "stream", "split"])
+def test_all_equal_and_single(path):
+    for N, c in [(1, 5.0), (1000, -3.25), (4096, 80.0), (9999, 0.0)]:
+        x = wl.from_values(np.full((3, N), c))
+        y, m, d, lse = _run_fwd(x, path)
+        assert np.all(np.abs(y.astype(np.float64) - 1.0 / N) <= 1e-6 + 1e-5 / N)
+        assert np.all(m == np.float32(c))
+        assert np.all(np.abs(d - N) <= 1e-5 * N)
+
+
+@pytest.mark.parametrize("path", ["resident", "stream", "split"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_special_values(path, dtype):
+    inf, nan = math.inf, math.nan
+    N = 300
+    rows = np.random.default_rng(4).standard_normal((5, N))
+    rows[0, ::3] = -inf                     # masked elements
+    rows[1, :] = -inf                       # fully masked row
+    rows[2, 17] = nan                       # NaN element
+    rows[3, 200] = inf                      # +inf element
+    x = wl.from_values(rows, dtype=dtype)
+    y, m, d, lse = _run_fwd(x, path)
+    y_ref, m_ref, d_ref, l_ref = oracle.softmax(x)
+    yf = y.astype(np.float64) if y.dtype == np.float32 else oracle.bf16_bits_to_f64(y)
+    # masked row 0 behaves like the row without the masked elements
+    check_y(y[0:1], y_ref[0:1], f"masked {path}")
+    check_m(m[0:1], m_ref[0:1])
+    check_d(d[0:1], d_ref[0:1])
+    assert np.all(yf[0, ::3] == 0)
+    # fully masked: m = -inf, d = 0, lse = -inf, y NaN
+    assert m[1] == -inf and d[1] == 0 and lse[1] == -inf
+    assert np.all(np.isnan(yf[1]))
+    # NaN / +inf rows: NaN d, lse and y, as the oracle
+    for r in (2, 3):
+        assert np.isnan(d[r]) and np.isnan(lse[r]) and np.all(np.isnan(yf[r]))
+        assert np.isnan(d_ref[r])
+    assert m[2] == m_ref[2] and m[3] == inf
+    check_y(y[4:5], y_ref[4:5], f"plain row {path}")
+
+
+@pytest.mark.parametrize("path", ["resident", "stream", "split"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_in_place(path, dtype):
+    x_h = wl.normal(6, 5000, scale=2.0, seed=12, dtype=dtype)
+    x = to_device(x_h)
+    rw.softmax_fwd(x, x, path=path)
+    torch.cuda.synchronize()
+    y_ref, *_ = oracle.softmax(x_h)
+    check_y(to_host(x), y_ref, f"in place {path} {dtype}")
+
+
+@pytest.mark.parametrize("path", ["resident", "stream", "split"])
+def test_deterministic(path):
+    x_h = wl.normal(64, 4096, seed=13)
+    a = _run_fwd(x_h, path)
+    b = _run_fwd(x_h, path)
+    for u, v in zip(a, b):
+        assert np.array_equal(u.view(np.uint32), v.view(np.uint32))
+
+
+def test_empty_rows_noop():
+    x = torch.empty((0, 16), device="cuda")
+    y = torch.empty((0, 16), device="cuda")
+    rw.softmax_fwd(x, y)
+    torch.cuda.synchronize()
+
+
+def test_adversarial_order_small():
+    # every element a new running max along the row
+    x_h = wl.ascending(8, 32768, seed=14)
+    for path in ("resident", "stream", "split"):
+        _check_all(x_h, _run_fwd(x_h, path), f"ascending {path}")
