@@ -53,7 +53,11 @@ def algorithmic_bytes(w, path, n_stats):
     return b
 
 
-def measure(w, steps, warmup, path="auto", rotate=True):
+def measure(w, steps, warmup, path="auto", rotate=True, graph=False):
+    """Average device time per step (ms), the rotation depth, and the host
+    time per launch (us).  Steps cycle over R buffer sets; with graph=True
+    the launches are captured once in a HIP graph and replayed."""
+    import numpy as np
     import torch
     import row_wise_online_amd as rw
     from row_wise_online_amd import workloads as wl
@@ -63,7 +67,6 @@ def measure(w, steps, warmup, path="auto", rotate=True):
     if w.dtype == "f32":
         x0 = torch.from_numpy(x_host).cuda()
     else:
-        import numpy as np
         x0 = torch.from_numpy(x_host.view(np.int16)).view(tdt).cuda()
     per_set = 2 * w.M * w.N * w.esize
     R = max(2, -(-ROTATE_BYTES // per_set)) if rotate else 1
@@ -75,24 +78,50 @@ def measure(w, steps, warmup, path="auto", rotate=True):
     ws_bytes = rw.workspace_bytes(w.M, w.N, w.dtype, path)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
 
-    def step(i):
-        rw.softmax_fwd(xs[i % R], ys[i % R], m=m, d=d, lse=lse, ws=ws,
-                       path=path)
+    def prepared():
+        return [rw.prepare_fwd(xs[i], ys[i], m=m, d=d, lse=lse, ws=ws,
+                               path=path) for i in range(R)]
 
-    for i in range(warmup):
-        step(i)
-    torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
-    start.record()
-    for i in range(steps):
-        step(i)
-    end.record()
-    end.synchronize()
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / steps
+    if not graph:
+        calls = prepared()
+        for i in range(warmup):
+            calls[i % R]()
+        torch.cuda.synchronize()
+        start.record()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            calls[i % R]()
+        host_us = (time.perf_counter() - t0) / steps * 1e6
+        end.record()
+        end.synchronize()
+        torch.cuda.synchronize()
+        ms = start.elapsed_time(end) / steps
+    else:
+        per_graph = R * max(1, 32 // R)
+        g = torch.cuda.CUDAGraph()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            calls = prepared()
+            for i in range(per_graph):
+                calls[i % R]()
+        reps = max(1, -(-steps // per_graph))
+        for _ in range(max(1, warmup // per_graph)):
+            g.replay()
+        torch.cuda.synchronize()
+        start.record()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            g.replay()
+        host_us = (time.perf_counter() - t0) / (reps * per_graph) * 1e6
+        end.record()
+        end.synchronize()
+        torch.cuda.synchronize()
+        ms = start.elapsed_time(end) / (reps * per_graph)
+        del g
     del xs, ys
-    return ms, R
+    return ms, R, host_us
 
 
 def copy_ceiling(nbytes, steps=50):
@@ -153,14 +182,16 @@ def traffic_record(workload):
 
 
 def run_workload(name, steps, warmup, path="auto", want_cpu=True,
-                 cpu_budget=10.0):
+                 cpu_budget=10.0, extras=True):
     import row_wise_online_amd as rw
     from row_wise_online_amd import workloads as wl
     w = wl.WORKLOADS[name]
     resolved = rw.select_path(w.M, w.N, w.dtype) if path == "auto" else path
     n_stats = len(set(w.outputs) & {"m", "d", "lse"})
-    ms, R = measure(w, steps, warmup, path)
-    warm_ms, _ = measure(w, max(10, steps // 4), 3, path, rotate=False)
+    ms, R, host_us = measure(w, steps, warmup, path)
+    if extras:
+        graph_ms, _, _ = measure(w, steps, warmup, path, graph=True)
+        warm_ms, _, _ = measure(w, max(10, steps // 4), 3, path, rotate=False)
     nbytes = algorithmic_bytes(w, resolved, n_stats)
     gbs = nbytes / (ms * 1e-3) / 1e9
     eff = (2 * w.M * w.N * w.esize + 4 * w.M * n_stats) / (ms * 1e-3) / 1e9
@@ -185,7 +216,7 @@ def run_workload(name, steps, warmup, path="auto", want_cpu=True,
         "pct_of_peak": round(100.0 * gbs / PEAK_GBS, 2),
         "rows_per_s": round(w.M / (ms * 1e-3), 1),
         "effective_single_read_GBps": round(eff, 1),
-        "warm_cache_GBps": round(nbytes / (warm_ms * 1e-3) / 1e9, 1),
+        "host_us_per_launch": round(host_us, 2),
         "roofline": {
             "bound": "hbm",
             "achieved": round(gbs, 1),
@@ -198,6 +229,9 @@ def run_workload(name, steps, warmup, path="auto", want_cpu=True,
         },
         "kernel_source": kernel_source_hash(),
     }
+    if extras:
+        rec["warm_cache_GBps"] = round(nbytes / (warm_ms * 1e-3) / 1e9, 1)
+        rec["graph_replay_GBps"] = round(nbytes / (graph_ms * 1e-3) / 1e9, 1)
     rec["copy_ceiling_GBps"] = round(
         copy_ceiling(w.M * w.N * w.esize), 1)
     if want_cpu:
@@ -219,6 +253,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true",
                     help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--no-extras", action="store_true",
+                    help="time only the headline loop and the copy "
+                         "calibration (for profiler runs)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -239,12 +276,13 @@ def main():
         for name in ["c1", "c2", "c3", "c4", "c5"]:
             print(f"[bench] workload {name}", file=sys.stderr, flush=True)
             r = run_workload(name, args.steps, args.warmup, "auto",
-                             want_cpu=False)
+                             want_cpu=False, extras=not args.no_extras)
             print(json.dumps(r), file=sys.stderr, flush=True)
     print(f"[bench] headline workload {args.workload}", file=sys.stderr,
           flush=True)
     rec = run_workload(args.workload, args.steps, args.warmup, args.path,
-                       want_cpu=not args.no_cpu, cpu_budget=args.cpu_budget)
+                       want_cpu=not args.no_cpu, cpu_budget=args.cpu_budget,
+                       extras=not args.no_extras)
     print(json.dumps(rec), flush=True)
 
 

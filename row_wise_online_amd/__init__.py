@@ -17,8 +17,8 @@ Same names as the C ABI, without the ``os_`` prefix:
 from . import _lib
 from ._lib import OsError, PATHS, PATH_NAMES  # noqa: F401
 
-__all__ = ["softmax_fwd", "softmax_stats", "state_merge", "workspace_bytes",
-           "select_path", "OsError", "load"]
+__all__ = ["softmax_fwd", "prepare_fwd", "softmax_stats", "state_merge",
+           "workspace_bytes", "select_path", "OsError", "load"]
 
 
 def load():
@@ -126,6 +126,36 @@ def softmax_fwd(x, y=None, *, m=None, d=None, lse=None, ws=None,
                                  _stream(stream))
     _lib.check("os_softmax_fwd_path", st)
     return y
+
+
+def prepare_fwd(x, y, *, m=None, d=None, lse=None, ws=None, path="auto",
+                stream=None):
+    """Marshal the arguments of one softmax_fwd call once and return a
+    function that repeats the call (same tensors, same stream) with only
+    the ctypes call left per invocation -- for tight launch loops."""
+    lib = _lib.load()
+    dt = _dtype_code(x.dtype)
+    if y.dtype != x.dtype or y.shape != x.shape:
+        raise ValueError("y must have the dtype and shape of x")
+    xp, ldx = _matrix(x, "x")
+    yp, ldy = _matrix(y, "y")
+    M, N = x.shape
+    pc = _path_code(path)
+    need = lib.os_softmax_workspace_bytes(M, N, dt, pc)
+    if need and ws is None:
+        raise ValueError(f"path needs a workspace of {need} bytes")
+    wp, wb = _workspace(ws, need, x.device)
+    args = (xp, ldx, yp, ldy, M, N, dt, _vec(m, "m", M), _vec(d, "d", M),
+            _vec(lse, "lse", M), wp, wb, pc, _stream(stream))
+    fn = lib.os_softmax_fwd_path
+    keep = (x, y, m, d, lse, ws)   # the tensors must outlive the closure
+
+    def call():
+        st = fn(*args)
+        if st:
+            _lib.check("os_softmax_fwd_path", st)
+    call.tensors = keep
+    return call
 
 
 def softmax_stats(x, m, d, lse=None, *, inc=1, ws=None, path="auto",

@@ -88,8 +88,29 @@ struct BF16 {
 // row are numbered 0, 1, ...; slot s covers elements [s*W, s*W + W) with
 // W = E or 1.  A slot that runs past N is loaded element by element with
 // -inf fill, and stored element by element.
+//
+// NT = true marks the vector accesses non-temporal (the "nt" cache policy
+// on gfx950): every byte of x and y is touched exactly once per pass, so
+// there is nothing to gain from keeping the lines in L2 / Infinity Cache.
 
-template <class Tr, bool VEC>
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+template <bool NT>
+__device__ __forceinline__ uint4 vload(const void *p) {
+    const u32x4 *q = static_cast<const u32x4 *>(p);
+    u32x4 r;
+    if constexpr (NT) r = __builtin_nontemporal_load(q); else r = *q;
+    return make_uint4(r.x, r.y, r.z, r.w);
+}
+
+template <bool NT>
+__device__ __forceinline__ void vstore(void *p, const uint4 &v) {
+    u32x4 *q = static_cast<u32x4 *>(p);
+    const u32x4 w = {v.x, v.y, v.z, v.w};
+    if constexpr (NT) __builtin_nontemporal_store(w, q); else *q = w;
+}
+
+template <class Tr, bool VEC, bool NT = false>
 struct Slot {
     static constexpr int W = VEC ? Tr::E : 1;
     using elem_t = typename Tr::elem_t;
@@ -100,8 +121,7 @@ struct Slot {
         const int j0 = s * W;
         if constexpr (VEC) {
             if (j0 + W <= N) {
-                uint4 u = *reinterpret_cast<const uint4 *>(row + j0);
-                Tr::unpack(u, f);
+                Tr::unpack(vload<NT>(row + j0), f);
             } else {
 #pragma unroll
                 for (int e = 0; e < W; ++e)
@@ -117,8 +137,7 @@ struct Slot {
                                                      float *f) {
         const int j0 = s * W;
         if constexpr (VEC) {
-            uint4 u = *reinterpret_cast<const uint4 *>(row + j0);
-            Tr::unpack(u, f);
+            Tr::unpack(vload<NT>(row + j0), f);
         } else {
             f[0] = Tr::to_f32(row[j0]);
         }
@@ -129,7 +148,7 @@ struct Slot {
         const int j0 = s * W;
         if constexpr (VEC) {
             if (j0 + W <= N) {
-                *reinterpret_cast<uint4 *>(row + j0) = Tr::pack(f);
+                vstore<NT>(row + j0, Tr::pack(f));
             } else {
 #pragma unroll
                 for (int e = 0; e < W; ++e)
@@ -144,7 +163,7 @@ struct Slot {
                                                       const float *f) {
         const int j0 = s * W;
         if constexpr (VEC) {
-            *reinterpret_cast<uint4 *>(row + j0) = Tr::pack(f);
+            vstore<NT>(row + j0, Tr::pack(f));
         } else {
             row[j0] = Tr::from_f32(f[0]);
         }

@@ -22,14 +22,14 @@ namespace os {
 // independent rows (one per wavefront, no barrier).  Each lane keeps
 // EPL = SPL * W elements in VGPRs; the row must have N <= SPL*W*64*WAVES.
 // ---------------------------------------------------------------------------
-template <class Tr, bool VEC, int WAVES, int ROWS, int SPL>
+template <class Tr, bool VEC, int WAVES, int ROWS, int SPL, bool NT = false>
 __global__ __launch_bounds__(kWave *WAVES *ROWS) void resident_kernel(
     const typename Tr::elem_t *x, int64_t ldx, typename Tr::elem_t *y,
     int64_t ldy, int64_t M, int N, float *m_out, float *d_out,
     float *lse_out) {
     static_assert(WAVES == 1 || ROWS == 1, "rows share a workgroup only "
                                            "when each row has one wave");
-    using S = Slot<Tr, VEC>;
+    using S = Slot<Tr, VEC, NT>;
     constexpr int W = S::W;
     constexpr int EPL = SPL * W;
     constexpr int STRIDE = kWave * WAVES;  // slots between a lane's slots
@@ -88,13 +88,92 @@ __global__ __launch_bounds__(kWave *WAVES *ROWS) void resident_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Persistent variant of the resident path ("5.2 CUDA Online Softmax 实现优化"
+// §7: a fixed grid walks the rows with a grid stride, here combined with the
+// register-resident row of §6).  While row r is reduced and written, the
+// loads of the wavefront's next row r + stride are already in flight, so
+// the memory pipe never drains between rows.  WAVES wavefronts share a row;
+// with WAVES == 1 each of the ROWS wavefronts of a workgroup walks its own
+// rows.  The cross-wave LDS cells are double-buffered by iteration parity:
+// the barrier of iteration i+1 orders the reads of cells (i & 1) before any
+// wave writes them again in iteration i+2.
+// ---------------------------------------------------------------------------
+template <class Tr, bool VEC, int WAVES, int ROWS, int SPL, bool NT>
+__global__ __launch_bounds__(kWave *WAVES *ROWS) void resident_persistent_kernel(
+    const typename Tr::elem_t *x, int64_t ldx, typename Tr::elem_t *y,
+    int64_t ldy, int64_t M, int N, float *m_out, float *d_out,
+    float *lse_out) {
+    static_assert(WAVES == 1 || ROWS == 1, "rows share a workgroup only "
+                                           "when each row has one wave");
+    using S = Slot<Tr, VEC, NT>;
+    constexpr int W = S::W;
+    constexpr int EPL = SPL * W;
+    constexpr int STRIDE = kWave * WAVES;
+    __shared__ float2 lds[2][WAVES];
+
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int wr = (ROWS > 1) ? 0 : wave;
+    const int64_t first = (ROWS > 1) ? static_cast<int64_t>(blockIdx.x) * ROWS + wave
+                                     : static_cast<int64_t>(blockIdx.x);
+    const int64_t step = static_cast<int64_t>(gridDim.x) * ROWS;
+    const int base = wr * kWave + lane;
+    const bool full = (N == SPL * W * STRIDE);
+
+    auto load_row = [&](int64_t row, float *v) {
+        const typename Tr::elem_t *xr = x + row * ldx;
+        if (full) {
+#pragma unroll
+            for (int k = 0; k < SPL; ++k) S::load_full(xr, k * STRIDE + base, &v[k * W]);
+        } else {
+#pragma unroll
+            for (int k = 0; k < SPL; ++k) S::load(xr, k * STRIDE + base, N, &v[k * W]);
+        }
+    };
+
+    if (first >= M) return;  // (ROWS > 1 only: a whole wavefront without rows)
+    float cur[EPL], nxt[EPL];
+    load_row(first, cur);
+    int it = 0;
+    for (int64_t row = first; row < M; row += step, ++it) {
+        const int64_t rn = row + step;
+        if (rn < M) load_row(rn, nxt);
+
+        float m = kNegInf, d = 0.0f;
+        fold_chunk<EPL>(m, d, cur);
+        State st = wave_merge(m, d);
+        st = block_merge<WAVES>(st, wr, lane, lds[it & 1]);
+
+        const float r = safe_ref(st.m);
+        const float inv = 1.0f / st.d;
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) cur[i] = exp_shifted(cur[i] - r) * inv;
+        typename Tr::elem_t *yr = y + row * ldy;
+        if (full) {
+#pragma unroll
+            for (int k = 0; k < SPL; ++k) S::store_full(yr, k * STRIDE + base, &cur[k * W]);
+        } else {
+#pragma unroll
+            for (int k = 0; k < SPL; ++k) S::store(yr, k * STRIDE + base, N, &cur[k * W]);
+        }
+        if (wr == 0 && lane == 0) {
+            if (m_out) m_out[row] = st.m;
+            if (d_out) d_out[row] = st.d;
+            if (lse_out) lse_out[row] = st.m + __builtin_logf(st.d);
+        }
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) cur[i] = nxt[i];
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Streaming building blocks: a workgroup of WAVES wavefronts walks a range
 // of n elements in tiles of U slots per lane.  The next tile's loads are
 // issued before the current tile is consumed (two tiles of registers).
 // ---------------------------------------------------------------------------
-template <class Tr, bool VEC, int WAVES, int U>
+template <class Tr, bool VEC, int WAVES, int U, bool NT = false>
 struct Tiles {
-    using S = Slot<Tr, VEC>;
+    using S = Slot<Tr, VEC, NT>;
     using elem_t = typename Tr::elem_t;
     static constexpr int W = S::W;
     static constexpr int K = U * W;               // elements per lane per tile
@@ -170,12 +249,12 @@ struct Tiles {
 // Streaming two-read path: one workgroup per row.  With WRITE_Y false it is
 // the pass-1-only statistics kernel (states written with stride inc_out).
 // ---------------------------------------------------------------------------
-template <class Tr, bool VEC, int WAVES, int U, bool WRITE_Y>
+template <class Tr, bool VEC, int WAVES, int U, bool WRITE_Y, bool NT = false>
 __global__ __launch_bounds__(kWave *WAVES) void stream_kernel(
     const typename Tr::elem_t *x, int64_t ldx, typename Tr::elem_t *y,
     int64_t ldy, int64_t M, int N, float *m_out, float *d_out,
     int64_t inc_out, float *lse_out) {
-    using T = Tiles<Tr, VEC, WAVES, U>;
+    using T = Tiles<Tr, VEC, WAVES, U, NT>;
     __shared__ float2 lds[WAVES];
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
@@ -205,11 +284,11 @@ __global__ __launch_bounds__(kWave *WAVES) void stream_kernel(
 // partial results).  Row i is cut into P chunks of C elements (the last one
 // shorter); workgroup b handles row b / P, chunk b % P.
 // ---------------------------------------------------------------------------
-template <class Tr, bool VEC, int WAVES, int U>
+template <class Tr, bool VEC, int WAVES, int U, bool NT = false>
 __global__ __launch_bounds__(kWave *WAVES) void split_partial_kernel(
     const typename Tr::elem_t *x, int64_t ldx, int N, int P, int C,
     float *ws_m, float *ws_d) {
-    using T = Tiles<Tr, VEC, WAVES, U>;
+    using T = Tiles<Tr, VEC, WAVES, U, NT>;
     __shared__ float2 lds[WAVES];
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
@@ -229,12 +308,12 @@ __global__ __launch_bounds__(kWave *WAVES) void split_partial_kernel(
     }
 }
 
-template <class Tr, bool VEC, int WAVES, int U>
+template <class Tr, bool VEC, int WAVES, int U, bool NT = false>
 __global__ __launch_bounds__(kWave *WAVES) void split_normalize_kernel(
     const typename Tr::elem_t *x, int64_t ldx, typename Tr::elem_t *y,
     int64_t ldy, int N, int P, int C, const float *row_m,
     const float *row_d, int64_t inc) {
-    using T = Tiles<Tr, VEC, WAVES, U>;
+    using T = Tiles<Tr, VEC, WAVES, U, NT>;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
     const int64_t b = blockIdx.x;

@@ -44,7 +44,7 @@ void run(const FwdArgs &a, void *ws) {
     const dim3 block(kWave * kSplitWaves);
     const E *x = static_cast<const E *>(a.x);
 
-    split_partial_kernel<Tr, VEC, kSplitWaves, U><<<grid, block, 0, a.stream>>>(
+    split_partial_kernel<Tr, VEC, kSplitWaves, U, true><<<grid, block, 0, a.stream>>>(
         x, a.ldx, a.N, plan.P, plan.C, l.part_m, l.part_d);
 
     // Row states go to the workspace (read by the normalise kernel) and to
@@ -54,7 +54,7 @@ void run(const FwdArgs &a, void *ws) {
                        a.stream);
 
     if (a.y) {
-        split_normalize_kernel<Tr, VEC, kSplitWaves, U><<<grid, block, 0, a.stream>>>(
+        split_normalize_kernel<Tr, VEC, kSplitWaves, U, true><<<grid, block, 0, a.stream>>>(
             x, a.ldx, static_cast<E *>(a.y), a.ldy, a.N, plan.P, plan.C,
             l.row_m, l.row_d, 1);
     }

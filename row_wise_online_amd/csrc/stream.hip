@@ -23,11 +23,11 @@ void run(const FwdArgs &a) {
     const dim3 block(kWave * kStreamWaves);
     const E *x = static_cast<const E *>(a.x);
     if (a.y) {
-        stream_kernel<Tr, VEC, kStreamWaves, U, true><<<grid, block, 0, a.stream>>>(
+        stream_kernel<Tr, VEC, kStreamWaves, U, true, true><<<grid, block, 0, a.stream>>>(
             x, a.ldx, static_cast<E *>(a.y), a.ldy, a.M, a.N, a.m_out, a.d_out,
             a.inc_out, a.lse_out);
     } else {
-        stream_kernel<Tr, VEC, kStreamWaves, U, false><<<grid, block, 0, a.stream>>>(
+        stream_kernel<Tr, VEC, kStreamWaves, U, false, true><<<grid, block, 0, a.stream>>>(
             x, a.ldx, nullptr, 0, a.M, a.N, a.m_out, a.d_out, a.inc_out,
             a.lse_out);
     }
