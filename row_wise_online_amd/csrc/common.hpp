@@ -11,13 +11,46 @@ constexpr int kWave = 64;                    // CDNA wavefront width
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInf = -__builtin_huge_valf();
 
-// e^t for t = x - m, computed as 2^(t * log2 e).  The subtraction x - m is
-// done first by the caller (exact when x is near m), then scaled; folding
-// -m * log2 e into an fma would lose the low bits of large maxima.
-// __builtin_exp2f lowers to v_exp_f32 with a range fix-up that keeps
-// results in the fp32 subnormal range accurate.
+// Exponentials are evaluated as 2^(t * log2 e) with t = x - m formed first
+// (exact when x is near m) and then scaled; folding -m * log2 e into an fma
+// would lose the low bits of large maxima.
+//
+// exp2_fast is the bare v_exp_f32: results below 2^-126 come out as zero.
+// That loses nothing in a sum that already holds a term of 1 (the max), and
+// stays within the fp32 output tolerance, but a bf16 output can still
+// represent values down to 2^-133, so bf16 outputs use exp2_full whenever
+// an argument falls below -126 (see any_may_underflow).
+__device__ __forceinline__ float exp2_fast(float t) {
+    return __builtin_amdgcn_exp2f(t);
+}
+// exp2_full: __builtin_exp2f lowers to v_exp_f32 plus a range fix-up that
+// keeps results in the fp32 subnormal range accurate.
+__device__ __forceinline__ float exp2_full(float t) {
+    return __builtin_exp2f(t);
+}
+// Accurate e^t, used for the per-lane and per-row correction factors.
 __device__ __forceinline__ float exp_shifted(float t) {
-    return __builtin_exp2f(t * kLog2e);
+    return exp2_full(t * kLog2e);
+}
+
+// True if some t[k] lies in (-inf, -126), where exp2_fast would flush a
+// subnormal result.  On the bit patterns: t in (-inf, -126) exactly when
+// bits(t) - bits(-126) - 1 < bits(-inf) - bits(-126) - 1 as unsigned
+// integers (NaN, -inf, zero and t >= -126 all land above the bound), so one
+// subtract and a running unsigned min per value decide it.
+template <int K>
+__device__ __forceinline__ bool lane_may_underflow(const float *t) {
+    constexpr uint32_t kLo = 0xC2FC0001u;            // just below -126.0f
+    constexpr uint32_t kSpan = 0xFF800000u - kLo;    // up to -inf, exclusive
+    uint32_t mn = 0xFFFFFFFFu;
+#pragma unroll
+    for (int k = 0; k < K; ++k) mn = min(mn, __float_as_uint(t[k]) - kLo);
+    return mn < kSpan;
+}
+
+// Wavefront-uniform OR of a per-lane predicate (a scalar result).
+__device__ __forceinline__ bool wave_any(bool p) {
+    return __builtin_amdgcn_ballot_w64(p) != 0;
 }
 
 // The reference point used for exponents: the max itself, or 0 when the
@@ -35,6 +68,7 @@ __device__ __forceinline__ float safe_ref(float m) {
 struct F32 {
     using elem_t = float;
     static constexpr int E = 4;
+    static constexpr bool kExactTiny = false;  // fp32 y below 2^-126 may be 0
     __device__ __forceinline__ static float to_f32(float v) { return v; }
     __device__ __forceinline__ static float from_f32(float v) { return v; }
     __device__ __forceinline__ static void unpack(const uint4 &u, float *f) {
@@ -55,6 +89,7 @@ struct F32 {
 struct BF16 {
     using elem_t = uint16_t;
     static constexpr int E = 8;
+    static constexpr bool kExactTiny = true;   // keep bf16 subnormal outputs
     __device__ __forceinline__ static float to_f32(uint16_t b) {
         return __uint_as_float(static_cast<uint32_t>(b) << 16);
     }

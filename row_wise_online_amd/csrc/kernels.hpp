@@ -61,17 +61,21 @@ __global__ __launch_bounds__(kWave *WAVES *ROWS) void resident_kernel(
         for (int k = 0; k < SPL; ++k) S::load(xr, k * STRIDE + base, N, &v[k * W]);
     }
 
-    // pass 1: lane fold -> wavefront merge -> cross-wave merge
-    float m = kNegInf, d = 0.0f;
-    fold_chunk<EPL>(m, d, v);
-    State st = wave_merge(m, d);
+    // pass 1: lane fold -> wavefront merge -> cross-wave merge.  The lane's
+    // state is that of its EPL resident values: m_l = their max and
+    // d_l = sum_i e^(v_i - m_l).  The terms e^(v_i - m_l) stay in registers.
+    const float ml = tree_max<EPL>(v);
+    const float rl = safe_ref(ml);
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) v[i] = (v[i] - rl) * kLog2e;
+    exp2_inplace<Tr::kExactTiny, EPL>(v);
+    State st = wave_merge(ml, tree_sum<EPL>(v));
     st = block_merge<WAVES>(st, wr, lane, lds);
 
-    // pass 2 from registers
-    const float r = safe_ref(st.m);
-    const float inv = 1.0f / st.d;
+    // pass 2 from registers: e^(x - m) / d = e^(x - m_l) * (e^(m_l - m) / d)
+    const float scale = exp_shifted(ml - safe_ref(st.m)) * (1.0f / st.d);
 #pragma unroll
-    for (int i = 0; i < EPL; ++i) v[i] = exp_shifted(v[i] - r) * inv;
+    for (int i = 0; i < EPL; ++i) v[i] *= scale;
     if (full) {
 #pragma unroll
         for (int k = 0; k < SPL; ++k) S::store_full(yr, k * STRIDE + base, &v[k * W]);
@@ -139,15 +143,17 @@ __global__ __launch_bounds__(kWave *WAVES *ROWS) void resident_persistent_kernel
         const int64_t rn = row + step;
         if (rn < M) load_row(rn, nxt);
 
-        float m = kNegInf, d = 0.0f;
-        fold_chunk<EPL>(m, d, cur);
-        State st = wave_merge(m, d);
+        const float ml = tree_max<EPL>(cur);
+        const float rl = safe_ref(ml);
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) cur[i] = (cur[i] - rl) * kLog2e;
+        exp2_inplace<Tr::kExactTiny, EPL>(cur);
+        State st = wave_merge(ml, tree_sum<EPL>(cur));
         st = block_merge<WAVES>(st, wr, lane, lds[it & 1]);
 
-        const float r = safe_ref(st.m);
-        const float inv = 1.0f / st.d;
+        const float scale = exp_shifted(ml - safe_ref(st.m)) * (1.0f / st.d);
 #pragma unroll
-        for (int i = 0; i < EPL; ++i) cur[i] = exp_shifted(cur[i] - r) * inv;
+        for (int i = 0; i < EPL; ++i) cur[i] *= scale;
         typename Tr::elem_t *yr = y + row * ldy;
         if (full) {
 #pragma unroll
@@ -237,7 +243,10 @@ struct Tiles {
         for (int t = 0; t < nt; ++t) {
             if (t + 1 < nt) load_tile(p, t + 1, base, n, tile_full(t + 1, n), nxt);
 #pragma unroll
-            for (int i = 0; i < K; ++i) cur[i] = exp_shifted(cur[i] - r) * inv;
+            for (int i = 0; i < K; ++i) cur[i] = (cur[i] - r) * kLog2e;
+            exp2_inplace<Tr::kExactTiny, K>(cur);
+#pragma unroll
+            for (int i = 0; i < K; ++i) cur[i] *= inv;
             store_tile(q, t, base, n, tile_full(t, n), cur);
 #pragma unroll
             for (int i = 0; i < K; ++i) cur[i] = nxt[i];

@@ -93,15 +93,43 @@ __device__ __forceinline__ float tree_max(const float *v) {
     }
 }
 
-// Sum of e^(v[k] - r), pairwise (depth log2 K) for accuracy and ILP.
+template <int K>
+__device__ __forceinline__ float tree_sum(const float *v) {
+    if constexpr (K == 1) {
+        return v[0];
+    } else {
+        constexpr int H = K / 2;
+        return tree_sum<H>(v) + tree_sum<K - H>(v + H);
+    }
+}
+
+// Sum of e^(v[k] - r), pairwise (depth log2 K) for accuracy and ILP.  The
+// terms may flush below 2^-126: next to the term of the max (1) they are
+// far below the sum's rounding.
 template <int K>
 __device__ __forceinline__ float tree_sum_exp(const float *v, float r) {
     if constexpr (K == 1) {
-        return exp_shifted(v[0] - r);
+        return exp2_fast((v[0] - r) * kLog2e);
     } else {
         constexpr int H = K / 2;
         return tree_sum_exp<H>(v, r) + tree_sum_exp<K - H>(v + H, r);
     }
+}
+
+// t[k] <- 2^t[k] in place.  With EXACT_TINY a wavefront whose arguments
+// reach below -126 takes the subnormal-exact exponential (a uniform
+// branch); otherwise the bare v_exp_f32.
+template <bool EXACT_TINY, int K>
+__device__ __forceinline__ void exp2_inplace(float *t) {
+    if constexpr (EXACT_TINY) {
+        if (wave_any(lane_may_underflow<K>(t))) {
+#pragma unroll
+            for (int k = 0; k < K; ++k) t[k] = exp2_full(t[k]);
+            return;
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < K; ++k) t[k] = exp2_fast(t[k]);
 }
 
 // ---- the lane fold ----------------------------------------------------------
@@ -113,7 +141,7 @@ __device__ __forceinline__ void fold_chunk(float &m, float &d, const float *v) {
     const float mn = fmaxf(m, tree_max<K>(v));
     const float r = safe_ref(mn);
     const float s = tree_sum_exp<K>(v, r);
-    d = d * exp_shifted(m - r) + s;
+    d = d * exp2_fast((m - r) * kLog2e) + s;
     m = mn;
 }
 

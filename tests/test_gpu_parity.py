@@ -337,3 +337,18 @@ def test_adversarial_order_small():
     x_h = wl.ascending(8, 32768, seed=14)
     for path in ("resident", "stream", "split"):
         _check_all(x_h, _run_fwd(x_h, path), f"ascending {path}")
+
+
+@pytest.mark.parametrize("path", ["resident", "stream", "split"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_wide_range_rows_keep_subnormal_outputs(path, dtype):
+    # rows spanning ~0 .. -95: e^(x - m) reaches below 2^-126, where bf16
+    # still has subnormals down to 2^-133; bf16 outputs must stay within one
+    # step there, fp32 outputs within the absolute tolerance
+    rng = np.random.default_rng(15)
+    N = 3000
+    rows = -95.0 * rng.random((4, N))
+    rows[:, 7] = 0.0
+    rows[1] = np.sort(rows[1])          # ascending: every value a new max
+    x = wl.from_values(rows, dtype=dtype)
+    _check_all(x, _run_fwd(x, path), f"wide range {path} {dtype}")
