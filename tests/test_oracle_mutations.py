@@ -1,0 +1,54 @@
+"""Plant mistakes in the oracle (on the CPU) and check that its pins catch
+each one: the oracle source is copied, one plausible slip is introduced,
+the copy is built into a temporary library, and the pin suite is run
+against it in a subprocess; it must fail.
+"""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "oracle.c")
+
+MUTATIONS = {
+    "dropped correction factor":
+        ("d = d * corr + exp(v - m_new);", "d = d + exp(v - m_new);"),
+    "exponent sign flipped":
+        ("double t = (v == -INFINITY) ? 0.0 : exp(v - m);",
+         "double t = (v == -INFINITY) ? 0.0 : exp(m - v);"),
+    "row stride replaced by N":
+        ("double v = load_elem(x, dtype, i * ld + j);",
+         "double v = load_elem(x, dtype, i * N + j);"),
+    "identity guard lost":
+        ("if (m == -INFINITY) {", "if (0) {"),
+    "merge rescale of b dropped":
+        ("*d_out = da * exp(ma - m) + db * exp(mb - m);",
+         "*d_out = da * exp(ma - m) + db;"),
+    "lse without m":
+        ("if (lse_out) lse_out[i] = m + log(d);",
+         "if (lse_out) lse_out[i] = log(d);"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_pins_catch_planted_mistake(name, tmp_path):
+    old, new = MUTATIONS[name]
+    src = open(SRC).read()
+    assert src.count(old) >= 1, f"mutation site not found: {old}"
+    mutated = tmp_path / "oracle.c"
+    mutated.write_text(src.replace(old, new))
+    (tmp_path / "oracle.h").write_text(
+        open(os.path.join(ROOT, "oracle", "oracle.h")).read())
+    lib = tmp_path / "liboracle_mut.so"
+    subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared",
+                    "-ffp-contract=off", "-o", str(lib), str(mutated), "-lm"],
+                   check=True)
+    env = dict(os.environ, ORACLE_LIB=str(lib))
+    r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x",
+                        "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle.py")],
+                       cwd=ROOT, env=env, capture_output=True, text=True,
+                       timeout=600)
+    assert r.returncode != 0, f"pins did not catch: {name}\n{r.stdout[-2000:]}"
