@@ -242,8 +242,9 @@ def run_workload(name, steps, warmup, path="auto", want_cpu=True,
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=400)
-    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--steps", type=int, default=1000)
+    # the clocks take ~10 ms of sustained launches to settle after setup
+    ap.add_argument("--warmup", type=int, default=2000)
     ap.add_argument("--workload", default="c2",
                     choices=["c1", "c2", "c3", "c4", "c5"])
     ap.add_argument("--path", default="auto",

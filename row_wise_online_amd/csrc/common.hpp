@@ -124,9 +124,9 @@ struct BF16 {
 // W = E or 1.  A slot that runs past N is loaded element by element with
 // -inf fill, and stored element by element.
 //
-// NT = true marks the vector accesses non-temporal (the "nt" cache policy
-// on gfx950): every byte of x and y is touched exactly once per pass, so
-// there is nothing to gain from keeping the lines in L2 / Infinity Cache.
+// NTL / NTS mark the vector loads / stores non-temporal (the "nt" cache
+// policy on gfx950): where every byte is touched once, there is nothing to
+// gain from keeping the lines in L2 / Infinity Cache.
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -145,7 +145,7 @@ __device__ __forceinline__ void vstore(void *p, const uint4 &v) {
     if constexpr (NT) __builtin_nontemporal_store(w, q); else *q = w;
 }
 
-template <class Tr, bool VEC, bool NT = false>
+template <class Tr, bool VEC, bool NTL = false, bool NTS = NTL>
 struct Slot {
     static constexpr int W = VEC ? Tr::E : 1;
     using elem_t = typename Tr::elem_t;
@@ -156,7 +156,7 @@ struct Slot {
         const int j0 = s * W;
         if constexpr (VEC) {
             if (j0 + W <= N) {
-                Tr::unpack(vload<NT>(row + j0), f);
+                Tr::unpack(vload<NTL>(row + j0), f);
             } else {
 #pragma unroll
                 for (int e = 0; e < W; ++e)
@@ -172,7 +172,7 @@ struct Slot {
                                                      float *f) {
         const int j0 = s * W;
         if constexpr (VEC) {
-            Tr::unpack(vload<NT>(row + j0), f);
+            Tr::unpack(vload<NTL>(row + j0), f);
         } else {
             f[0] = Tr::to_f32(row[j0]);
         }
@@ -183,7 +183,7 @@ struct Slot {
         const int j0 = s * W;
         if constexpr (VEC) {
             if (j0 + W <= N) {
-                vstore<NT>(row + j0, Tr::pack(f));
+                vstore<NTS>(row + j0, Tr::pack(f));
             } else {
 #pragma unroll
                 for (int e = 0; e < W; ++e)
@@ -198,7 +198,7 @@ struct Slot {
                                                       const float *f) {
         const int j0 = s * W;
         if constexpr (VEC) {
-            vstore<NT>(row + j0, Tr::pack(f));
+            vstore<NTS>(row + j0, Tr::pack(f));
         } else {
             row[j0] = Tr::from_f32(f[0]);
         }

@@ -177,9 +177,10 @@ __global__ __launch_bounds__(kWave *WAVES *ROWS) void resident_persistent_kernel
 // of n elements in tiles of U slots per lane.  The next tile's loads are
 // issued before the current tile is consumed (two tiles of registers).
 // ---------------------------------------------------------------------------
-template <class Tr, bool VEC, int WAVES, int U, bool NT = false>
+template <class Tr, bool VEC, int WAVES, int U, bool NTL = false,
+          bool NTS = NTL>
 struct Tiles {
-    using S = Slot<Tr, VEC, NT>;
+    using S = Slot<Tr, VEC, NTL, NTS>;
     using elem_t = typename Tr::elem_t;
     static constexpr int W = S::W;
     static constexpr int K = U * W;               // elements per lane per tile
@@ -234,36 +235,55 @@ struct Tiles {
 
     // Pass 2 over [0, n): y = e^(x - r) * inv.  Tile t+1 is read before tile
     // t is written, which is safe in place (they are different elements).
+    // REV walks the tiles last to first: after a pass 1 that went first to
+    // last, the most recently read lines come first, while they are most
+    // likely still in the Infinity Cache.
+    template <bool REV = false>
     __device__ __forceinline__ static void normalize(const elem_t *p, elem_t *q,
                                                      int n, int base, float r,
                                                      float inv) {
         const int nt = num_tiles(n);
         float cur[K], nxt[K];
-        load_tile(p, 0, base, n, tile_full(0, n), cur);
-        for (int t = 0; t < nt; ++t) {
-            if (t + 1 < nt) load_tile(p, t + 1, base, n, tile_full(t + 1, n), nxt);
+        const int t0 = REV ? nt - 1 : 0;
+        load_tile(p, t0, base, n, tile_full(t0, n), cur);
+        for (int i = 0; i < nt; ++i) {
+            const int t = REV ? nt - 1 - i : i;
+            const int tn = REV ? t - 1 : t + 1;
+            if (i + 1 < nt) load_tile(p, tn, base, n, tile_full(tn, n), nxt);
 #pragma unroll
-            for (int i = 0; i < K; ++i) cur[i] = (cur[i] - r) * kLog2e;
+            for (int k = 0; k < K; ++k) cur[k] = (cur[k] - r) * kLog2e;
             exp2_inplace<Tr::kExactTiny, K>(cur);
 #pragma unroll
-            for (int i = 0; i < K; ++i) cur[i] *= inv;
+            for (int k = 0; k < K; ++k) cur[k] *= inv;
             store_tile(q, t, base, n, tile_full(t, n), cur);
 #pragma unroll
-            for (int i = 0; i < K; ++i) cur[i] = nxt[i];
+            for (int k = 0; k < K; ++k) cur[k] = nxt[k];
         }
     }
 };
 
 // ---------------------------------------------------------------------------
+// Cache policy of the two-read paths: non-temporal pass-1 loads, pass-2
+// loads and pass-2 stores, and the pass-2 tile order (REV: last tile first).
+// ---------------------------------------------------------------------------
+template <bool NT1, bool NT2, bool NTS, bool REV>
+struct TwoPass {
+    static constexpr bool nt1 = NT1, nt2 = NT2, nts = NTS, rev = REV;
+};
+using StreamingNT = TwoPass<true, true, true, false>;
+
+// ---------------------------------------------------------------------------
 // Streaming two-read path: one workgroup per row.  With WRITE_Y false it is
 // the pass-1-only statistics kernel (states written with stride inc_out).
 // ---------------------------------------------------------------------------
-template <class Tr, bool VEC, int WAVES, int U, bool WRITE_Y, bool NT = false>
+template <class Tr, bool VEC, int WAVES, int U, bool WRITE_Y,
+          class Pol = StreamingNT>
 __global__ __launch_bounds__(kWave *WAVES) void stream_kernel(
     const typename Tr::elem_t *x, int64_t ldx, typename Tr::elem_t *y,
     int64_t ldy, int64_t M, int N, float *m_out, float *d_out,
     int64_t inc_out, float *lse_out) {
-    using T = Tiles<Tr, VEC, WAVES, U, NT>;
+    using T = Tiles<Tr, VEC, WAVES, U, Pol::nt1>;
+    using T2 = Tiles<Tr, VEC, WAVES, U, Pol::nt2, Pol::nts>;
     __shared__ float2 lds[WAVES];
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
@@ -277,7 +297,8 @@ __global__ __launch_bounds__(kWave *WAVES) void stream_kernel(
     st = block_merge<WAVES>(st, wave, lane, lds);
 
     if constexpr (WRITE_Y) {
-        T::normalize(xr, y + row * ldy, N, base, safe_ref(st.m), 1.0f / st.d);
+        T2::template normalize<Pol::rev>(xr, y + row * ldy, N, base,
+                                         safe_ref(st.m), 1.0f / st.d);
     }
     if (threadIdx.x == 0) {
         const int64_t o = row * inc_out;
@@ -293,11 +314,11 @@ __global__ __launch_bounds__(kWave *WAVES) void stream_kernel(
 // partial results).  Row i is cut into P chunks of C elements (the last one
 // shorter); workgroup b handles row b / P, chunk b % P.
 // ---------------------------------------------------------------------------
-template <class Tr, bool VEC, int WAVES, int U, bool NT = false>
+template <class Tr, bool VEC, int WAVES, int U, class Pol = StreamingNT>
 __global__ __launch_bounds__(kWave *WAVES) void split_partial_kernel(
     const typename Tr::elem_t *x, int64_t ldx, int N, int P, int C,
     float *ws_m, float *ws_d) {
-    using T = Tiles<Tr, VEC, WAVES, U, NT>;
+    using T = Tiles<Tr, VEC, WAVES, U, Pol::nt1>;
     __shared__ float2 lds[WAVES];
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
@@ -317,12 +338,12 @@ __global__ __launch_bounds__(kWave *WAVES) void split_partial_kernel(
     }
 }
 
-template <class Tr, bool VEC, int WAVES, int U, bool NT = false>
+template <class Tr, bool VEC, int WAVES, int U, class Pol = StreamingNT>
 __global__ __launch_bounds__(kWave *WAVES) void split_normalize_kernel(
     const typename Tr::elem_t *x, int64_t ldx, typename Tr::elem_t *y,
     int64_t ldy, int N, int P, int C, const float *row_m,
     const float *row_d, int64_t inc) {
-    using T = Tiles<Tr, VEC, WAVES, U, NT>;
+    using T = Tiles<Tr, VEC, WAVES, U, Pol::nt2, Pol::nts>;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
     const int64_t b = blockIdx.x;
@@ -332,8 +353,9 @@ __global__ __launch_bounds__(kWave *WAVES) void split_normalize_kernel(
     const int n = min(C, N - c0);
     const float m = row_m[row * inc];
     const float d = row_d[row * inc];
-    T::normalize(x + row * ldx + c0, y + row * ldy + c0, n, wave * kWave + lane,
-                 safe_ref(m), 1.0f / d);
+    T::template normalize<Pol::rev>(x + row * ldx + c0, y + row * ldy + c0,
+                                    n, wave * kWave + lane, safe_ref(m),
+                                    1.0f / d);
 }
 
 // ---------------------------------------------------------------------------

@@ -352,3 +352,27 @@ def test_wide_range_rows_keep_subnormal_outputs(path, dtype):
     rows[1] = np.sort(rows[1])          # ascending: every value a new max
     x = wl.from_values(rows, dtype=dtype)
     _check_all(x, _run_fwd(x, path), f"wide range {path} {dtype}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("N", [17000, 32768])
+def test_resident_row_loop_many_rows(dtype, N):
+    # more rows than the persistent grid: workgroups walk 2-3 rows each with
+    # the next row's loads in flight; check rows on both sides of the grid
+    # stride and every row's sum
+    M = 1100
+    x_h = wl.normal(M, N, scale=2.0, seed=16, dtype=dtype)
+    x = to_device(x_h)
+    y = torch.empty_like(x)
+    m = torch.empty(M, device="cuda")
+    d = torch.empty(M, device="cuda")
+    rw.softmax_fwd(x, y, m=m, d=d, path="resident")
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 511, 512, 513, 587, 1023, 1024, 1025, 1099])
+    xs = np.ascontiguousarray(x_h[rows])
+    y_ref, m_ref, d_ref, _ = oracle.softmax(xs)
+    check_y(to_host(y[torch.as_tensor(rows, device="cuda")]), y_ref, "row loop")
+    check_m(m.cpu().numpy()[rows], m_ref)
+    check_d(d.cpu().numpy()[rows], d_ref)
+    tol = 2.0 ** -7 if dtype == "bf16" else 1e-4
+    assert np.all(np.abs(y.double().sum(dim=1).cpu().numpy() - 1.0) < tol)
