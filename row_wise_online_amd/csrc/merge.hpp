@@ -165,9 +165,23 @@ __device__ __forceinline__ State wave_merge(float m, float d) {
 }
 
 // ---- the cross-wave merge through LDS -------------------------------------
-// W wave states of one row -> LDS -> one barrier -> every wave merges the W
-// states in the same fixed order, so all lanes of the workgroup hold the
-// identical row state.  The LDS cells are written once per launch.
+// W wave states of one row -> LDS -> one barrier.  Then lane w < W of every
+// wave holds state w (the rest hold the identity) and the n-ary merge runs
+// across those lanes: a max over the first W lanes, one correction
+// exponential per lane, a sum over the first W lanes (log2 W DPP butterfly
+// steps each), and a v_readlane of lane 0 makes the row state wave-uniform.
+// Every wave computes the same bits, so all lanes of the workgroup hold the
+// identical row state.
+template <int W, class Op>
+__device__ __forceinline__ float first_lanes_allreduce(float v, Op op) {
+    static_assert(W == 2 || W == 4 || W == 8 || W == 16, "2..16 waves");
+    v = op(v, dpp_move<kDppQuadXor1>(v));
+    if constexpr (W >= 4) v = op(v, dpp_move<kDppQuadXor2>(v));
+    if constexpr (W >= 8) v = op(v, dpp_move<kDppRowHalfMirror>(v));
+    if constexpr (W >= 16) v = op(v, dpp_move<kDppRowMirror>(v));
+    return read_lane(v, 0);
+}
+
 template <int W>
 __device__ __forceinline__ State block_merge(State s, int wave, int lane,
                                              float2 *lds) {
@@ -176,16 +190,11 @@ __device__ __forceinline__ State block_merge(State s, int wave, int lane,
     } else {
         if (lane == 0) lds[wave] = make_float2(s.m, s.d);
         __syncthreads();
-        float2 st[W];
-#pragma unroll
-        for (int w = 0; w < W; ++w) st[w] = lds[w];
-        float m = st[0].x;
-#pragma unroll
-        for (int w = 1; w < W; ++w) m = fmaxf(m, st[w].x);
+        const float2 mine = (lane < W) ? lds[lane] : make_float2(kNegInf, 0.0f);
+        const float m = first_lanes_allreduce<W>(mine.x, OpMax{});
         const float r = safe_ref(m);
-        float d = 0.0f;
-#pragma unroll
-        for (int w = 0; w < W; ++w) d += st[w].y * exp_shifted(st[w].x - r);
+        const float e = mine.y * exp_shifted(mine.x - r);
+        const float d = first_lanes_allreduce<W>(e, OpAdd{});
         return {m, d};
     }
 }
