@@ -40,6 +40,11 @@ def _load():
         lib.oracle_merge2.restype = None
         lib.oracle_merge.argtypes = [dp, dp, i64, i64, i64, dp, dp, dp]
         lib.oracle_merge.restype = i32
+        lib.oracle_log_softmax.argtypes = [vp, i64, i64, i64, i32, dp]
+        lib.oracle_log_softmax.restype = i32
+        lib.oracle_cross_entropy.argtypes = [vp, i64, i64, i64, i32, vp, dp,
+                                             dp]
+        lib.oracle_cross_entropy.restype = i32
         _lib = lib
     return _lib
 
@@ -123,6 +128,36 @@ def merge(m_in, d_in):
     if rc != 0:
         raise ValueError("oracle_merge rejected its arguments")
     return m, d, lse
+
+
+def log_softmax(x):
+    """log p = z - LSE(z) for every row of ``x`` (fp64 [M, N])."""
+    x, code = _as_input(x)
+    M, N = x.shape
+    ld = x.strides[0] // x.itemsize
+    y = np.empty((M, N), np.float64)
+    rc = _load().oracle_log_softmax(_ptr(x), ld, M, N, code, _ptr(y))
+    if rc != 0:
+        raise ValueError("oracle_log_softmax rejected its arguments")
+    return y
+
+
+def cross_entropy(x, labels):
+    """Per-row cross-entropy (fp64 [M]) and the mean over rows whose
+    label is not negative."""
+    x, code = _as_input(x)
+    M, N = x.shape
+    ld = x.strides[0] // x.itemsize
+    labels = np.ascontiguousarray(labels, dtype=np.int64)
+    if labels.shape != (M,):
+        raise ValueError("one label per row")
+    loss = np.empty(M, np.float64)
+    mean = np.empty(1, np.float64)
+    rc = _load().oracle_cross_entropy(_ptr(x), ld, M, N, code, _ptr(labels),
+                                      _ptr(loss), _ptr(mean))
+    if rc != 0:
+        raise ValueError("oracle_cross_entropy rejected its arguments")
+    return loss, float(mean[0])
 
 
 # ---------------------------------------------------------------------------

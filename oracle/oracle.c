@@ -22,6 +22,9 @@
  *  [P4] "Softmax 数值稳定性与 IO-Aware Attention：从在线归一化到 FlashAttention":
  *       §3 (three passes), §4 (running state), §4.1 (merge of two states,
  *       associativity, the random-chunking check).
+ *       Also the log-softmax log p_j = z_j - LSE(z), and the cross-entropy of
+ *       a labelled row, -log p_label, with its batch mean (section on the
+ *       cross-entropy loss and the hand-worked loss example).
  *  [P5] "FlashAttention：为什么加速推理的同时还能节省显存": the 3-pass
  *       safe_softmax and the 2-pass online_safe_softmax listings (used as a
  *       description of what is computed, not copied).
@@ -177,5 +180,64 @@ int oracle_merge(const double *m_in, const double *d_in, int64_t ld,
         if (d_out) d_out[i] = d;
         if (lse_out) lse_out[i] = m + log(d);
     }
+    return ORACLE_OK;
+}
+
+/* ---- log-softmax -----------------------------------------------------------
+ * [P3] stable-form section: log p_j = z_j - LSE(z), LSE = m + log d, with m
+ * and d from the definition above (oracle_softmax).  y is dense fp64
+ * [M][N].  A row of only -inf gives -inf - (-inf) = NaN, as y = 0/0 does. */
+int oracle_log_softmax(const void *x, int64_t ld, int64_t M, int64_t N,
+                       int dtype, double *y)
+{
+    int rc = check_args(x, ld, M, N, dtype);
+    if (rc != ORACLE_OK) return rc;
+    if (M > 0 && y == NULL) return ORACLE_EINVAL;
+    for (int64_t i = 0; i < M; ++i) {
+        double lse;
+        oracle_softmax((const char *)x + (size_t)(i * ld) *
+                           (dtype == ORACLE_F32 ? 4 : 2),
+                       ld, 1, N, dtype, NULL, NULL, NULL, &lse);
+        for (int64_t j = 0; j < N; ++j)
+            y[i * N + j] = load_elem(x, dtype, i * ld + j) - lse;
+    }
+    return ORACLE_OK;
+}
+
+/* ---- cross-entropy -----------------------------------------------------------
+ * [P3] cross-entropy section: the loss of a row whose true class is c is
+ * -log p_c = LSE(z) - z_c; the batch loss is the mean over rows.  Reading
+ * for labels outside the row (the page has none): a negative label marks a
+ * row to ignore (loss 0, left out of the mean), a label >= N gives NaN.
+ * mean (nullable) is the mean over non-ignored rows, NaN when there are
+ * none. */
+int oracle_cross_entropy(const void *x, int64_t ld, int64_t M, int64_t N,
+                         int dtype, const int64_t *labels, double *loss,
+                         double *mean)
+{
+    int rc = check_args(x, ld, M, N, dtype);
+    if (rc != ORACLE_OK) return rc;
+    if (M > 0 && (labels == NULL || loss == NULL)) return ORACLE_EINVAL;
+    double total = 0.0;
+    int64_t count = 0;
+    for (int64_t i = 0; i < M; ++i) {
+        const int64_t c = labels[i];
+        if (c < 0) {
+            loss[i] = 0.0;
+            continue;
+        }
+        if (c >= N) {
+            loss[i] = NAN;
+        } else {
+            double lse;
+            oracle_softmax((const char *)x + (size_t)(i * ld) *
+                               (dtype == ORACLE_F32 ? 4 : 2),
+                           ld, 1, N, dtype, NULL, NULL, NULL, &lse);
+            loss[i] = lse - load_elem(x, dtype, i * ld + c);
+        }
+        total = total + loss[i];
+        count = count + 1;
+    }
+    if (mean) *mean = (count > 0) ? total / (double)count : NAN;
     return ORACLE_OK;
 }

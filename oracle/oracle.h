@@ -32,6 +32,16 @@ void oracle_merge2(double ma, double da, double mb, double db,
 int oracle_merge(const double *m_in, const double *d_in, int64_t ld,
                  int64_t M, int64_t K, double *m, double *d, double *lse);
 
+/* log p = z - LSE(z) per row: y fp64 dense [M][N]. */
+int oracle_log_softmax(const void *x, int64_t ld, int64_t M, int64_t N,
+                       int dtype, double *y);
+
+/* Cross-entropy per row from int64 labels; mean (nullable) over the rows
+ * whose label is not negative. */
+int oracle_cross_entropy(const void *x, int64_t ld, int64_t M, int64_t N,
+                         int dtype, const int64_t *labels, double *loss,
+                         double *mean);
+
 #ifdef __cplusplus
 }
 #endif

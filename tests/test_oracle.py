@@ -461,3 +461,81 @@ def test_generator_bf16_rounding():
     got = wl.f32_to_bf16_bits(f)
     want = oracle.round_f64_to_bf16_bits(f.astype(np.float64))
     assert np.array_equal(got, want)
+
+
+# ---------------------------------------------------------------------------
+# Log-softmax and cross-entropy ("从原始Softmax到在线Softmax": log p = z - LSE;
+# the loss of a labelled row is -log p_label, the batch loss its mean)
+# ---------------------------------------------------------------------------
+
+def test_worked_cross_entropy_example():
+    g = _golden("p3_worked_examples.json")
+    for ex in g["lse_examples"]:
+        x = wl.from_values(ex["x"])
+        loss, mean = oracle.cross_entropy(x, [ex["label"]])
+        assert abs(loss[0] - ex["loss"]) <= ex["tol"]
+        assert abs(mean - ex["loss"]) <= ex["tol"]
+        lp = oracle.log_softmax(x)
+        assert abs(-lp[0, ex["label"]] - ex["loss"]) <= ex["tol"]
+    for ex in g["softmax_examples"]:
+        lp = oracle.log_softmax(wl.from_values(ex["x"]))
+        assert np.max(np.abs(np.exp(lp[0]) - np.array(ex["y"]))) <= ex["y_tol"]
+
+
+@pytest.mark.parametrize("M,N,scale,seed", [(3, 1, 1.0, 1), (7, 63, 3.0, 3),
+                                            (4, 1000, 3.0, 4), (2, 32768, 1.0, 6)])
+def test_log_softmax_matches_scipy(M, N, scale, seed):
+    x = wl.normal(M, N, scale=scale, seed=seed)
+    lp = oracle.log_softmax(x)
+    np.testing.assert_allclose(
+        lp, scipy.special.log_softmax(x.astype(np.float64), axis=1),
+        rtol=1e-13, atol=1e-12)
+    # sum_j e^(log p_j) = 1
+    assert np.all(np.abs(np.exp(lp).sum(axis=1) - 1.0) <= N * 2.0 ** -52 + 1e-15)
+
+
+def test_log_softmax_closed_forms():
+    lp = oracle.log_softmax(wl.from_values(np.full((2, 1000), 7.5)))
+    assert np.allclose(lp, -math.log(1000), rtol=0, atol=1e-13)
+    assert oracle.log_softmax(wl.from_values([3.0]))[0, 0] == 0.0
+    a, b = 1.25, -2.0
+    lp = oracle.log_softmax(wl.from_values([a, b]))
+    assert lp[0, 0] == pytest.approx(-math.log1p(math.exp(b - a)), rel=1e-15)
+    bf = wl.normal(3, 300, scale=2.0, seed=71, dtype="bf16")
+    np.testing.assert_allclose(
+        oracle.log_softmax(bf),
+        scipy.special.log_softmax(oracle.bf16_bits_to_f64(bf), axis=1),
+        rtol=1e-13, atol=1e-12)
+
+
+def test_cross_entropy_against_scipy_and_labels():
+    rng = np.random.default_rng(72)
+    M, N = 50, 777
+    x = wl.normal(M, N, scale=3.0, seed=72)
+    labels = rng.integers(0, N, size=M)
+    labels[3] = -100          # ignored row
+    labels[9] = -1            # ignored row
+    labels[11] = N            # out of range
+    loss, mean = oracle.cross_entropy(x, labels)
+    x64 = x.astype(np.float64)
+    ref = scipy.special.logsumexp(x64, axis=1) - x64[np.arange(M),
+                                                     np.clip(labels, 0, N - 1)]
+    ok = (labels >= 0) & (labels < N)
+    np.testing.assert_allclose(loss[ok], ref[ok], rtol=1e-13, atol=1e-13)
+    assert loss[3] == 0.0 and loss[9] == 0.0 and np.isnan(loss[11])
+    assert np.isnan(mean)                       # the NaN row is counted
+    labels[11] = 5
+    loss, mean = oracle.cross_entropy(x, labels)
+    keep = labels >= 0
+    assert mean == pytest.approx(loss[keep].sum() / keep.sum(), rel=1e-14)
+    # every row ignored: no mean
+    _, m0 = oracle.cross_entropy(x[:2], [-1, -100])
+    assert np.isnan(m0)
+
+
+def test_cross_entropy_closed_form():
+    # all-equal rows: every class has p = 1/N, so every loss is log N
+    x = wl.from_values(np.full((5, 4096), -2.5))
+    loss, mean = oracle.cross_entropy(x, [0, 7, 4095, 100, 2048])
+    assert np.allclose(loss, math.log(4096), rtol=0, atol=1e-12)
+    assert mean == pytest.approx(math.log(4096), abs=1e-12)

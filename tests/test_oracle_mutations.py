@@ -29,6 +29,15 @@ MUTATIONS = {
     "lse without m":
         ("if (lse_out) lse_out[i] = m + log(d);",
          "if (lse_out) lse_out[i] = log(d);"),
+    "log-softmax without lse":
+        ("y[i * N + j] = load_elem(x, dtype, i * ld + j) - lse;",
+         "y[i * N + j] = load_elem(x, dtype, i * ld + j);"),
+    "cross-entropy sign of the label term":
+        ("loss[i] = lse - load_elem(x, dtype, i * ld + c);",
+         "loss[i] = lse + load_elem(x, dtype, i * ld + c);"),
+    "cross-entropy mean counts ignored rows":
+        ("            loss[i] = 0.0;\n            continue;",
+         "            loss[i] = 0.0;\n            count = count + 1;\n            continue;"),
 }
 
 
