@@ -8,16 +8,20 @@
  * What is computed (per row i of x[M,N]):
  *   m_i   = max_j x_ij                               (the running max)
  *   d_i   = sum_j e^(x_ij - m_i)                     (the normaliser)
- *   y_ij  = e^(x_ij - m_i) / d_i
- *   lse_i = m_i + log d_i
+ *   y_ij  = e^(x_ij - m_i) / d_i                     (softmax)
+ *   lse_i = m_i + log d_i                            (log-sum-exp)
+ *   y_ij  = x_ij - lse_i                             (log-softmax)
+ *   loss_i = lse_i - x_{i,c_i}                       (cross-entropy, label c_i)
  * The pass that produces (m, d) keeps a running state and combines partial
  * states with the associative merge
  *   m = max(m_a, m_b),  d = d_a e^(m_a - m) + d_b e^(m_b - m),
  * as derived in "5.2 CUDA Online Softmax 实现优化" (AIInfraGuide), §2.1
  * (recurrence), §2.2 (two passes), §4.1 (merge); the same state and merge
  * appear in "Softmax 数值稳定性与 IO-Aware Attention：从在线归一化到
- * FlashAttention" §4 and §4.1.  log-sum-exp as defined in "从原始Softmax到在线
- * Softmax" (section deriving the stable form).
+ * FlashAttention" §4 and §4.1.  log-sum-exp and log-softmax as defined in
+ * "从原始Softmax到在线Softmax" (section deriving the stable form); the
+ * cross-entropy of a labelled row, -log p_label, and its batch mean from the
+ * same page's cross-entropy section.
  *
  * Conventions shared by all entry points
  *  - Layout: x and y are row-major; element (i, j) sits at base + i*ld + j
@@ -76,9 +80,11 @@ typedef enum { OS_F32 = 0, OS_BF16 = 1 } os_dtype;
  *  RESIDENT: each row is loaded once into registers, reduced, and
  *            normalised from registers (one read + one write of x).  Rows of
  *            up to 32768 elements.  ("5.2 CUDA Online Softmax 实现优化" §6,
- *            register-cached one-read version.)
+ *            register-cached one-read version.)  For statistics and
+ *            cross-entropy: the same kernel without pass 2.
  *  STREAM:   one workgroup per row; pass 1 streams the row folding (m, d),
  *            pass 2 re-reads it and writes y (two reads + one write).  Any N.
+ *            For statistics and cross-entropy: pass 1 only (one read).
  *  SPLIT:    several workgroups per row: a partial-state kernel, the
  *            state-merge kernel, and a normalise kernel (§7.1 of the same
  *            page names this two-stage scheme for few, very long rows).
@@ -125,14 +131,53 @@ os_status os_softmax_stats(const void *x, int64_t ld_x, int64_t M, int64_t N,
                            int64_t inc_out, float *lse_out, void *ws,
                            size_t ws_bytes, hipStream_t stream);
 
-/* os_softmax_stats on a chosen path: STREAM (one workgroup per row) or SPLIT
- * (several per row, then the merge kernel); RESIDENT is treated as STREAM,
- * since pass 1 alone keeps nothing resident. */
+/* os_softmax_stats on a chosen path: RESIDENT (the register-resident row
+ * kernel without pass 2; N <= 32768, else OS_ERR_UNSUPPORTED), STREAM (one
+ * workgroup per row) or SPLIT (several per row, then the merge kernel). */
 os_status os_softmax_stats_path(const void *x, int64_t ld_x, int64_t M,
                                 int64_t N, os_dtype dt, float *m_out,
                                 float *d_out, int64_t inc_out, float *lse_out,
                                 void *ws, size_t ws_bytes, os_path path,
                                 hipStream_t stream);
+
+/* Log-softmax forward: y_ij = x_ij - lse_i, written as (x_ij - m_i) - log d_i
+ * ("从原始Softmax到在线Softmax", stable-form section).  Arguments, paths,
+ * workspace, layout and errors as os_softmax_fwd / os_softmax_fwd_path;
+ * y has the dtype of x. */
+os_status os_log_softmax_fwd(const void *x, int64_t ld_x, void *y,
+                             int64_t ld_y, int64_t M, int64_t N, os_dtype dt,
+                             float *m_out, float *d_out, float *lse_out,
+                             void *ws, size_t ws_bytes, hipStream_t stream);
+
+os_status os_log_softmax_fwd_path(const void *x, int64_t ld_x, void *y,
+                                  int64_t ld_y, int64_t M, int64_t N,
+                                  os_dtype dt, float *m_out, float *d_out,
+                                  float *lse_out, void *ws, size_t ws_bytes,
+                                  os_path path, hipStream_t stream);
+
+/* Cross-entropy forward from logits ("从原始Softmax到在线Softmax",
+ * cross-entropy section): one read of x.
+ *  labels    int64 [M] device array, required.  A negative label marks a row
+ *            to ignore: its loss is 0 and it is left out of the mean.  A label
+ *            >= N gives a NaN loss (and so a NaN mean).
+ *  loss_out  fp32 [M], required: lse_i - x_{i,label_i}.
+ *  lse_out   fp32 [M], nullable.
+ *  mean_out  fp32 scalar, nullable: the mean loss over rows whose label is
+ *            not negative (NaN when there are none; computed by one more
+ *            single-workgroup kernel in a fixed order, so deterministic).
+ * Paths, workspace and errors as os_softmax_stats(_path). */
+os_status os_cross_entropy_fwd(const void *x, int64_t ld_x, int64_t M,
+                               int64_t N, os_dtype dt, const int64_t *labels,
+                               float *loss_out, float *lse_out,
+                               float *mean_out, void *ws, size_t ws_bytes,
+                               hipStream_t stream);
+
+os_status os_cross_entropy_fwd_path(const void *x, int64_t ld_x, int64_t M,
+                                    int64_t N, os_dtype dt,
+                                    const int64_t *labels, float *loss_out,
+                                    float *lse_out, float *mean_out, void *ws,
+                                    size_t ws_bytes, os_path path,
+                                    hipStream_t stream);
 
 /* Merge K partial states per row ("5.2 CUDA Online Softmax 实现优化" §4.1):
  * row i's states are (m_in[i*ld_in + k], d_in[i*ld_in + k]), k < K, fp32.
@@ -142,13 +187,15 @@ os_status os_state_merge(const float *m_in, const float *d_in, int64_t ld_in,
                          int64_t M, int64_t K, float *m_out, float *d_out,
                          float *lse_out, hipStream_t stream);
 
-/* Workspace bytes that os_softmax_fwd(_path) and os_softmax_stats(_path)
- * need for this shape and path (0 unless the split path is taken).  A pure
- * function of its arguments; returns 0 for invalid arguments. */
+/* Workspace bytes that every row-wise entry point (softmax, log-softmax,
+ * statistics, cross-entropy) needs for this shape and path (0 unless the
+ * split path is taken).  A pure function of its arguments; returns 0 for
+ * invalid arguments. */
 size_t os_softmax_workspace_bytes(int64_t M, int64_t N, os_dtype dt,
                                   os_path path);
 
-/* The path AUTO resolves to for os_softmax_fwd at this shape (host only). */
+/* The path AUTO resolves to at this shape, for every row-wise entry point
+ * (host only). */
 os_path os_softmax_select_path(int64_t M, int64_t N, os_dtype dt);
 
 /* Static description of a status code (never NULL). */

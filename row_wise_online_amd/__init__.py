@@ -10,6 +10,9 @@ there is no fallback when the library is missing.
 Same names as the C ABI, without the ``os_`` prefix:
 
 * ``softmax_fwd(x, y=None, m=None, d=None, lse=None, ws=None, path="auto")``
+* ``log_softmax_fwd(x, y=None, m=None, d=None, lse=None, ws=None, path="auto")``
+* ``cross_entropy_fwd(x, labels, loss=None, lse=None, mean=None, ws=None,
+  path="auto")``
 * ``softmax_stats(x, m, d, lse=None, inc=1, ws=None, path="auto")``
 * ``state_merge(m_in, d_in, m_out, d_out, lse_out=None)``
 * ``workspace_bytes(M, N, dtype, path="auto")``, ``select_path(M, N, dtype)``
@@ -17,8 +20,9 @@ Same names as the C ABI, without the ``os_`` prefix:
 from . import _lib
 from ._lib import OsError, PATHS, PATH_NAMES  # noqa: F401
 
-__all__ = ["softmax_fwd", "prepare_fwd", "softmax_stats", "state_merge",
-           "workspace_bytes", "select_path", "OsError", "load"]
+__all__ = ["softmax_fwd", "log_softmax_fwd", "cross_entropy_fwd",
+           "prepare_fwd", "softmax_stats", "state_merge", "workspace_bytes",
+           "select_path", "OsError", "load"]
 
 
 def load():
@@ -104,9 +108,7 @@ def _workspace(ws, need, device):
     return ws.data_ptr(), ws.numel() * ws.element_size()
 
 
-def softmax_fwd(x, y=None, *, m=None, d=None, lse=None, ws=None,
-                path="auto", stream=None):
-    """y = softmax(x) along rows; optional fp32 row statistics m, d, lse."""
+def _fwd(fn_name, x, y, m, d, lse, ws, path, stream):
     torch = _torch()
     lib = _lib.load()
     dt = _dtype_code(x.dtype)
@@ -120,19 +122,57 @@ def softmax_fwd(x, y=None, *, m=None, d=None, lse=None, ws=None,
     pc = _path_code(path)
     need = lib.os_softmax_workspace_bytes(M, N, dt, pc)
     wp, wb = _workspace(ws, need, x.device)
-    st = lib.os_softmax_fwd_path(xp, ldx, yp, ldy, M, N, dt,
-                                 _vec(m, "m", M), _vec(d, "d", M),
-                                 _vec(lse, "lse", M), wp, wb, pc,
-                                 _stream(stream))
-    _lib.check("os_softmax_fwd_path", st)
+    st = getattr(lib, fn_name)(xp, ldx, yp, ldy, M, N, dt, _vec(m, "m", M),
+                               _vec(d, "d", M), _vec(lse, "lse", M), wp, wb,
+                               pc, _stream(stream))
+    _lib.check(fn_name, st)
     return y
 
 
+def softmax_fwd(x, y=None, *, m=None, d=None, lse=None, ws=None,
+                path="auto", stream=None):
+    """y = softmax(x) along rows; optional fp32 row statistics m, d, lse."""
+    return _fwd("os_softmax_fwd_path", x, y, m, d, lse, ws, path, stream)
+
+
+def log_softmax_fwd(x, y=None, *, m=None, d=None, lse=None, ws=None,
+                    path="auto", stream=None):
+    """y = log_softmax(x) = x - lse along rows; optional m, d, lse."""
+    return _fwd("os_log_softmax_fwd_path", x, y, m, d, lse, ws, path, stream)
+
+
+def cross_entropy_fwd(x, labels, loss=None, *, lse=None, mean=None, ws=None,
+                      path="auto", stream=None):
+    """Per-row cross-entropy of the logits x against int64 labels (negative
+    label: ignored row).  Returns the fp32 loss vector; ``mean`` (a 1-element
+    fp32 tensor) receives the mean over non-ignored rows."""
+    torch = _torch()
+    lib = _lib.load()
+    dt = _dtype_code(x.dtype)
+    xp, ldx = _matrix(x, "x")
+    M, N = x.shape
+    if labels.dtype != torch.int64 or not labels.is_cuda or labels.dim() != 1 \
+            or labels.numel() != M or labels.stride(0) != 1:
+        raise ValueError("labels must be a contiguous int64 GPU vector of M")
+    if loss is None:
+        loss = torch.empty(M, dtype=torch.float32, device=x.device)
+    pc = _path_code(path)
+    need = lib.os_softmax_workspace_bytes(M, N, dt, pc)
+    wp, wb = _workspace(ws, need, x.device)
+    st = lib.os_cross_entropy_fwd_path(
+        xp, ldx, M, N, dt, labels.data_ptr(), _vec(loss, "loss", M),
+        _vec(lse, "lse", M), _vec(mean, "mean", 1), wp, wb, pc,
+        _stream(stream))
+    _lib.check("os_cross_entropy_fwd_path", st)
+    return loss
+
+
 def prepare_fwd(x, y, *, m=None, d=None, lse=None, ws=None, path="auto",
-                stream=None):
-    """Marshal the arguments of one softmax_fwd call once and return a
-    function that repeats the call (same tensors, same stream) with only
-    the ctypes call left per invocation -- for tight launch loops."""
+                stream=None, log=False):
+    """Marshal the arguments of one softmax_fwd (log=True: log_softmax_fwd)
+    call once and return a function that repeats the call (same tensors,
+    same stream) with only the ctypes call left per invocation -- for tight
+    launch loops."""
     lib = _lib.load()
     dt = _dtype_code(x.dtype)
     if y.dtype != x.dtype or y.shape != x.shape:
@@ -147,13 +187,14 @@ def prepare_fwd(x, y, *, m=None, d=None, lse=None, ws=None, path="auto",
     wp, wb = _workspace(ws, need, x.device)
     args = (xp, ldx, yp, ldy, M, N, dt, _vec(m, "m", M), _vec(d, "d", M),
             _vec(lse, "lse", M), wp, wb, pc, _stream(stream))
-    fn = lib.os_softmax_fwd_path
+    name = "os_log_softmax_fwd_path" if log else "os_softmax_fwd_path"
+    fn = getattr(lib, name)
     keep = (x, y, m, d, lse, ws)   # the tensors must outlive the closure
 
     def call():
         st = fn(*args)
         if st:
-            _lib.check("os_softmax_fwd_path", st)
+            _lib.check(name, st)
     call.tensors = keep
     return call
 

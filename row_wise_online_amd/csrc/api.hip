@@ -15,18 +15,16 @@ constexpr int64_t kMaxM = (int64_t(1) << 31) - 1;
 //    few that one workgroup per row would leave most CUs idle;
 //  - longer rows with many rows stream, one workgroup per row;
 //  - few long rows are split across workgroups.
+// The same rule serves the statistics-only passes (the resident kernel
+// without its pass 2).
 constexpr int64_t kManyRows = 512;
 constexpr int64_t kShortRow = 4096;
 
-os_path select_fwd(int64_t M, int64_t N) {
+os_path select_path(int64_t M, int64_t N) {
     if (N <= os::kResidentMaxN && (M >= kManyRows || N <= kShortRow))
         return OS_PATH_RESIDENT;
     if (M >= kManyRows) return OS_PATH_STREAM;
     return OS_PATH_SPLIT;
-}
-
-os_path select_stats(int64_t M, int64_t N) {
-    return (M >= kManyRows || N <= kShortRow) ? OS_PATH_STREAM : OS_PATH_SPLIT;
 }
 
 int esize(os_dtype dt) { return dt == OS_BF16 ? 2 : 4; }
@@ -42,13 +40,71 @@ os_status check_shape(int64_t M, int64_t N, os_dtype dt) {
     return OS_OK;
 }
 
-os_status finish() {
-    return hipGetLastError() == hipSuccess ? OS_OK : OS_ERR_HIP;
-}
+bool valid_path(os_path p) { return p >= OS_PATH_AUTO && p <= OS_PATH_SPLIT; }
 
 size_t workspace_for(int64_t M, int64_t N, os_path resolved) {
     return (resolved == OS_PATH_SPLIT && M > 0) ? os::split_workspace_bytes(M, N)
                                                 : 0;
+}
+
+// Validation shared by every row-wise entry point once the pointers that
+// the mode requires are known to be present.  Resolves AUTO and checks the
+// forced path and the workspace.
+os_status resolve(int64_t M, int64_t N, os_path path, void *ws,
+                  size_t ws_bytes, os_path *out) {
+    const os_path p = (path == OS_PATH_AUTO) ? select_path(M, N) : path;
+    if (p == OS_PATH_RESIDENT && N > os::kResidentMaxN) return OS_ERR_UNSUPPORTED;
+    const size_t need = workspace_for(M, N, p);
+    if (need > 0 && (ws == nullptr || ws_bytes < need)) return OS_ERR_WORKSPACE;
+    *out = p;
+    return OS_OK;
+}
+
+os_status launch(const os::FwdArgs &a, os_path p, void *ws) {
+    switch (p) {
+        case OS_PATH_RESIDENT: os::launch_resident(a); break;
+        case OS_PATH_STREAM: os::launch_stream(a); break;
+        default: os::launch_split(a, ws); break;
+    }
+    return hipGetLastError() == hipSuccess ? OS_OK : OS_ERR_HIP;
+}
+
+os::FwdArgs make_args(const void *x, int64_t ld_x, void *y, int64_t ld_y,
+                      int64_t M, int64_t N, os_dtype dt, os::Mode mode,
+                      hipStream_t stream) {
+    os::FwdArgs a{};
+    a.x = x;
+    a.ldx = ld_x;
+    a.y = y;
+    a.ldy = ld_y;
+    a.M = M;
+    a.N = static_cast<int>(N);
+    a.mode = mode;
+    a.inc_out = 1;
+    a.dt = dt == OS_F32 ? os::Dt::F32 : os::Dt::BF16;
+    a.vec = aligned16(x, ld_x, dt) && (y == nullptr || aligned16(y, ld_y, dt));
+    a.stream = stream;
+    return a;
+}
+
+// softmax and log-softmax forward
+os_status fwd(os::Mode mode, const void *x, int64_t ld_x, void *y,
+              int64_t ld_y, int64_t M, int64_t N, os_dtype dt, float *m_out,
+              float *d_out, float *lse_out, void *ws, size_t ws_bytes,
+              os_path path, hipStream_t stream) {
+    os_status s = check_shape(M, N, dt);
+    if (s != OS_OK) return s;
+    if (!valid_path(path)) return OS_ERR_PATH;
+    if (ld_x < N || ld_y < N) return OS_ERR_STRIDE;
+    if (M == 0) return OS_OK;
+    if (x == nullptr || y == nullptr) return OS_ERR_NULL;
+    os_path p;
+    if ((s = resolve(M, N, path, ws, ws_bytes, &p)) != OS_OK) return s;
+    os::FwdArgs a = make_args(x, ld_x, y, ld_y, M, N, dt, mode, stream);
+    a.m_out = m_out;
+    a.d_out = d_out;
+    a.lse_out = lse_out;
+    return launch(a, p, ws);
 }
 
 }  // namespace
@@ -57,20 +113,13 @@ extern "C" {
 
 os_path os_softmax_select_path(int64_t M, int64_t N, os_dtype dt) {
     if (check_shape(M, N, dt) != OS_OK) return OS_PATH_AUTO;
-    return select_fwd(M, N);
+    return select_path(M, N);
 }
 
 size_t os_softmax_workspace_bytes(int64_t M, int64_t N, os_dtype dt,
                                   os_path path) {
-    if (check_shape(M, N, dt) != OS_OK) return 0;
-    if (path < OS_PATH_AUTO || path > OS_PATH_SPLIT) return 0;
-    // one size covers the forward and the statistics call on this path
-    if (path == OS_PATH_AUTO) {
-        const size_t a = workspace_for(M, N, select_fwd(M, N));
-        const size_t b = workspace_for(M, N, select_stats(M, N));
-        return a > b ? a : b;
-    }
-    return workspace_for(M, N, path);
+    if (check_shape(M, N, dt) != OS_OK || !valid_path(path)) return 0;
+    return workspace_for(M, N, path == OS_PATH_AUTO ? select_path(M, N) : path);
 }
 
 os_status os_softmax_fwd_path(const void *x, int64_t ld_x, void *y,
@@ -78,45 +127,33 @@ os_status os_softmax_fwd_path(const void *x, int64_t ld_x, void *y,
                               os_dtype dt, float *m_out, float *d_out,
                               float *lse_out, void *ws, size_t ws_bytes,
                               os_path path, hipStream_t stream) {
-    os_status s = check_shape(M, N, dt);
-    if (s != OS_OK) return s;
-    if (path < OS_PATH_AUTO || path > OS_PATH_SPLIT) return OS_ERR_PATH;
-    if (ld_x < N || ld_y < N) return OS_ERR_STRIDE;
-    if (M == 0) return OS_OK;
-    if (x == nullptr || y == nullptr) return OS_ERR_NULL;
-    const os_path p = (path == OS_PATH_AUTO) ? select_fwd(M, N) : path;
-    if (p == OS_PATH_RESIDENT && N > os::kResidentMaxN) return OS_ERR_UNSUPPORTED;
-    const size_t need = workspace_for(M, N, p);
-    if (need > 0 && (ws == nullptr || ws_bytes < need)) return OS_ERR_WORKSPACE;
-
-    os::FwdArgs a{};
-    a.x = x;
-    a.ldx = ld_x;
-    a.y = y;
-    a.ldy = ld_y;
-    a.M = M;
-    a.N = static_cast<int>(N);
-    a.m_out = m_out;
-    a.d_out = d_out;
-    a.inc_out = 1;
-    a.lse_out = lse_out;
-    a.dt = dt == OS_F32 ? os::Dt::F32 : os::Dt::BF16;
-    a.vec = aligned16(x, ld_x, dt) && aligned16(y, ld_y, dt);
-    a.stream = stream;
-    switch (p) {
-        case OS_PATH_RESIDENT: os::launch_resident(a); break;
-        case OS_PATH_STREAM: os::launch_stream(a); break;
-        default: os::launch_split(a, ws); break;
-    }
-    return finish();
+    return fwd(os::Mode::Prob, x, ld_x, y, ld_y, M, N, dt, m_out, d_out,
+               lse_out, ws, ws_bytes, path, stream);
 }
 
 os_status os_softmax_fwd(const void *x, int64_t ld_x, void *y, int64_t ld_y,
                          int64_t M, int64_t N, os_dtype dt, float *m_out,
                          float *d_out, float *lse_out, void *ws,
                          size_t ws_bytes, hipStream_t stream) {
-    return os_softmax_fwd_path(x, ld_x, y, ld_y, M, N, dt, m_out, d_out,
-                               lse_out, ws, ws_bytes, OS_PATH_AUTO, stream);
+    return fwd(os::Mode::Prob, x, ld_x, y, ld_y, M, N, dt, m_out, d_out,
+               lse_out, ws, ws_bytes, OS_PATH_AUTO, stream);
+}
+
+os_status os_log_softmax_fwd_path(const void *x, int64_t ld_x, void *y,
+                                  int64_t ld_y, int64_t M, int64_t N,
+                                  os_dtype dt, float *m_out, float *d_out,
+                                  float *lse_out, void *ws, size_t ws_bytes,
+                                  os_path path, hipStream_t stream) {
+    return fwd(os::Mode::LogProb, x, ld_x, y, ld_y, M, N, dt, m_out, d_out,
+               lse_out, ws, ws_bytes, path, stream);
+}
+
+os_status os_log_softmax_fwd(const void *x, int64_t ld_x, void *y,
+                             int64_t ld_y, int64_t M, int64_t N, os_dtype dt,
+                             float *m_out, float *d_out, float *lse_out,
+                             void *ws, size_t ws_bytes, hipStream_t stream) {
+    return fwd(os::Mode::LogProb, x, ld_x, y, ld_y, M, N, dt, m_out, d_out,
+               lse_out, ws, ws_bytes, OS_PATH_AUTO, stream);
 }
 
 os_status os_softmax_stats_path(const void *x, int64_t ld_x, int64_t M,
@@ -126,32 +163,19 @@ os_status os_softmax_stats_path(const void *x, int64_t ld_x, int64_t M,
                                 hipStream_t stream) {
     os_status s = check_shape(M, N, dt);
     if (s != OS_OK) return s;
-    if (path < OS_PATH_AUTO || path > OS_PATH_SPLIT) return OS_ERR_PATH;
+    if (!valid_path(path)) return OS_ERR_PATH;
     if (ld_x < N || inc_out < 1) return OS_ERR_STRIDE;
     if (M == 0) return OS_OK;
     if (x == nullptr || m_out == nullptr || d_out == nullptr) return OS_ERR_NULL;
-    os_path p = (path == OS_PATH_AUTO) ? select_stats(M, N) : path;
-    if (p == OS_PATH_RESIDENT) p = OS_PATH_STREAM;
-    const size_t need = workspace_for(M, N, p);
-    if (need > 0 && (ws == nullptr || ws_bytes < need)) return OS_ERR_WORKSPACE;
-
-    os::FwdArgs a{};
-    a.x = x;
-    a.ldx = ld_x;
-    a.y = nullptr;
-    a.ldy = 0;
-    a.M = M;
-    a.N = static_cast<int>(N);
+    os_path p;
+    if ((s = resolve(M, N, path, ws, ws_bytes, &p)) != OS_OK) return s;
+    os::FwdArgs a = make_args(x, ld_x, nullptr, 0, M, N, dt, os::Mode::Stats,
+                              stream);
     a.m_out = m_out;
     a.d_out = d_out;
-    a.inc_out = inc_out;
     a.lse_out = lse_out;
-    a.dt = dt == OS_F32 ? os::Dt::F32 : os::Dt::BF16;
-    a.vec = aligned16(x, ld_x, dt);
-    a.stream = stream;
-    if (p == OS_PATH_STREAM) os::launch_stream(a);
-    else os::launch_split(a, ws);
-    return finish();
+    a.inc_out = inc_out;
+    return launch(a, p, ws);
 }
 
 os_status os_softmax_stats(const void *x, int64_t ld_x, int64_t M, int64_t N,
@@ -160,6 +184,49 @@ os_status os_softmax_stats(const void *x, int64_t ld_x, int64_t M, int64_t N,
                            size_t ws_bytes, hipStream_t stream) {
     return os_softmax_stats_path(x, ld_x, M, N, dt, m_out, d_out, inc_out,
                                  lse_out, ws, ws_bytes, OS_PATH_AUTO, stream);
+}
+
+os_status os_cross_entropy_fwd_path(const void *x, int64_t ld_x, int64_t M,
+                                    int64_t N, os_dtype dt,
+                                    const int64_t *labels, float *loss_out,
+                                    float *lse_out, float *mean_out, void *ws,
+                                    size_t ws_bytes, os_path path,
+                                    hipStream_t stream) {
+    os_status s = check_shape(M, N, dt);
+    if (s != OS_OK) return s;
+    if (!valid_path(path)) return OS_ERR_PATH;
+    if (ld_x < N) return OS_ERR_STRIDE;
+    if (M == 0) {
+        // no rows: the mean of nothing is NaN, and it is still an output
+        if (mean_out == nullptr) return OS_OK;
+        os::launch_ce_mean(nullptr, nullptr, 0, mean_out, stream);
+        return hipGetLastError() == hipSuccess ? OS_OK : OS_ERR_HIP;
+    }
+    if (x == nullptr || labels == nullptr || loss_out == nullptr)
+        return OS_ERR_NULL;
+    os_path p;
+    if ((s = resolve(M, N, path, ws, ws_bytes, &p)) != OS_OK) return s;
+    os::FwdArgs a = make_args(x, ld_x, nullptr, 0, M, N, dt, os::Mode::Stats,
+                              stream);
+    a.lse_out = lse_out;
+    a.labels = labels;
+    a.loss = loss_out;
+    if ((s = launch(a, p, ws)) != OS_OK) return s;
+    if (mean_out != nullptr) {
+        os::launch_ce_mean(loss_out, labels, M, mean_out, stream);
+        if (hipGetLastError() != hipSuccess) return OS_ERR_HIP;
+    }
+    return OS_OK;
+}
+
+os_status os_cross_entropy_fwd(const void *x, int64_t ld_x, int64_t M,
+                               int64_t N, os_dtype dt, const int64_t *labels,
+                               float *loss_out, float *lse_out,
+                               float *mean_out, void *ws, size_t ws_bytes,
+                               hipStream_t stream) {
+    return os_cross_entropy_fwd_path(x, ld_x, M, N, dt, labels, loss_out,
+                                     lse_out, mean_out, ws, ws_bytes,
+                                     OS_PATH_AUTO, stream);
 }
 
 os_status os_state_merge(const float *m_in, const float *d_in, int64_t ld_in,
@@ -172,8 +239,8 @@ os_status os_state_merge(const float *m_in, const float *d_in, int64_t ld_in,
         d_out == nullptr)
         return OS_ERR_NULL;
     os::launch_state_merge(m_in, d_in, ld_in, M, static_cast<int>(K), m_out,
-                           d_out, 1, nullptr, nullptr, lse_out, 1, stream);
-    return finish();
+                           d_out, lse_out, 1, stream);
+    return hipGetLastError() == hipSuccess ? OS_OK : OS_ERR_HIP;
 }
 
 const char *os_status_string(os_status s) {

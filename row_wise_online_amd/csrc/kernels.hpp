@@ -2,7 +2,10 @@
 //
 // Pass 1 produces each row's state (m, d); pass 2 writes
 // y = e^(x - m) * (1/d) ("5.2 CUDA Online Softmax 实现优化" §2.2: two passes;
-// the reciprocal-then-multiply form of its kernels).
+// the reciprocal-then-multiply form of its kernels), or the log-softmax
+// y = x - LSE ("从原始Softmax到在线Softmax", stable-form section), or nothing
+// (statistics only, optionally with the cross-entropy of a labelled row,
+// LSE - x_label, from the same page's cross-entropy section).
 //
 // Memory layout: a row is a sequence of slots (16-byte vectors, or single
 // elements when the row is not 16-byte aligned).  Within a row the slot
@@ -15,160 +18,176 @@
 
 namespace os {
 
-// ---------------------------------------------------------------------------
-// Resident single-read path ("5.2 CUDA Online Softmax 实现优化" §6: keep the
-// row on chip after pass 1 and normalise from registers; x is read once).
-// WAVES wavefronts share a row; with WAVES == 1 a workgroup runs ROWS
-// independent rows (one per wavefront, no barrier).  Each lane keeps
-// EPL = SPL * W elements in VGPRs; the row must have N <= SPL*W*64*WAVES.
-// ---------------------------------------------------------------------------
-template <class Tr, bool VEC, int WAVES, int ROWS, int SPL, bool NT = false>
-__global__ __launch_bounds__(kWave *WAVES *ROWS) void resident_kernel(
-    const typename Tr::elem_t *x, int64_t ldx, typename Tr::elem_t *y,
-    int64_t ldy, int64_t M, int N, float *m_out, float *d_out,
-    float *lse_out) {
-    static_assert(WAVES == 1 || ROWS == 1, "rows share a workgroup only "
-                                           "when each row has one wave");
-    using S = Slot<Tr, VEC, NT>;
-    constexpr int W = S::W;
-    constexpr int EPL = SPL * W;
-    constexpr int STRIDE = kWave * WAVES;  // slots between a lane's slots
-    __shared__ float2 lds[WAVES];
+// What pass 2 writes.
+enum class Out { Prob, LogProb, None };
 
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
-    int64_t row;
-    int wr;  // wave index within the row
-    if constexpr (ROWS > 1) {
-        row = static_cast<int64_t>(blockIdx.x) * ROWS + wave;
-        wr = 0;
-        if (row >= M) return;  // whole wavefront leaves; no barrier follows
-    } else {
-        row = blockIdx.x;
-        wr = wave;
-    }
-    const typename Tr::elem_t *xr = x + row * ldx;
-    typename Tr::elem_t *yr = y + row * ldy;
-    const int base = wr * kWave + lane;
-    const bool full = (N == SPL * W * STRIDE);
+// Per-row outputs of pass 1.  Every pointer is nullable.  m, d and lse are
+// written at row * inc.  With labels, loss[row] is the cross-entropy of the
+// row against labels[row]: 0 for a negative (ignored) label, NaN for a
+// label >= N, else LSE - x_label.
+struct StatsOut {
+    float *m;
+    float *d;
+    float *lse;
+    int64_t inc;
+    const int64_t *labels;
+    float *loss;
+};
 
-    float v[EPL];
-    if (full) {
-#pragma unroll
-        for (int k = 0; k < SPL; ++k) S::load_full(xr, k * STRIDE + base, &v[k * W]);
-    } else {
-#pragma unroll
-        for (int k = 0; k < SPL; ++k) S::load(xr, k * STRIDE + base, N, &v[k * W]);
-    }
-
-    // pass 1: lane fold -> wavefront merge -> cross-wave merge.  The lane's
-    // state is that of its EPL resident values: m_l = their max and
-    // d_l = sum_i e^(v_i - m_l).  The terms e^(v_i - m_l) stay in registers.
-    const float ml = tree_max<EPL>(v);
-    const float rl = safe_ref(ml);
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) v[i] = (v[i] - rl) * kLog2e;
-    exp2_inplace<Tr::kExactTiny, EPL>(v);
-    State st = wave_merge(ml, tree_sum<EPL>(v));
-    st = block_merge<WAVES>(st, wr, lane, lds);
-
-    // pass 2 from registers: e^(x - m) / d = e^(x - m_l) * (e^(m_l - m) / d)
-    const float scale = exp_shifted(ml - safe_ref(st.m)) * (1.0f / st.d);
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) v[i] *= scale;
-    if (full) {
-#pragma unroll
-        for (int k = 0; k < SPL; ++k) S::store_full(yr, k * STRIDE + base, &v[k * W]);
-    } else {
-#pragma unroll
-        for (int k = 0; k < SPL; ++k) S::store(yr, k * STRIDE + base, N, &v[k * W]);
-    }
-
-    if (wr == 0 && lane == 0) {
-        if (m_out) m_out[row] = st.m;
-        if (d_out) d_out[row] = st.d;
-        if (lse_out) lse_out[row] = st.m + __builtin_logf(st.d);
+// Written by one thread of the row once the row state is final.  The
+// cross-entropy is formed as (m - x_c) + log d rather than (m + log d) - x_c,
+// so that the large common part m cancels before rounding.
+template <class Tr>
+__device__ __forceinline__ void write_row_stats(const StatsOut &o, int64_t row,
+                                                const State &st,
+                                                const typename Tr::elem_t *xr,
+                                                int N) {
+    const int64_t k = row * o.inc;
+    const float logd = __builtin_logf(st.d);
+    if (o.m) o.m[k] = st.m;
+    if (o.d) o.d[k] = st.d;
+    if (o.lse) o.lse[k] = st.m + logd;
+    if (o.labels) {
+        const int64_t c = o.labels[row];
+        float l;
+        if (c < 0) {
+            l = 0.0f;
+        } else if (c >= N) {
+            l = __builtin_nanf("");
+        } else {
+            l = (safe_ref(st.m) - Tr::to_f32(xr[c])) + logd;
+        }
+        o.loss[row] = l;
     }
 }
 
 // ---------------------------------------------------------------------------
-// Persistent variant of the resident path ("5.2 CUDA Online Softmax 实现优化"
-// §7: a fixed grid walks the rows with a grid stride, here combined with the
-// register-resident row of §6).  While row r is reduced and written, the
-// loads of the wavefront's next row r + stride are already in flight, so
-// the memory pipe never drains between rows.  WAVES wavefronts share a row;
-// with WAVES == 1 each of the ROWS wavefronts of a workgroup walks its own
-// rows.  The cross-wave LDS cells are double-buffered by iteration parity:
-// the barrier of iteration i+1 orders the reads of cells (i & 1) before any
-// wave writes them again in iteration i+2.
+// Resident single-read path ("5.2 CUDA Online Softmax 实现优化" §6: keep the
+// row on chip after pass 1 and normalise from registers; x is read once).
+// One workgroup of WAVES wavefronts per row; each lane keeps EPL = SPL * W
+// elements in VGPRs; the row must have N <= SPL * W * 64 * WAVES.
+//
+// Prob: the lane's state is that of its EPL values, m_l = their max and
+// d_l = sum_i e^(v_i - m_l); the terms e^(v_i - m_l) stay in registers and
+// pass 2 scales them by e^(m_l - m) / d (one exponential per element).
+// LogProb / None: the registers keep x; pass 2 (LogProb) writes
+// (x - m) - log d.
 // ---------------------------------------------------------------------------
-template <class Tr, bool VEC, int WAVES, int ROWS, int SPL, bool NT>
-__global__ __launch_bounds__(kWave *WAVES *ROWS) void resident_persistent_kernel(
-    const typename Tr::elem_t *x, int64_t ldx, typename Tr::elem_t *y,
-    int64_t ldy, int64_t M, int N, float *m_out, float *d_out,
-    float *lse_out) {
-    static_assert(WAVES == 1 || ROWS == 1, "rows share a workgroup only "
-                                           "when each row has one wave");
+template <class Tr, bool VEC, int WAVES, int SPL, bool NT, Out OUT>
+struct ResidentRow {
     using S = Slot<Tr, VEC, NT>;
-    constexpr int W = S::W;
-    constexpr int EPL = SPL * W;
-    constexpr int STRIDE = kWave * WAVES;
-    __shared__ float2 lds[2][WAVES];
+    using elem_t = typename Tr::elem_t;
+    static constexpr int W = S::W;
+    static constexpr int EPL = SPL * W;
+    static constexpr int STRIDE = kWave * WAVES;  // slots between a lane's slots
+    static constexpr int CAPACITY = EPL * STRIDE;
 
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
-    const int wr = (ROWS > 1) ? 0 : wave;
-    const int64_t first = (ROWS > 1) ? static_cast<int64_t>(blockIdx.x) * ROWS + wave
-                                     : static_cast<int64_t>(blockIdx.x);
-    const int64_t step = static_cast<int64_t>(gridDim.x) * ROWS;
-    const int base = wr * kWave + lane;
-    const bool full = (N == SPL * W * STRIDE);
-
-    auto load_row = [&](int64_t row, float *v) {
-        const typename Tr::elem_t *xr = x + row * ldx;
-        if (full) {
+    __device__ __forceinline__ static void load(const elem_t *xr, int N,
+                                                int base, float *v) {
+        if (N == CAPACITY) {
 #pragma unroll
             for (int k = 0; k < SPL; ++k) S::load_full(xr, k * STRIDE + base, &v[k * W]);
         } else {
 #pragma unroll
             for (int k = 0; k < SPL; ++k) S::load(xr, k * STRIDE + base, N, &v[k * W]);
         }
-    };
+    }
 
-    if (first >= M) return;  // (ROWS > 1 only: a whole wavefront without rows)
-    float cur[EPL], nxt[EPL];
-    load_row(first, cur);
-    int it = 0;
-    for (int64_t row = first; row < M; row += step, ++it) {
-        const int64_t rn = row + step;
-        if (rn < M) load_row(rn, nxt);
-
-        const float ml = tree_max<EPL>(cur);
+    // Pass 1 to the row state; v is left as pass 2 needs it.
+    __device__ __forceinline__ static State reduce(float *v, int wr, int lane,
+                                                   float2 *lds, float &ml) {
+        ml = tree_max<EPL>(v);
         const float rl = safe_ref(ml);
+        float dl;
+        if constexpr (OUT == Out::Prob) {
 #pragma unroll
-        for (int i = 0; i < EPL; ++i) cur[i] = (cur[i] - rl) * kLog2e;
-        exp2_inplace<Tr::kExactTiny, EPL>(cur);
-        State st = wave_merge(ml, tree_sum<EPL>(cur));
-        st = block_merge<WAVES>(st, wr, lane, lds[it & 1]);
-
-        const float scale = exp_shifted(ml - safe_ref(st.m)) * (1.0f / st.d);
-#pragma unroll
-        for (int i = 0; i < EPL; ++i) cur[i] *= scale;
-        typename Tr::elem_t *yr = y + row * ldy;
-        if (full) {
-#pragma unroll
-            for (int k = 0; k < SPL; ++k) S::store_full(yr, k * STRIDE + base, &cur[k * W]);
+            for (int i = 0; i < EPL; ++i) v[i] = (v[i] - rl) * kLog2e;
+            exp2_inplace<Tr::kExactTiny, EPL>(v);
+            dl = tree_sum<EPL>(v);
         } else {
-#pragma unroll
-            for (int k = 0; k < SPL; ++k) S::store(yr, k * STRIDE + base, N, &cur[k * W]);
+            dl = tree_sum_exp<EPL>(v, rl);
         }
-        if (wr == 0 && lane == 0) {
-            if (m_out) m_out[row] = st.m;
-            if (d_out) d_out[row] = st.d;
-            if (lse_out) lse_out[row] = st.m + __builtin_logf(st.d);
-        }
+        State st = wave_merge(ml, dl);
+        return block_merge<WAVES>(st, wr, lane, lds);
+    }
+
+    __device__ __forceinline__ static void write(elem_t *yr, int N, int base,
+                                                 const State &st, float ml,
+                                                 float *v) {
+        if constexpr (OUT == Out::Prob) {
+            const float scale = exp_shifted(ml - safe_ref(st.m)) * (1.0f / st.d);
 #pragma unroll
-        for (int i = 0; i < EPL; ++i) cur[i] = nxt[i];
+            for (int i = 0; i < EPL; ++i) v[i] *= scale;
+        } else if constexpr (OUT == Out::LogProb) {
+            const float r = safe_ref(st.m);
+            const float logd = __builtin_logf(st.d);
+#pragma unroll
+            for (int i = 0; i < EPL; ++i) v[i] = (v[i] - r) - logd;
+        }
+        if constexpr (OUT != Out::None) {
+            if (N == CAPACITY) {
+#pragma unroll
+                for (int k = 0; k < SPL; ++k) S::store_full(yr, k * STRIDE + base, &v[k * W]);
+            } else {
+#pragma unroll
+                for (int k = 0; k < SPL; ++k) S::store(yr, k * STRIDE + base, N, &v[k * W]);
+            }
+        }
+    }
+};
+
+template <class Tr, bool VEC, int WAVES, int SPL, bool NT, Out OUT>
+__global__ __launch_bounds__(kWave *WAVES) void resident_kernel(
+    const typename Tr::elem_t *x, int64_t ldx, typename Tr::elem_t *y,
+    int64_t ldy, int N, StatsOut so) {
+    using R = ResidentRow<Tr, VEC, WAVES, SPL, NT, OUT>;
+    __shared__ float2 lds[WAVES];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wr = threadIdx.x / kWave;
+    const int64_t row = blockIdx.x;
+    const typename Tr::elem_t *xr = x + row * ldx;
+    const int base = wr * kWave + lane;
+
+    float v[R::EPL];
+    R::load(xr, N, base, v);
+    float ml;
+    const State st = R::reduce(v, wr, lane, lds, ml);
+    R::write(y + row * ldy, N, base, st, ml, v);
+    if (threadIdx.x == 0) write_row_stats<Tr>(so, row, st, xr, N);
+}
+
+// ---------------------------------------------------------------------------
+// Persistent variant of the resident path ("5.2 CUDA Online Softmax 实现优化"
+// §7: a fixed grid walks the rows with a grid stride, here combined with the
+// register-resident row of §6).  While row r is reduced and written, the
+// loads of the workgroup's next row r + gridDim.x are already in flight, so
+// the memory pipe never drains between rows.  The cross-wave LDS cells are
+// double-buffered by iteration parity: the barrier of iteration i+1 orders
+// the reads of cells (i & 1) before any wave writes them again in i+2.
+// ---------------------------------------------------------------------------
+template <class Tr, bool VEC, int WAVES, int SPL, bool NT, Out OUT>
+__global__ __launch_bounds__(kWave *WAVES) void resident_persistent_kernel(
+    const typename Tr::elem_t *x, int64_t ldx, typename Tr::elem_t *y,
+    int64_t ldy, int64_t M, int N, StatsOut so) {
+    using R = ResidentRow<Tr, VEC, WAVES, SPL, NT, OUT>;
+    __shared__ float2 lds[2][WAVES];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wr = threadIdx.x / kWave;
+    const int64_t step = gridDim.x;
+    const int base = wr * kWave + lane;
+
+    float cur[R::EPL], nxt[R::EPL];
+    R::load(x + static_cast<int64_t>(blockIdx.x) * ldx, N, base, cur);
+    int it = 0;
+    for (int64_t row = blockIdx.x; row < M; row += step, ++it) {
+        const int64_t rn = row + step;
+        if (rn < M) R::load(x + rn * ldx, N, base, nxt);
+        float ml;
+        const State st = R::reduce(cur, wr, lane, lds[it & 1], ml);
+        R::write(y + row * ldy, N, base, st, ml, cur);
+        if (threadIdx.x == 0) write_row_stats<Tr>(so, row, st, x + row * ldx, N);
+#pragma unroll
+        for (int i = 0; i < R::EPL; ++i) cur[i] = nxt[i];
     }
 }
 
@@ -233,15 +252,20 @@ struct Tiles {
         }
     }
 
-    // Pass 2 over [0, n): y = e^(x - r) * inv.  Tile t+1 is read before tile
-    // t is written, which is safe in place (they are different elements).
-    // REV walks the tiles last to first: after a pass 1 that went first to
-    // last, the most recently read lines come first, while they are most
-    // likely still in the Infinity Cache.
-    template <bool REV = false>
+    // Pass 2 over [0, n) for the row state st: Prob writes e^(x - m) / d,
+    // LogProb writes (x - m) - log d.  Tile t+1 is read before tile t is
+    // written, which is safe in place (they are different elements).  REV
+    // walks the tiles last to first: after a pass 1 that went first to last,
+    // the most recently read lines come first, while they are most likely
+    // still in the Infinity Cache.
+    template <Out OUT, bool REV>
     __device__ __forceinline__ static void normalize(const elem_t *p, elem_t *q,
-                                                     int n, int base, float r,
-                                                     float inv) {
+                                                     int n, int base,
+                                                     const State &st) {
+        static_assert(OUT != Out::None, "pass 2 writes something");
+        const float r = safe_ref(st.m);
+        const float inv = 1.0f / st.d;
+        const float logd = __builtin_logf(st.d);
         const int nt = num_tiles(n);
         float cur[K], nxt[K];
         const int t0 = REV ? nt - 1 : 0;
@@ -250,11 +274,16 @@ struct Tiles {
             const int t = REV ? nt - 1 - i : i;
             const int tn = REV ? t - 1 : t + 1;
             if (i + 1 < nt) load_tile(p, tn, base, n, tile_full(tn, n), nxt);
+            if constexpr (OUT == Out::Prob) {
 #pragma unroll
-            for (int k = 0; k < K; ++k) cur[k] = (cur[k] - r) * kLog2e;
-            exp2_inplace<Tr::kExactTiny, K>(cur);
+                for (int k = 0; k < K; ++k) cur[k] = (cur[k] - r) * kLog2e;
+                exp2_inplace<Tr::kExactTiny, K>(cur);
 #pragma unroll
-            for (int k = 0; k < K; ++k) cur[k] *= inv;
+                for (int k = 0; k < K; ++k) cur[k] *= inv;
+            } else {
+#pragma unroll
+                for (int k = 0; k < K; ++k) cur[k] = (cur[k] - r) - logd;
+            }
             store_tile(q, t, base, n, tile_full(t, n), cur);
 #pragma unroll
             for (int k = 0; k < K; ++k) cur[k] = nxt[k];
@@ -273,15 +302,13 @@ struct TwoPass {
 using StreamingNT = TwoPass<true, true, true, false>;
 
 // ---------------------------------------------------------------------------
-// Streaming two-read path: one workgroup per row.  With WRITE_Y false it is
-// the pass-1-only statistics kernel (states written with stride inc_out).
+// Streaming two-read path: one workgroup per row.  With OUT == None it is a
+// pass-1-only statistics kernel (one read of x).
 // ---------------------------------------------------------------------------
-template <class Tr, bool VEC, int WAVES, int U, bool WRITE_Y,
-          class Pol = StreamingNT>
+template <class Tr, bool VEC, int WAVES, int U, Out OUT, class Pol = StreamingNT>
 __global__ __launch_bounds__(kWave *WAVES) void stream_kernel(
     const typename Tr::elem_t *x, int64_t ldx, typename Tr::elem_t *y,
-    int64_t ldy, int64_t M, int N, float *m_out, float *d_out,
-    int64_t inc_out, float *lse_out) {
+    int64_t ldy, int N, StatsOut so) {
     using T = Tiles<Tr, VEC, WAVES, U, Pol::nt1>;
     using T2 = Tiles<Tr, VEC, WAVES, U, Pol::nt2, Pol::nts>;
     __shared__ float2 lds[WAVES];
@@ -296,16 +323,10 @@ __global__ __launch_bounds__(kWave *WAVES) void stream_kernel(
     State st = wave_merge(m, d);
     st = block_merge<WAVES>(st, wave, lane, lds);
 
-    if constexpr (WRITE_Y) {
-        T2::template normalize<Pol::rev>(xr, y + row * ldy, N, base,
-                                         safe_ref(st.m), 1.0f / st.d);
+    if constexpr (OUT != Out::None) {
+        T2::template normalize<OUT, Pol::rev>(xr, y + row * ldy, N, base, st);
     }
-    if (threadIdx.x == 0) {
-        const int64_t o = row * inc_out;
-        if (m_out) m_out[o] = st.m;
-        if (d_out) d_out[o] = st.d;
-        if (lse_out) lse_out[o] = st.m + __builtin_logf(st.d);
-    }
+    if (threadIdx.x == 0) write_row_stats<Tr>(so, row, st, xr, N);
 }
 
 // ---------------------------------------------------------------------------
@@ -338,11 +359,11 @@ __global__ __launch_bounds__(kWave *WAVES) void split_partial_kernel(
     }
 }
 
-template <class Tr, bool VEC, int WAVES, int U, class Pol = StreamingNT>
+template <class Tr, bool VEC, int WAVES, int U, Out OUT, class Pol = StreamingNT>
 __global__ __launch_bounds__(kWave *WAVES) void split_normalize_kernel(
     const typename Tr::elem_t *x, int64_t ldx, typename Tr::elem_t *y,
     int64_t ldy, int N, int P, int C, const float *row_m,
-    const float *row_d, int64_t inc) {
+    const float *row_d) {
     using T = Tiles<Tr, VEC, WAVES, U, Pol::nt2, Pol::nts>;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
@@ -351,24 +372,24 @@ __global__ __launch_bounds__(kWave *WAVES) void split_normalize_kernel(
     const int p = static_cast<int>(b - row * P);
     const int c0 = p * C;
     const int n = min(C, N - c0);
-    const float m = row_m[row * inc];
-    const float d = row_d[row * inc];
-    T::template normalize<Pol::rev>(x + row * ldx + c0, y + row * ldy + c0,
-                                    n, wave * kWave + lane, safe_ref(m),
-                                    1.0f / d);
+    const State st{row_m[row], row_d[row]};
+    T::template normalize<OUT, Pol::rev>(x + row * ldx + c0, y + row * ldy + c0,
+                                         n, wave * kWave + lane, st);
 }
 
 // ---------------------------------------------------------------------------
 // Second-level state merge ("5.2 CUDA Online Softmax 实现优化" §4.1): one
 // wavefront per row, ROWS rows per workgroup.  Each lane folds states
 // k = lane, lane + 64, ... with the pairwise merge; the wavefront merge
-// combines the 64 lane states.
+// combines the 64 lane states.  The row state goes to (m_a, d_a) at stride
+// inc_a and to the StatsOut b; b's cross-entropy reads x[row, label] from
+// x (element type Tr), which may be NULL when b has no labels.
 // ---------------------------------------------------------------------------
-template <int ROWS>
+template <int ROWS, class Tr = F32>
 __global__ __launch_bounds__(kWave *ROWS) void state_merge_kernel(
     const float *m_in, const float *d_in, int64_t ld, int64_t M, int K,
-    float *m_a, float *d_a, int64_t inc_a, float *m_b, float *d_b,
-    float *lse_b, int64_t inc_b) {
+    float *m_a, float *d_a, int64_t inc_a, StatsOut b,
+    const typename Tr::elem_t *x, int64_t ldx, int N) {
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t row = static_cast<int64_t>(blockIdx.x) * ROWS + threadIdx.x / kWave;
     if (row >= M) return;
@@ -378,14 +399,44 @@ __global__ __launch_bounds__(kWave *ROWS) void state_merge_kernel(
     for (int k = lane; k < K; k += kWave) merge_into(m, d, mr[k], dr[k]);
     const State st = wave_merge(m, d);
     if (lane == 0) {
-        // two optional destinations: (m_a, d_a) at stride inc_a, and
-        // (m_b, d_b, lse_b) at stride inc_b
         if (m_a) m_a[row * inc_a] = st.m;
         if (d_a) d_a[row * inc_a] = st.d;
-        const int64_t o = row * inc_b;
-        if (m_b) m_b[o] = st.m;
-        if (d_b) d_b[o] = st.d;
-        if (lse_b) lse_b[o] = st.m + __builtin_logf(st.d);
+        write_row_stats<Tr>(b, row, st, x ? x + row * ldx : nullptr, N);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Batch mean of the cross-entropy ("从原始Softmax到在线Softmax", cross-entropy
+// section: the mean over the batch), over rows whose label is not negative.
+// One workgroup of THREADS lanes; each lane sums rows i = lane, lane +
+// THREADS, ... in order, then a fixed butterfly / LDS order combines them,
+// so the result is deterministic.  NaN when no row counts.
+// ---------------------------------------------------------------------------
+template <int THREADS>
+__global__ __launch_bounds__(THREADS) void ce_mean_kernel(
+    const float *loss, const int64_t *labels, int64_t M, float *mean) {
+    constexpr int WAVES = THREADS / kWave;
+    __shared__ float2 lds[WAVES];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    float s = 0.0f, c = 0.0f;
+    for (int64_t i = threadIdx.x; i < M; i += THREADS) {
+        if (labels[i] >= 0) {
+            s += loss[i];
+            c += 1.0f;
+        }
+    }
+    s = wave_allreduce(s, OpAdd{});
+    c = wave_allreduce(c, OpAdd{});
+    if (lane == 0) lds[wave] = make_float2(s, c);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float ts = 0.0f, tc = 0.0f;
+        for (int w = 0; w < WAVES; ++w) {
+            ts += lds[w].x;
+            tc += lds[w].y;
+        }
+        *mean = (tc > 0.0f) ? ts / tc : __builtin_nanf("");
     }
 }
 

@@ -8,18 +8,24 @@
 namespace os {
 
 enum class Dt { F32, BF16 };
+enum class Mode { Prob, LogProb, Stats };
 
 struct FwdArgs {
     const void *x;
     int64_t ldx;
-    void *y;          // NULL for statistics only
+    void *y;          // NULL for Mode::Stats
     int64_t ldy;
     int64_t M;
     int N;
+    Mode mode;
+    // row statistics (all nullable); m / d / lse at row * inc_out
     float *m_out;
     float *d_out;
-    int64_t inc_out;  // stride of m_out / d_out / lse_out (1 for softmax)
     float *lse_out;
+    int64_t inc_out;
+    // cross-entropy (Mode::Stats only): loss[row] against labels[row]
+    const int64_t *labels;
+    float *loss;
     Dt dt;
     bool vec;         // 16-byte vector access is legal for x (and y)
     hipStream_t stream;
@@ -29,7 +35,7 @@ struct FwdArgs {
 constexpr int kResidentMaxN = 32768;
 void launch_resident(const FwdArgs &a);
 
-// Streaming path, one workgroup per row (softmax if a.y, else stats only).
+// Streaming path, one workgroup per row.
 void launch_stream(const FwdArgs &a);
 
 // Split-row plan: P chunks of C elements per row.
@@ -40,14 +46,18 @@ struct SplitPlan {
 SplitPlan split_plan(int64_t M, int64_t N);
 size_t split_workspace_bytes(int64_t M, int64_t N);
 
-// Split path: partial states into ws, state merge, then (if a.y) normalise.
+// Split path: partial states into ws, state merge (row statistics and
+// cross-entropy), then (unless Mode::Stats) the normalise kernel.
 void launch_split(const FwdArgs &a, void *ws);
 
-// Second-level state merge.  Row states go to (m_a, d_a) at row * inc_a
-// and to (m_b, d_b, lse_b) at row * inc_b; every pointer is nullable.
+// Second-level state merge of K fp32 states per row (no cross-entropy):
+// m, d and lse (nullable) at row * inc.
 void launch_state_merge(const float *m_in, const float *d_in, int64_t ld,
-                        int64_t M, int K, float *m_a, float *d_a,
-                        int64_t inc_a, float *m_b, float *d_b, float *lse_b,
-                        int64_t inc_b, hipStream_t stream);
+                        int64_t M, int K, float *m_out, float *d_out,
+                        float *lse_out, int64_t inc, hipStream_t stream);
+
+// Mean of loss[i] over rows with labels[i] >= 0 (one workgroup).
+void launch_ce_mean(const float *loss, const int64_t *labels, int64_t M,
+                    float *mean, hipStream_t stream);
 
 }  // namespace os

@@ -1,5 +1,5 @@
-// Split-row path (partial states -> state merge -> normalise) and the
-// state-merge launcher.
+// Split-row path (partial states -> state merge -> normalise), the public
+// state-merge launcher and the cross-entropy mean.
 #include "kernels.hpp"
 #include "launch.hpp"
 
@@ -13,8 +13,10 @@ constexpr int64_t kChunkAlign = 4096;  // chunk length granularity (elements)
 
 // Temporal pass-1 loads leave x in the Infinity Cache for the normalise
 // pass (non-temporal); on fp32 16 x 4194304 this is 126 us against 142 us
-// with non-temporal loads in both passes.
+// with non-temporal loads in both passes.  Statistics alone read x once,
+// non-temporally.
 using SplitPolicy = TwoPass<false, true, true, false>;
+using StatsPolicy = TwoPass<true, true, true, false>;
 
 template <class Tr, bool VEC>
 constexpr int tile_slots() {
@@ -39,7 +41,7 @@ WsLayout layout(void *ws, int64_t M, int P) {
     return l;
 }
 
-template <class Tr, bool VEC>
+template <class Tr, bool VEC, class Pol>
 void run(const FwdArgs &a, void *ws) {
     using E = typename Tr::elem_t;
     constexpr int U = tile_slots<Tr, VEC>();
@@ -49,20 +51,37 @@ void run(const FwdArgs &a, void *ws) {
     const dim3 block(kWave * kSplitWaves);
     const E *x = static_cast<const E *>(a.x);
 
-    split_partial_kernel<Tr, VEC, kSplitWaves, U, SplitPolicy><<<grid, block, 0, a.stream>>>(
+    split_partial_kernel<Tr, VEC, kSplitWaves, U, Pol><<<grid, block, 0, a.stream>>>(
         x, a.ldx, a.N, plan.P, plan.C, l.part_m, l.part_d);
 
     // Row states go to the workspace (read by the normalise kernel) and to
-    // whichever of the caller's m / d / lse are given, in one merge launch.
-    launch_state_merge(l.part_m, l.part_d, plan.P, a.M, plan.P, l.row_m,
-                       l.row_d, 1, a.m_out, a.d_out, a.lse_out, a.inc_out,
-                       a.stream);
+    // whichever of the caller's m / d / lse / cross-entropy are asked for,
+    // in one merge launch.
+    const StatsOut so{a.m_out, a.d_out, a.lse_out, a.inc_out, a.labels, a.loss};
+    state_merge_kernel<kMergeRows, Tr>
+        <<<dim3(static_cast<unsigned>((a.M + kMergeRows - 1) / kMergeRows)),
+           dim3(kWave * kMergeRows), 0, a.stream>>>(
+            l.part_m, l.part_d, plan.P, a.M, plan.P, l.row_m, l.row_d, 1, so,
+            x, a.ldx, a.N);
 
-    if (a.y) {
-        split_normalize_kernel<Tr, VEC, kSplitWaves, U, SplitPolicy><<<grid, block, 0, a.stream>>>(
-            x, a.ldx, static_cast<E *>(a.y), a.ldy, a.N, plan.P, plan.C,
-            l.row_m, l.row_d, 1);
+    if (a.mode != Mode::Stats) {
+        E *y = static_cast<E *>(a.y);
+        if (a.mode == Mode::Prob) {
+            split_normalize_kernel<Tr, VEC, kSplitWaves, U, Out::Prob, Pol>
+                <<<grid, block, 0, a.stream>>>(x, a.ldx, y, a.ldy, a.N, plan.P,
+                                               plan.C, l.row_m, l.row_d);
+        } else {
+            split_normalize_kernel<Tr, VEC, kSplitWaves, U, Out::LogProb, Pol>
+                <<<grid, block, 0, a.stream>>>(x, a.ldx, y, a.ldy, a.N, plan.P,
+                                               plan.C, l.row_m, l.row_d);
+        }
     }
+}
+
+template <class Tr, bool VEC>
+void by_mode(const FwdArgs &a, void *ws) {
+    if (a.mode == Mode::Stats) run<Tr, VEC, StatsPolicy>(a, ws);
+    else run<Tr, VEC, SplitPolicy>(a, ws);
 }
 
 }  // namespace
@@ -84,20 +103,26 @@ size_t split_workspace_bytes(int64_t M, int64_t N) {
 
 void launch_split(const FwdArgs &a, void *ws) {
     if (a.dt == Dt::F32) {
-        if (a.vec) run<F32, true>(a, ws); else run<F32, false>(a, ws);
+        if (a.vec) by_mode<F32, true>(a, ws); else by_mode<F32, false>(a, ws);
     } else {
-        if (a.vec) run<BF16, true>(a, ws); else run<BF16, false>(a, ws);
+        if (a.vec) by_mode<BF16, true>(a, ws); else by_mode<BF16, false>(a, ws);
     }
 }
 
 void launch_state_merge(const float *m_in, const float *d_in, int64_t ld,
-                        int64_t M, int K, float *m_a, float *d_a,
-                        int64_t inc_a, float *m_b, float *d_b, float *lse_b,
-                        int64_t inc_b, hipStream_t stream) {
-    const dim3 grid(static_cast<unsigned>((M + kMergeRows - 1) / kMergeRows));
-    const dim3 block(kWave * kMergeRows);
-    state_merge_kernel<kMergeRows><<<grid, block, 0, stream>>>(
-        m_in, d_in, ld, M, K, m_a, d_a, inc_a, m_b, d_b, lse_b, inc_b);
+                        int64_t M, int K, float *m_out, float *d_out,
+                        float *lse_out, int64_t inc, hipStream_t stream) {
+    const StatsOut so{nullptr, nullptr, lse_out, inc, nullptr, nullptr};
+    state_merge_kernel<kMergeRows, F32>
+        <<<dim3(static_cast<unsigned>((M + kMergeRows - 1) / kMergeRows)),
+           dim3(kWave * kMergeRows), 0, stream>>>(m_in, d_in, ld, M, K, m_out,
+                                                  d_out, inc, so, nullptr, 0, 0);
+}
+
+void launch_ce_mean(const float *loss, const int64_t *labels, int64_t M,
+                    float *mean, hipStream_t stream) {
+    ce_mean_kernel<1024><<<dim3(1), dim3(1024), 0, stream>>>(loss, labels, M,
+                                                             mean);
 }
 
 }  // namespace os

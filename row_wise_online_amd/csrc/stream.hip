@@ -1,5 +1,5 @@
-// Launchers of the streaming path (one workgroup per row) and of the
-// statistics-only kernel.
+// Launchers of the streaming path (one workgroup per row): two reads of x
+// for softmax / log-softmax, one read for statistics and cross-entropy.
 #include "kernels.hpp"
 #include "launch.hpp"
 
@@ -11,8 +11,10 @@ constexpr int kStreamWaves = 4;
 // Pass 1 loads are temporal so that the row stays in the Infinity Cache;
 // pass 2 walks the row last tile first (the most recently read lines
 // first) with non-temporal loads and stores.  Measured on fp32 1024 x 32768:
-// 52 us against 68 us with non-temporal pass-1 loads.
+// 52 us against 68 us with non-temporal pass-1 loads.  A statistics-only
+// pass has no second read and loads non-temporally.
 using StreamPolicy = TwoPass<false, true, true, true>;
+using StatsPolicy = TwoPass<true, true, true, false>;
 
 // Slots per lane per tile: 32 values per lane for vectors, 16 elements per
 // lane for element access.
@@ -21,21 +23,23 @@ constexpr int tile_slots() {
     return VEC ? 32 / Tr::E : 16;
 }
 
-template <class Tr, bool VEC>
+template <class Tr, bool VEC, Out OUT, class Pol>
 void run(const FwdArgs &a) {
     using E = typename Tr::elem_t;
     constexpr int U = tile_slots<Tr, VEC>();
-    const dim3 grid(static_cast<unsigned>(a.M));
-    const dim3 block(kWave * kStreamWaves);
-    const E *x = static_cast<const E *>(a.x);
-    if (a.y) {
-        stream_kernel<Tr, VEC, kStreamWaves, U, true, StreamPolicy><<<grid, block, 0, a.stream>>>(
-            x, a.ldx, static_cast<E *>(a.y), a.ldy, a.M, a.N, a.m_out, a.d_out,
-            a.inc_out, a.lse_out);
-    } else {
-        stream_kernel<Tr, VEC, kStreamWaves, U, false, StreamPolicy><<<grid, block, 0, a.stream>>>(
-            x, a.ldx, nullptr, 0, a.M, a.N, a.m_out, a.d_out, a.inc_out,
-            a.lse_out);
+    const StatsOut so{a.m_out, a.d_out, a.lse_out, a.inc_out, a.labels, a.loss};
+    stream_kernel<Tr, VEC, kStreamWaves, U, OUT, Pol>
+        <<<dim3(static_cast<unsigned>(a.M)), dim3(kWave * kStreamWaves), 0, a.stream>>>(
+            static_cast<const E *>(a.x), a.ldx, static_cast<E *>(a.y), a.ldy,
+            a.N, so);
+}
+
+template <class Tr, bool VEC>
+void by_mode(const FwdArgs &a) {
+    switch (a.mode) {
+        case Mode::Prob: run<Tr, VEC, Out::Prob, StreamPolicy>(a); break;
+        case Mode::LogProb: run<Tr, VEC, Out::LogProb, StreamPolicy>(a); break;
+        default: run<Tr, VEC, Out::None, StatsPolicy>(a); break;
     }
 }
 
@@ -43,9 +47,9 @@ void run(const FwdArgs &a) {
 
 void launch_stream(const FwdArgs &a) {
     if (a.dt == Dt::F32) {
-        if (a.vec) run<F32, true>(a); else run<F32, false>(a);
+        if (a.vec) by_mode<F32, true>(a); else by_mode<F32, false>(a);
     } else {
-        if (a.vec) run<BF16, true>(a); else run<BF16, false>(a);
+        if (a.vec) by_mode<BF16, true>(a); else by_mode<BF16, false>(a);
     }
 }
 

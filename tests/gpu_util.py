@@ -94,3 +94,29 @@ def check_lse(l_host, l_ref, what=""):
     tol = LSE_ABS + oracle.f32_ulp(l_ref)
     assert np.all(err <= tol), f"{what}: lse err {err.max():.3e}"
     return float(err.max())
+
+
+def check_log(y_host, y_ref, what=""):
+    """log-softmax / loss values: fp32 within 1e-5 + 2 ulp(y_ref) (the
+    output's own rounding plus that of x - m), bf16 within one step;
+    infinities and NaNs must sit where the oracle has them."""
+    if y_host.dtype == np.uint16:
+        yf = oracle.bf16_bits_to_f64(y_host)
+    else:
+        yf = y_host.astype(np.float64)
+    special = ~np.isfinite(y_ref)
+    assert np.array_equal(np.isnan(yf), np.isnan(y_ref)), f"{what}: NaN layout"
+    inf = np.isinf(y_ref)
+    assert np.array_equal(yf[inf], y_ref[inf]), f"{what}: infinities"
+    fin = ~special
+    if y_host.dtype == np.uint16:
+        want = oracle.round_f64_to_bf16_bits(y_ref[fin])
+        dist = oracle.bf16_ulp_distance(y_host[fin], want)
+        assert dist.size == 0 or dist.max() <= 1, f"{what}: {dist.max()} bf16 steps"
+        return float(dist.max(initial=0))
+    err = np.abs(yf[fin] - y_ref[fin])
+    tol = 1e-5 + 2 * oracle.f32_ulp(y_ref[fin])
+    bad = err > tol
+    assert not bad.any(), (f"{what}: {int(bad.sum())} values off, worst "
+                           f"{err.max():.3e}")
+    return float(err.max(initial=0))

@@ -139,3 +139,44 @@ def test_workspace_bytes(lib):
     assert ws(0, 100, 0, 3) == 0
     # a single chunk per row when rows are many
     assert ws(4096, 4096, 0, 3) == 2 * 16384 + 2 * 16384
+
+
+def _logfwd(lib, x=FAKE, ldx=8, y=FAKE, ldy=8, M=4, N=8, dt=0, path=0):
+    return lib.os_log_softmax_fwd_path(x, ldx, y, ldy, M, N, dt, NUL, NUL, NUL,
+                                       NUL, 0, path, NUL)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(M=-1), 2), (dict(N=0), 2), (dict(ldy=7), 3), (dict(dt=3), 4),
+    (dict(y=NUL), 1), (dict(path=5), 6),
+    (dict(N=40000, ldx=40000, ldy=40000, path=1), 7),
+    (dict(M=16, N=1 << 22, ldx=1 << 22, ldy=1 << 22, path=3), 5),
+])
+def test_log_softmax_validation(lib, kw, status):
+    assert _logfwd(lib, **kw) == status
+    assert _logfwd(lib, x=NUL, y=NUL, M=0) == 0
+
+
+def _ce(lib, x=FAKE, ldx=8, M=4, N=8, dt=0, labels=FAKE, loss=FAKE, lse=NUL,
+        mean=NUL, ws=NUL, wsb=0, path=0):
+    return lib.os_cross_entropy_fwd_path(x, ldx, M, N, dt, labels, loss, lse,
+                                         mean, ws, wsb, path, NUL)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(M=-1), 2), (dict(N=0), 2), (dict(ldx=7), 3), (dict(dt=2), 4),
+    (dict(x=NUL), 1), (dict(labels=NUL), 1), (dict(loss=NUL), 1),
+    (dict(path=9), 6), (dict(N=40000, ldx=40000, path=1), 7),
+    (dict(M=16, N=1 << 22, ldx=1 << 22, path=3), 5),
+])
+def test_cross_entropy_validation(lib, kw, status):
+    assert _ce(lib, **kw) == status
+
+
+def test_cross_entropy_empty_without_mean_is_noop(lib):
+    assert _ce(lib, x=NUL, labels=NUL, loss=NUL, M=0) == 0
+
+
+def test_stats_resident_path_limit(lib):
+    # the register-resident statistics kernel takes rows up to 32768
+    assert _stats(lib, M=4, N=40000, ldx=40000, path=1) == 7

@@ -376,3 +376,150 @@ def test_resident_row_loop_many_rows(dtype, N):
     check_d(d.cpu().numpy()[rows], d_ref)
     tol = 2.0 ** -7 if dtype == "bf16" else 1e-4
     assert np.all(np.abs(y.double().sum(dim=1).cpu().numpy() - 1.0) < tol)
+
+
+# ---------------------------------------------------------------------------
+# Log-softmax and cross-entropy
+# ---------------------------------------------------------------------------
+
+from gpu_util import check_log  # noqa: E402
+
+LOG_SHAPES = [(3, 1), (7, 3), (4, 65), (9, 1000), (3, 1025), (5, 4096),
+              (2, 8191), (2, 32768)]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("misalign", [False, True])
+@pytest.mark.parametrize("path", ["resident", "stream", "split"])
+def test_log_softmax_paths(path, dtype, misalign):
+    shapes = LOG_SHAPES + ([(3, 70001)] if path != "resident" else [])
+    for i, (M, N) in enumerate(shapes):
+        what = f"log {path} {dtype} misalign={misalign} {M}x{N}"
+        _say(what)
+        x_h = _input(M, N, dtype, seed=300 + i, misalign=misalign)
+        x = to_device(x_h)
+        y = empty_like_rows(x)
+        lse = torch.empty(M, device="cuda")
+        rw.log_softmax_fwd(x, y, lse=lse, path=path)
+        torch.cuda.synchronize()
+        check_log(to_host(y), oracle.log_softmax(x_h), what)
+        _, _, _, l_ref = oracle.softmax(x_h, want_y=False)
+        check_lse(lse.cpu().numpy(), l_ref, what)
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c5"])
+def test_log_softmax_workloads(name):
+    w = wl.WORKLOADS[name]
+    x_h = wl.generate(name)
+    x = to_device(x_h)
+    y = torch.empty_like(x)
+    rw.log_softmax_fwd(x, y)
+    torch.cuda.synchronize()
+    rows = np.arange(w.M) if w.M <= 64 else np.sort(
+        np.random.default_rng(6).choice(w.M, size=8, replace=False))
+    if name == "c5":
+        rows = np.array([0, 9])
+    ys = to_host(y[torch.as_tensor(rows, device="cuda")])
+    check_log(ys, oracle.log_softmax(np.ascontiguousarray(x_h[rows])), name)
+
+
+@pytest.mark.parametrize("path", ["resident", "stream", "split"])
+def test_log_softmax_special_values_and_in_place(path):
+    inf, nan = math.inf, math.nan
+    rows = np.random.default_rng(7).standard_normal((4, 500))
+    rows[0, ::4] = -inf
+    rows[1, :] = -inf
+    rows[2, 3] = nan
+    x_h = wl.from_values(rows)
+    x = to_device(x_h)
+    y = torch.empty_like(x)
+    rw.log_softmax_fwd(x, y, path=path)
+    torch.cuda.synchronize()
+    check_log(to_host(y), oracle.log_softmax(x_h), f"log special {path}")
+    rw.log_softmax_fwd(x, x, path=path)            # in place
+    torch.cuda.synchronize()
+    check_log(to_host(x), oracle.log_softmax(x_h), f"log in place {path}")
+
+
+def _labels(M, N, seed):
+    rng = np.random.default_rng(seed)
+    lab = rng.integers(0, N, size=M).astype(np.int64)
+    if M > 4:
+        lab[1] = -100          # ignored
+        lab[3] = N - 1         # last column
+        lab[4] = 0             # first column
+    return lab
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("misalign", [False, True])
+@pytest.mark.parametrize("path", ["resident", "stream", "split"])
+def test_cross_entropy_paths(path, dtype, misalign):
+    shapes = [(9, 1000), (6, 63), (5, 4096), (3, 16385), (7, 32768)]
+    if path != "resident":
+        shapes += [(3, 70001)]
+    for i, (M, N) in enumerate(shapes):
+        what = f"ce {path} {dtype} misalign={misalign} {M}x{N}"
+        _say(what)
+        x_h = _input(M, N, dtype, seed=400 + i, misalign=misalign)
+        lab = _labels(M, N, 400 + i)
+        x = to_device(x_h)
+        labels = torch.from_numpy(lab).cuda()
+        loss = torch.full((M,), float("nan"), device="cuda")
+        lse = torch.empty(M, device="cuda")
+        mean = torch.empty(1, device="cuda")
+        rw.cross_entropy_fwd(x, labels, loss, lse=lse, mean=mean, path=path)
+        torch.cuda.synchronize()
+        l_ref, mean_ref = oracle.cross_entropy(x_h, lab)
+        check_log(loss.cpu().numpy(), l_ref, what)
+        _, _, _, lse_ref = oracle.softmax(x_h, want_y=False)
+        check_lse(lse.cpu().numpy(), lse_ref, what)
+        assert abs(mean.item() - mean_ref) <= 1e-5 + 1e-5 * abs(mean_ref), what
+
+
+def test_cross_entropy_label_edge_cases():
+    M, N = 6, 300
+    x_h = wl.normal(M, N, scale=2.0, seed=17)
+    x = to_device(x_h)
+    for lab, note in [(np.array([-1, -100, -1, -5, -1, -1]), "all ignored"),
+                      (np.array([0, N, 5, -1, 7, 2]), "one out of range")]:
+        labels = torch.from_numpy(lab.astype(np.int64)).cuda()
+        for path in ("resident", "stream", "split"):
+            loss = torch.empty(M, device="cuda")
+            mean = torch.empty(1, device="cuda")
+            rw.cross_entropy_fwd(x, labels, loss, mean=mean, path=path)
+            torch.cuda.synchronize()
+            l_ref, mean_ref = oracle.cross_entropy(x_h, lab)
+            check_log(loss.cpu().numpy(), l_ref, f"{note} {path}")
+            assert np.isnan(mean.item()) and np.isnan(mean_ref), note
+
+
+def test_cross_entropy_worked_example():
+    # "从原始Softmax到在线Softmax": logits [2, 1, 0.1], class 0 -> loss 0.4170
+    x = torch.tensor([[2.0, 1.0, 0.1]], device="cuda")
+    labels = torch.tensor([0], dtype=torch.int64, device="cuda")
+    mean = torch.empty(1, device="cuda")
+    loss = rw.cross_entropy_fwd(x, labels, mean=mean)
+    torch.cuda.synchronize()
+    assert abs(loss.item() - 0.4170) <= 5e-5
+    assert abs(mean.item() - 0.4170) <= 5e-5
+
+
+@pytest.mark.parametrize("name", ["c2", "c3", "c5"])
+def test_cross_entropy_workloads(name):
+    w = wl.WORKLOADS[name]
+    x_h = wl.generate(name)
+    lab = _labels(w.M, w.N, 18)
+    x = to_device(x_h)
+    labels = torch.from_numpy(lab).cuda()
+    mean = torch.empty(1, device="cuda")
+    loss = rw.cross_entropy_fwd(x, labels, mean=mean)
+    torch.cuda.synchronize()
+    rows = np.arange(w.M) if w.M <= 64 else np.sort(
+        np.random.default_rng(8).choice(w.M, size=64, replace=False))
+    l_ref, _ = oracle.cross_entropy(np.ascontiguousarray(x_h[rows]), lab[rows])
+    check_log(loss.cpu().numpy()[rows], l_ref, name)
+    # the mean against the device losses summed in fp64 (order-free check)
+    lh = loss.cpu().numpy().astype(np.float64)
+    keep = lab >= 0
+    assert abs(mean.item() - lh[keep].mean()) <= 1e-5 * abs(lh[keep].mean())
