@@ -42,18 +42,24 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def algorithmic_bytes(w, path, n_stats):
-    """Bytes the path must move for one step of workload w."""
+def algorithmic_bytes(w, path, n_stats, op="softmax"):
+    """Bytes the path must move for one step of workload w: x read once per
+    read pass, y written once, row statistics written; the cross-entropy
+    reads x once and moves 8 B of label + 4 B of loss per row (+ 4 B mean)."""
     import row_wise_online_amd as rw
     xy = w.M * w.N * w.esize
-    reads = 1 if path == "resident" else 2
-    b = reads * xy + xy + 4 * w.M * n_stats
+    if op == "cross_entropy":
+        b = xy + 12 * w.M + 4
+    else:
+        reads = 1 if path == "resident" else 2
+        b = reads * xy + xy + 4 * w.M * n_stats
     if path == "split":
         b += 2 * rw.workspace_bytes(w.M, w.N, w.dtype, "split")  # states w+r
     return b
 
 
-def measure(w, steps, warmup, path="auto", rotate=True, graph=False):
+def measure(w, steps, warmup, path="auto", rotate=True, graph=False,
+            op="softmax"):
     """Average device time per step (ms), the rotation depth, and the host
     time per launch (us).  Steps cycle over R buffer sets; with graph=True
     the launches are captured once in a HIP graph and replayed."""
@@ -68,19 +74,30 @@ def measure(w, steps, warmup, path="auto", rotate=True, graph=False):
         x0 = torch.from_numpy(x_host).cuda()
     else:
         x0 = torch.from_numpy(x_host.view(np.int16)).view(tdt).cuda()
-    per_set = 2 * w.M * w.N * w.esize
+    ce = op == "cross_entropy"
+    per_set = (1 if ce else 2) * w.M * w.N * w.esize
     R = max(2, -(-ROTATE_BYTES // per_set)) if rotate else 1
     xs = [x0] + [x0.clone() for _ in range(R - 1)]
-    ys = [torch.empty_like(x0) for _ in range(R)]
+    ys = [None if ce else torch.empty_like(x0) for _ in range(R)]
     want = set(w.outputs)
     stat = lambda k: torch.empty(w.M, device="cuda") if k in want else None
     m, d, lse = stat("m"), stat("d"), stat("lse")
     ws_bytes = rw.workspace_bytes(w.M, w.N, w.dtype, path)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+    if ce:
+        labels = torch.from_numpy(np.random.default_rng(w.seed).integers(
+            0, w.N, size=w.M)).cuda()
+        loss = torch.empty(w.M, device="cuda")
+        mean = torch.empty(1, device="cuda")
 
     def prepared():
+        if ce:
+            return [rw.prepare_cross_entropy(xs[i], labels, loss, mean=mean,
+                                             ws=ws, path=path)
+                    for i in range(R)]
         return [rw.prepare_fwd(xs[i], ys[i], m=m, d=d, lse=lse, ws=ws,
-                               path=path) for i in range(R)]
+                               path=path, log=(op == "log_softmax"))
+                for i in range(R)]
 
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
@@ -145,27 +162,39 @@ def copy_ceiling(nbytes, steps=50):
     return 2 * nbytes / (ms * 1e-3) / 1e9
 
 
-def cpu_baseline(w, n_stats, budget_s):
+def cpu_baseline(w, n_stats, budget_s, op="softmax"):
     """The fp64 oracle, as it is, on this host: whole input matrices of the
     workload, repeated until about budget_s seconds have passed."""
+    import numpy as np
     import oracle
     from row_wise_online_amd import workloads as wl
     x = wl.generate(w.name)
+    if op == "cross_entropy":
+        labels = np.random.default_rng(w.seed).integers(0, w.N, size=w.M)
+        fn = lambda: oracle.cross_entropy(x, labels)
+        what = "cross-entropy (loss, mean)"
+        b = w.M * w.N * w.esize + 12 * w.M + 4
+    elif op == "log_softmax":
+        fn = lambda: oracle.log_softmax(x)
+        what = "log-softmax"
+        b = 2 * w.M * w.N * w.esize
+    else:
+        fn = lambda: oracle.softmax(x)
+        what = "three-pass softmax (y, m, d, lse)"
+        b = 2 * w.M * w.N * w.esize + 4 * w.M * n_stats
     reps, t0 = 0, time.perf_counter()
     while True:
-        oracle.softmax(x)
+        fn()
         reps += 1
         el = time.perf_counter() - t0
         if el >= budget_s or reps >= 64:
             break
     per = el / reps
-    b = 2 * w.M * w.N * w.esize + 4 * w.M * n_stats
     return {"value": round(b / per / 1e9, 4), "unit": "GB/s", "cores": 1,
             "kind": "oracle",
             "rows_per_s": round(w.M / per, 1),
             "sample": f"{reps} x full {w.M}x{w.N} {w.dtype} matrix, fp64 "
-                      f"three-pass oracle (y, m, d, lse), 1 thread, "
-                      f"{el:.1f} s"}
+                      f"{what} oracle, 1 thread, {el:.1f} s"}
 
 
 def traffic_record(workload):
@@ -182,22 +211,27 @@ def traffic_record(workload):
 
 
 def run_workload(name, steps, warmup, path="auto", want_cpu=True,
-                 cpu_budget=10.0, extras=True):
+                 cpu_budget=10.0, extras=True, op="softmax"):
     import row_wise_online_amd as rw
     from row_wise_online_amd import workloads as wl
     w = wl.WORKLOADS[name]
     resolved = rw.select_path(w.M, w.N, w.dtype) if path == "auto" else path
     n_stats = len(set(w.outputs) & {"m", "d", "lse"})
-    ms, R, host_us = measure(w, steps, warmup, path)
+    if op == "cross_entropy":
+        n_stats = 0
+    ms, R, host_us = measure(w, steps, warmup, path, op=op)
     if extras:
-        graph_ms, _, _ = measure(w, steps, warmup, path, graph=True)
-        warm_ms, _, _ = measure(w, max(10, steps // 4), 3, path, rotate=False)
-    nbytes = algorithmic_bytes(w, resolved, n_stats)
+        graph_ms, _, _ = measure(w, steps, warmup, path, graph=True, op=op)
+        warm_ms, _, _ = measure(w, max(10, steps // 4), 3, path,
+                                rotate=False, op=op)
+    nbytes = algorithmic_bytes(w, resolved, n_stats, op)
     gbs = nbytes / (ms * 1e-3) / 1e9
     eff = (2 * w.M * w.N * w.esize + 4 * w.M * n_stats) / (ms * 1e-3) / 1e9
+    opname = {"softmax": "softmax", "log_softmax": "log-softmax",
+              "cross_entropy": "cross-entropy"}[op]
     rec = {
-        "metric": METRIC if name == "c2" else
-        f"achieved HBM GB/s (% of peak) + rows/s, online softmax fwd "
+        "metric": METRIC if (name == "c2" and op == "softmax") else
+        f"achieved HBM GB/s (% of peak) + rows/s, online {opname} fwd "
         f"{w.dtype} {w.M}x{w.N}",
         "value": round(gbs, 1),
         "unit": "GB/s",
@@ -211,8 +245,9 @@ def run_workload(name, steps, warmup, path="auto", want_cpu=True,
         "dtype": "f32" if w.dtype == "f32" else "bf16",
         "data": "synthetic (seeded numpy PCG64 normals, HBM-resident, "
                 f"{R} rotating buffer sets)",
-        "config": {"workload": w.desc, "M": w.M, "N": w.N,
-                   "outputs": list(w.outputs), "path": resolved},
+        "config": {"workload": w.desc, "M": w.M, "N": w.N, "op": op,
+                   "outputs": (["loss", "mean"] if op == "cross_entropy"
+                               else list(w.outputs)), "path": resolved},
         "pct_of_peak": round(100.0 * gbs / PEAK_GBS, 2),
         "rows_per_s": round(w.M / (ms * 1e-3), 1),
         "effective_single_read_GBps": round(eff, 1),
@@ -223,7 +258,7 @@ def run_workload(name, steps, warmup, path="auto", want_cpu=True,
             "peak": PEAK_GBS,
             "unit": "GB/s",
             "frac": round(gbs / PEAK_GBS, 4),
-            "traffic": traffic_record(name),
+            "traffic": traffic_record(name) if op == "softmax" else None,
             "algorithmic_bytes_per_launch": nbytes,
             "kernel_launches_per_step": 1 if resolved != "split" else 3,
         },
@@ -235,7 +270,7 @@ def run_workload(name, steps, warmup, path="auto", want_cpu=True,
     rec["copy_ceiling_GBps"] = round(
         copy_ceiling(w.M * w.N * w.esize), 1)
     if want_cpu:
-        rec["cpu_baseline"] = cpu_baseline(w, n_stats, cpu_budget)
+        rec["cpu_baseline"] = cpu_baseline(w, n_stats, cpu_budget, op)
     return rec
 
 
@@ -249,6 +284,8 @@ def main():
                     choices=["c1", "c2", "c3", "c4", "c5"])
     ap.add_argument("--path", default="auto",
                     choices=["auto", "resident", "stream", "split"])
+    ap.add_argument("--op", default="softmax",
+                    choices=["softmax", "log_softmax", "cross_entropy"])
     ap.add_argument("--all", action="store_true",
                     help="also report every workload on stderr")
     ap.add_argument("--no-cpu", action="store_true",
@@ -274,16 +311,19 @@ def main():
     rw.load()
 
     if args.all:
-        for name in ["c1", "c2", "c3", "c4", "c5"]:
-            print(f"[bench] workload {name}", file=sys.stderr, flush=True)
-            r = run_workload(name, args.steps, args.warmup, "auto",
-                             want_cpu=False, extras=not args.no_extras)
-            print(json.dumps(r), file=sys.stderr, flush=True)
+        for op in ["softmax", "log_softmax", "cross_entropy"]:
+            for name in ["c1", "c2", "c3", "c4", "c5"]:
+                print(f"[bench] {op} workload {name}", file=sys.stderr,
+                      flush=True)
+                r = run_workload(name, args.steps, args.warmup, "auto",
+                                 want_cpu=False, extras=not args.no_extras,
+                                 op=op)
+                print(json.dumps(r), file=sys.stderr, flush=True)
     print(f"[bench] headline workload {args.workload}", file=sys.stderr,
           flush=True)
     rec = run_workload(args.workload, args.steps, args.warmup, args.path,
                        want_cpu=not args.no_cpu, cpu_budget=args.cpu_budget,
-                       extras=not args.no_extras)
+                       extras=not args.no_extras, op=args.op)
     print(json.dumps(rec), flush=True)
 
 

@@ -21,8 +21,8 @@ from . import _lib
 from ._lib import OsError, PATHS, PATH_NAMES  # noqa: F401
 
 __all__ = ["softmax_fwd", "log_softmax_fwd", "cross_entropy_fwd",
-           "prepare_fwd", "softmax_stats", "state_merge", "workspace_bytes",
-           "select_path", "OsError", "load"]
+           "prepare_fwd", "prepare_cross_entropy", "softmax_stats",
+           "state_merge", "workspace_bytes", "select_path", "OsError", "load"]
 
 
 def load():
@@ -195,6 +195,37 @@ def prepare_fwd(x, y, *, m=None, d=None, lse=None, ws=None, path="auto",
         st = fn(*args)
         if st:
             _lib.check(name, st)
+    call.tensors = keep
+    return call
+
+
+def prepare_cross_entropy(x, labels, loss, *, lse=None, mean=None, ws=None,
+                          path="auto", stream=None):
+    """cross_entropy_fwd's counterpart of prepare_fwd: marshal once, return
+    a function that repeats the call."""
+    torch = _torch()
+    lib = _lib.load()
+    dt = _dtype_code(x.dtype)
+    xp, ldx = _matrix(x, "x")
+    M, N = x.shape
+    if labels.dtype != torch.int64 or not labels.is_cuda or \
+            labels.numel() != M or labels.stride(0) != 1:
+        raise ValueError("labels must be a contiguous int64 GPU vector of M")
+    pc = _path_code(path)
+    need = lib.os_softmax_workspace_bytes(M, N, dt, pc)
+    if need and ws is None:
+        raise ValueError(f"path needs a workspace of {need} bytes")
+    wp, wb = _workspace(ws, need, x.device)
+    args = (xp, ldx, M, N, dt, labels.data_ptr(), _vec(loss, "loss", M),
+            _vec(lse, "lse", M), _vec(mean, "mean", 1), wp, wb, pc,
+            _stream(stream))
+    fn = lib.os_cross_entropy_fwd_path
+    keep = (x, labels, loss, lse, mean, ws)
+
+    def call():
+        st = fn(*args)
+        if st:
+            _lib.check("os_cross_entropy_fwd_path", st)
     call.tensors = keep
     return call
 

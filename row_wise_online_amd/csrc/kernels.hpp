@@ -21,10 +21,11 @@ namespace os {
 // What pass 2 writes.
 enum class Out { Prob, LogProb, None };
 
-// Per-row outputs of pass 1.  Every pointer is nullable.  m, d and lse are
-// written at row * inc.  With labels, loss[row] is the cross-entropy of the
-// row against labels[row]: 0 for a negative (ignored) label, NaN for a
-// label >= N, else LSE - x_label.
+// Per-row outputs of pass 1.  m, d and lse are nullable and written at
+// row * inc.  In the cross-entropy kernels (CE = true) labels and loss are
+// required and loss[row] is the cross-entropy of the row against
+// labels[row]: 0 for a negative (ignored) label, NaN for a label >= N, else
+// LSE - x_label.
 struct StatsOut {
     float *m;
     float *d;
@@ -34,28 +35,52 @@ struct StatsOut {
     float *loss;
 };
 
+// The cross-entropy target of a row (kernels instantiated with CE = true).
+// It is fetched before the row's own loads are issued: the label, then the
+// element at the label clamped into the row (no branch, so nothing waits
+// for it), widened only when the loss is written.  Its two dependent loads
+// are then in flight together with the row instead of following the
+// reduction.  Both addresses are wavefront-uniform.
+template <class Tr>
+struct Target {
+    int64_t c;                   // the label
+    typename Tr::elem_t raw;     // x[row, clamp(c, 0, N - 1)] as stored
+};
+
+template <class Tr, bool CE>
+__device__ __forceinline__ Target<Tr> fetch_target(const StatsOut &o,
+                                                   int64_t row,
+                                                   const typename Tr::elem_t *xr,
+                                                   int N) {
+    Target<Tr> t{-1, typename Tr::elem_t(0)};
+    if constexpr (CE) {
+        t.c = o.labels[row];
+        const int64_t cc = t.c < 0 ? 0 : (t.c >= N ? N - 1 : t.c);
+        t.raw = xr[cc];
+    }
+    return t;
+}
+
 // Written by one thread of the row once the row state is final.  The
 // cross-entropy is formed as (m - x_c) + log d rather than (m + log d) - x_c,
 // so that the large common part m cancels before rounding.
-template <class Tr>
+template <class Tr, bool CE>
 __device__ __forceinline__ void write_row_stats(const StatsOut &o, int64_t row,
                                                 const State &st,
-                                                const typename Tr::elem_t *xr,
-                                                int N) {
+                                                const Target<Tr> &t, int N) {
     const int64_t k = row * o.inc;
     const float logd = __builtin_logf(st.d);
     if (o.m) o.m[k] = st.m;
     if (o.d) o.d[k] = st.d;
     if (o.lse) o.lse[k] = st.m + logd;
-    if (o.labels) {
-        const int64_t c = o.labels[row];
+    if constexpr (CE) {
         float l;
-        if (c < 0) {
+        if (t.c < 0) {
             l = 0.0f;
-        } else if (c >= N) {
+        } else if (t.c >= N) {
             l = __builtin_nanf("");
         } else {
-            l = (safe_ref(st.m) - Tr::to_f32(xr[c])) + logd;
+            l = (safe_ref(st.m) - Tr::to_f32(t.raw)) + logd;
         }
         o.loss[row] = l;
     }
@@ -136,7 +161,8 @@ struct ResidentRow {
     }
 };
 
-template <class Tr, bool VEC, int WAVES, int SPL, bool NT, Out OUT>
+template <class Tr, bool VEC, int WAVES, int SPL, bool NT, Out OUT,
+          bool CE = false>
 __global__ __launch_bounds__(kWave *WAVES) void resident_kernel(
     const typename Tr::elem_t *x, int64_t ldx, typename Tr::elem_t *y,
     int64_t ldy, int N, StatsOut so) {
@@ -148,12 +174,13 @@ __global__ __launch_bounds__(kWave *WAVES) void resident_kernel(
     const typename Tr::elem_t *xr = x + row * ldx;
     const int base = wr * kWave + lane;
 
+    const Target<Tr> tg = fetch_target<Tr, CE>(so, row, xr, N);
     float v[R::EPL];
     R::load(xr, N, base, v);
     float ml;
     const State st = R::reduce(v, wr, lane, lds, ml);
     R::write(y + row * ldy, N, base, st, ml, v);
-    if (threadIdx.x == 0) write_row_stats<Tr>(so, row, st, xr, N);
+    if (threadIdx.x == 0) write_row_stats<Tr, CE>(so, row, st, tg, N);
 }
 
 // ---------------------------------------------------------------------------
@@ -165,7 +192,8 @@ __global__ __launch_bounds__(kWave *WAVES) void resident_kernel(
 // double-buffered by iteration parity: the barrier of iteration i+1 orders
 // the reads of cells (i & 1) before any wave writes them again in i+2.
 // ---------------------------------------------------------------------------
-template <class Tr, bool VEC, int WAVES, int SPL, bool NT, Out OUT>
+template <class Tr, bool VEC, int WAVES, int SPL, bool NT, Out OUT,
+          bool CE = false>
 __global__ __launch_bounds__(kWave *WAVES) void resident_persistent_kernel(
     const typename Tr::elem_t *x, int64_t ldx, typename Tr::elem_t *y,
     int64_t ldy, int64_t M, int N, StatsOut so) {
@@ -181,11 +209,12 @@ __global__ __launch_bounds__(kWave *WAVES) void resident_persistent_kernel(
     int it = 0;
     for (int64_t row = blockIdx.x; row < M; row += step, ++it) {
         const int64_t rn = row + step;
+        const Target<Tr> tg = fetch_target<Tr, CE>(so, row, x + row * ldx, N);
         if (rn < M) R::load(x + rn * ldx, N, base, nxt);
         float ml;
         const State st = R::reduce(cur, wr, lane, lds[it & 1], ml);
         R::write(y + row * ldy, N, base, st, ml, cur);
-        if (threadIdx.x == 0) write_row_stats<Tr>(so, row, st, x + row * ldx, N);
+        if (threadIdx.x == 0) write_row_stats<Tr, CE>(so, row, st, tg, N);
 #pragma unroll
         for (int i = 0; i < R::EPL; ++i) cur[i] = nxt[i];
     }
@@ -305,7 +334,8 @@ using StreamingNT = TwoPass<true, true, true, false>;
 // Streaming two-read path: one workgroup per row.  With OUT == None it is a
 // pass-1-only statistics kernel (one read of x).
 // ---------------------------------------------------------------------------
-template <class Tr, bool VEC, int WAVES, int U, Out OUT, class Pol = StreamingNT>
+template <class Tr, bool VEC, int WAVES, int U, Out OUT, class Pol = StreamingNT,
+          bool CE = false>
 __global__ __launch_bounds__(kWave *WAVES) void stream_kernel(
     const typename Tr::elem_t *x, int64_t ldx, typename Tr::elem_t *y,
     int64_t ldy, int N, StatsOut so) {
@@ -318,6 +348,7 @@ __global__ __launch_bounds__(kWave *WAVES) void stream_kernel(
     const int base = wave * kWave + lane;
     const typename Tr::elem_t *xr = x + row * ldx;
 
+    const Target<Tr> tg = fetch_target<Tr, CE>(so, row, xr, N);
     float m = kNegInf, d = 0.0f;
     T::fold(xr, N, base, m, d);
     State st = wave_merge(m, d);
@@ -326,7 +357,7 @@ __global__ __launch_bounds__(kWave *WAVES) void stream_kernel(
     if constexpr (OUT != Out::None) {
         T2::template normalize<OUT, Pol::rev>(xr, y + row * ldy, N, base, st);
     }
-    if (threadIdx.x == 0) write_row_stats<Tr>(so, row, st, xr, N);
+    if (threadIdx.x == 0) write_row_stats<Tr, CE>(so, row, st, tg, N);
 }
 
 // ---------------------------------------------------------------------------
@@ -382,10 +413,10 @@ __global__ __launch_bounds__(kWave *WAVES) void split_normalize_kernel(
 // wavefront per row, ROWS rows per workgroup.  Each lane folds states
 // k = lane, lane + 64, ... with the pairwise merge; the wavefront merge
 // combines the 64 lane states.  The row state goes to (m_a, d_a) at stride
-// inc_a and to the StatsOut b; b's cross-entropy reads x[row, label] from
-// x (element type Tr), which may be NULL when b has no labels.
+// inc_a and to the StatsOut b; with CE, b's cross-entropy reads
+// x[row, label] from x (element type Tr; unused otherwise).
 // ---------------------------------------------------------------------------
-template <int ROWS, class Tr = F32>
+template <int ROWS, class Tr = F32, bool CE = false>
 __global__ __launch_bounds__(kWave *ROWS) void state_merge_kernel(
     const float *m_in, const float *d_in, int64_t ld, int64_t M, int K,
     float *m_a, float *d_a, int64_t inc_a, StatsOut b,
@@ -395,13 +426,14 @@ __global__ __launch_bounds__(kWave *ROWS) void state_merge_kernel(
     if (row >= M) return;
     const float *mr = m_in + row * ld;
     const float *dr = d_in + row * ld;
+    const Target<Tr> tg = fetch_target<Tr, CE>(b, row, x + row * ldx, N);
     float m = kNegInf, d = 0.0f;
     for (int k = lane; k < K; k += kWave) merge_into(m, d, mr[k], dr[k]);
     const State st = wave_merge(m, d);
     if (lane == 0) {
         if (m_a) m_a[row * inc_a] = st.m;
         if (d_a) d_a[row * inc_a] = st.d;
-        write_row_stats<Tr>(b, row, st, x ? x + row * ldx : nullptr, N);
+        write_row_stats<Tr, CE>(b, row, st, tg, N);
     }
 }
 
@@ -416,14 +448,26 @@ template <int THREADS>
 __global__ __launch_bounds__(THREADS) void ce_mean_kernel(
     const float *loss, const int64_t *labels, int64_t M, float *mean) {
     constexpr int WAVES = THREADS / kWave;
+    constexpr int B = 8;  // rows per lane per batch: 2 x 8 loads in flight
     __shared__ float2 lds[WAVES];
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
     float s = 0.0f, c = 0.0f;
-    for (int64_t i = threadIdx.x; i < M; i += THREADS) {
-        if (labels[i] >= 0) {
-            s += loss[i];
-            c += 1.0f;
+    for (int64_t i0 = threadIdx.x; i0 < M; i0 += int64_t(THREADS) * B) {
+        int64_t lab[B];
+        float l[B];
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+            const int64_t i = i0 + int64_t(b) * THREADS;
+            lab[b] = (i < M) ? labels[i] : -1;
+            l[b] = (i < M) ? loss[i] : 0.0f;
+        }
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+            if (lab[b] >= 0) {
+                s += l[b];
+                c += 1.0f;
+            }
         }
     }
     s = wave_allreduce(s, OpAdd{});

@@ -58,11 +58,17 @@ void run(const FwdArgs &a, void *ws) {
     // whichever of the caller's m / d / lse / cross-entropy are asked for,
     // in one merge launch.
     const StatsOut so{a.m_out, a.d_out, a.lse_out, a.inc_out, a.labels, a.loss};
-    state_merge_kernel<kMergeRows, Tr>
-        <<<dim3(static_cast<unsigned>((a.M + kMergeRows - 1) / kMergeRows)),
-           dim3(kWave * kMergeRows), 0, a.stream>>>(
+    const dim3 mgrid(static_cast<unsigned>((a.M + kMergeRows - 1) / kMergeRows));
+    const dim3 mblock(kWave * kMergeRows);
+    if (a.labels) {
+        state_merge_kernel<kMergeRows, Tr, true><<<mgrid, mblock, 0, a.stream>>>(
             l.part_m, l.part_d, plan.P, a.M, plan.P, l.row_m, l.row_d, 1, so,
             x, a.ldx, a.N);
+    } else {
+        state_merge_kernel<kMergeRows, Tr, false><<<mgrid, mblock, 0, a.stream>>>(
+            l.part_m, l.part_d, plan.P, a.M, plan.P, l.row_m, l.row_d, 1, so,
+            x, a.ldx, a.N);
+    }
 
     if (a.mode != Mode::Stats) {
         E *y = static_cast<E *>(a.y);
@@ -113,7 +119,7 @@ void launch_state_merge(const float *m_in, const float *d_in, int64_t ld,
                         int64_t M, int K, float *m_out, float *d_out,
                         float *lse_out, int64_t inc, hipStream_t stream) {
     const StatsOut so{nullptr, nullptr, lse_out, inc, nullptr, nullptr};
-    state_merge_kernel<kMergeRows, F32>
+    state_merge_kernel<kMergeRows, F32, false>
         <<<dim3(static_cast<unsigned>((M + kMergeRows - 1) / kMergeRows)),
            dim3(kWave * kMergeRows), 0, stream>>>(m_in, d_in, ld, M, K, m_out,
                                                   d_out, inc, so, nullptr, 0, 0);

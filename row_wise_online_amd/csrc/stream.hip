@@ -23,12 +23,12 @@ constexpr int tile_slots() {
     return VEC ? 32 / Tr::E : 16;
 }
 
-template <class Tr, bool VEC, Out OUT, class Pol>
+template <class Tr, bool VEC, Out OUT, class Pol, bool CE = false>
 void run(const FwdArgs &a) {
     using E = typename Tr::elem_t;
     constexpr int U = tile_slots<Tr, VEC>();
     const StatsOut so{a.m_out, a.d_out, a.lse_out, a.inc_out, a.labels, a.loss};
-    stream_kernel<Tr, VEC, kStreamWaves, U, OUT, Pol>
+    stream_kernel<Tr, VEC, kStreamWaves, U, OUT, Pol, CE>
         <<<dim3(static_cast<unsigned>(a.M)), dim3(kWave * kStreamWaves), 0, a.stream>>>(
             static_cast<const E *>(a.x), a.ldx, static_cast<E *>(a.y), a.ldy,
             a.N, so);
@@ -39,7 +39,10 @@ void by_mode(const FwdArgs &a) {
     switch (a.mode) {
         case Mode::Prob: run<Tr, VEC, Out::Prob, StreamPolicy>(a); break;
         case Mode::LogProb: run<Tr, VEC, Out::LogProb, StreamPolicy>(a); break;
-        default: run<Tr, VEC, Out::None, StatsPolicy>(a); break;
+        default:
+            if (a.labels) run<Tr, VEC, Out::None, StatsPolicy, true>(a);
+            else run<Tr, VEC, Out::None, StatsPolicy>(a);
+            break;
     }
 }
 
