@@ -45,6 +45,9 @@ def _load():
         lib.oracle_cross_entropy.argtypes = [vp, i64, i64, i64, i32, vp, dp,
                                              dp]
         lib.oracle_cross_entropy.restype = i32
+        lib.oracle_softmax_masked.argtypes = [vp, i64, i64, i64, i32, vp, i64,
+                                              dp, dp, dp, dp, dp]
+        lib.oracle_softmax_masked.restype = i32
         _lib = lib
     return _lib
 
@@ -158,6 +161,30 @@ def cross_entropy(x, labels):
     if rc != 0:
         raise ValueError("oracle_cross_entropy rejected its arguments")
     return loss, float(mean[0])
+
+
+def softmax_masked(x, row_len=None, causal=-1):
+    """Softmax and log-softmax of each row over its first n_i columns
+    (n_i from row_len and/or the causal offset).  Returns
+    (y, log_y, m, d, lse), fp64."""
+    x, code = _as_input(x)
+    M, N = x.shape
+    ld = x.strides[0] // x.itemsize
+    rl = None if row_len is None else np.ascontiguousarray(row_len,
+                                                            dtype=np.int32)
+    if rl is not None and rl.shape != (M,):
+        raise ValueError("one length per row")
+    y = np.empty((M, N), np.float64)
+    log_y = np.empty((M, N), np.float64)
+    m = np.empty(M, np.float64)
+    d = np.empty(M, np.float64)
+    lse = np.empty(M, np.float64)
+    rc = _load().oracle_softmax_masked(_ptr(x), ld, M, N, code, _ptr(rl),
+                                       int(causal), _ptr(y), _ptr(log_y),
+                                       _ptr(m), _ptr(d), _ptr(lse))
+    if rc != 0:
+        raise ValueError("oracle_softmax_masked rejected its arguments")
+    return y, log_y, m, d, lse
 
 
 # ---------------------------------------------------------------------------

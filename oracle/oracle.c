@@ -241,3 +241,68 @@ int oracle_cross_entropy(const void *x, int64_t ld, int64_t M, int64_t N,
     if (mean) *mean = (count > 0) ? total / (double)count : NAN;
     return ORACLE_OK;
 }
+
+/* ---- masked rows ----------------------------------------------------------
+ * Row i takes part in its softmax only through its first n_i columns:
+ *   n_i = N, lowered to row_len[i] (clipped to [0, N]) when row_len is
+ *   given, and to i + causal + 1 when causal >= 0 (a causal mask: row i sees
+ *   columns 0..i+causal).
+ * The other columns are masked: they are not read, and count as -inf
+ * elements ([P4] §9.2 lists mask boundaries among the inputs to test; the
+ * -inf reading above then fixes their output): y = 0 for softmax, -inf for
+ * log-softmax.  A row with n_i = 0 has m = -inf, d = 0, lse = -inf and a NaN
+ * y, as a row of only -inf.
+ * The valid columns follow the definition of oracle_softmax, written out
+ * again over j < n_i.  log_y (nullable): x - lse on valid columns. */
+static int64_t valid_cols(int64_t i, int64_t N, const int32_t *row_len,
+                          int64_t causal)
+{
+    int64_t n = N;
+    if (row_len) {
+        int64_t l = row_len[i];
+        if (l < 0) l = 0;
+        if (l < n) n = l;
+    }
+    if (causal >= 0 && i + causal + 1 < n) n = i + causal + 1;
+    return n;
+}
+
+int oracle_softmax_masked(const void *x, int64_t ld, int64_t M, int64_t N,
+                          int dtype, const int32_t *row_len, int64_t causal,
+                          double *y, double *log_y, double *m_out,
+                          double *d_out, double *lse_out)
+{
+    int rc = check_args(x, ld, M, N, dtype);
+    if (rc != ORACLE_OK) return rc;
+    for (int64_t i = 0; i < M; ++i) {
+        const int64_t base = i * ld;
+        const int64_t n = valid_cols(i, N, row_len, causal);
+        double m = -INFINITY;
+        for (int64_t j = 0; j < n; ++j) {
+            double v = load_elem(x, dtype, base + j);
+            if (v > m) m = v;
+        }
+        double d = 0.0;
+        for (int64_t j = 0; j < n; ++j) {
+            double v = load_elem(x, dtype, base + j);
+            double t = (v == -INFINITY) ? 0.0 : exp(v - m);
+            d = d + t;
+        }
+        const double lse = m + log(d);
+        for (int64_t j = 0; j < N; ++j) {
+            if (j < n) {
+                double v = load_elem(x, dtype, base + j);
+                double t = (v == -INFINITY) ? 0.0 : exp(v - m);
+                if (y) y[i * N + j] = t / d;
+                if (log_y) log_y[i * N + j] = v - lse;
+            } else {
+                if (y) y[i * N + j] = (n == 0) ? NAN : 0.0;
+                if (log_y) log_y[i * N + j] = (n == 0) ? NAN : -INFINITY;
+            }
+        }
+        if (m_out) m_out[i] = m;
+        if (d_out) d_out[i] = d;
+        if (lse_out) lse_out[i] = lse;
+    }
+    return ORACLE_OK;
+}

@@ -42,6 +42,14 @@ int oracle_cross_entropy(const void *x, int64_t ld, int64_t M, int64_t N,
                          int dtype, const int64_t *labels, double *loss,
                          double *mean);
 
+/* Softmax (y) and log-softmax (log_y) of each row over its first n_i
+ * columns (row_len and/or a causal offset; see oracle.c); all nullable
+ * except x. */
+int oracle_softmax_masked(const void *x, int64_t ld, int64_t M, int64_t N,
+                          int dtype, const int32_t *row_len, int64_t causal,
+                          double *y, double *log_y, double *m, double *d,
+                          double *lse);
+
 #ifdef __cplusplus
 }
 #endif

@@ -539,3 +539,63 @@ def test_cross_entropy_closed_form():
     loss, mean = oracle.cross_entropy(x, [0, 7, 4095, 100, 2048])
     assert np.allclose(loss, math.log(4096), rtol=0, atol=1e-12)
     assert mean == pytest.approx(math.log(4096), abs=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# Masked rows (valid lengths and a causal offset)
+# ---------------------------------------------------------------------------
+
+def test_masked_rows_match_scipy_on_truncated_rows():
+    M, N = 12, 300
+    x = wl.normal(M, N, scale=3.0, seed=81)
+    rng = np.random.default_rng(81)
+    row_len = rng.integers(-3, N + 20, size=M).astype(np.int32)
+    row_len[0] = 0
+    row_len[1] = N
+    row_len[2] = 1
+    y, ly, m, d, lse = oracle.softmax_masked(x, row_len)
+    x64 = x.astype(np.float64)
+    for i in range(M):
+        n = int(min(max(row_len[i], 0), N))
+        if n == 0:
+            assert np.all(np.isnan(y[i])) and np.all(np.isnan(ly[i]))
+            assert m[i] == -np.inf and d[i] == 0 and lse[i] == -np.inf
+            continue
+        np.testing.assert_allclose(y[i, :n], scipy.special.softmax(x64[i, :n]),
+                                   rtol=1e-13, atol=1e-300)
+        np.testing.assert_allclose(ly[i, :n],
+                                   scipy.special.log_softmax(x64[i, :n]),
+                                   rtol=1e-13, atol=1e-12)
+        assert np.all(y[i, n:] == 0.0) and np.all(ly[i, n:] == -np.inf)
+        assert lse[i] == pytest.approx(scipy.special.logsumexp(x64[i, :n]),
+                                       rel=1e-14)
+
+
+def test_masked_equals_minus_inf_fill():
+    # masking a column is the same as storing -inf there (bit for bit)
+    M, N = 6, 500
+    x = wl.normal(M, N, scale=2.0, seed=82)
+    row_len = np.array([500, 499, 250, 1, 37, 0], np.int32)
+    filled = x.copy()
+    for i, n in enumerate(row_len):
+        filled[i, n:] = -np.inf
+    a = oracle.softmax_masked(x, row_len)
+    b_y, b_m, b_d, b_lse = oracle.softmax(filled)
+    assert np.array_equal(a[0], b_y, equal_nan=True)
+    assert np.array_equal(a[2], b_m) and np.array_equal(a[3], b_d)
+    assert np.array_equal(a[4], b_lse)
+
+
+def test_causal_mask_closed_form():
+    # an all-equal matrix with a causal mask: row i spreads over i + 1 + off
+    M, N, off = 9, 7, 1
+    x = wl.from_values(np.full((M, N), 0.5))
+    y, ly, m, d, lse = oracle.softmax_masked(x, None, causal=off)
+    for i in range(M):
+        n = min(N, i + off + 1)
+        assert np.all(y[i, :n] == 1.0 / n) and np.all(y[i, n:] == 0.0)
+        assert d[i] == n
+        assert ly[i, 0] == pytest.approx(-math.log(n), abs=1e-15)
+    # both masks: the smaller length wins
+    y2, *_ = oracle.softmax_masked(x, np.full(M, 3, np.int32), causal=off)
+    assert np.all(y2[0, :2] == 0.5) and np.all(y2[5, :3] == 1.0 / 3)

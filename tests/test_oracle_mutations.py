@@ -38,6 +38,12 @@ MUTATIONS = {
     "cross-entropy mean counts ignored rows":
         ("            loss[i] = 0.0;\n            continue;",
          "            loss[i] = 0.0;\n            count = count + 1;\n            continue;"),
+    "masked columns read":
+        ("        for (int64_t j = 0; j < n; ++j) {\n            double v = load_elem(x, dtype, base + j);\n            if (v > m) m = v;",
+         "        for (int64_t j = 0; j < N; ++j) {\n            double v = load_elem(x, dtype, base + j);\n            if (v > m) m = v;"),
+    "causal offset off by one":
+        ("if (causal >= 0 && i + causal + 1 < n) n = i + causal + 1;",
+         "if (causal >= 0 && i + causal < n) n = i + causal;"),
 }
 
 
