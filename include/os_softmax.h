@@ -155,6 +155,31 @@ os_status os_log_softmax_fwd_path(const void *x, int64_t ld_x, void *y,
                                   float *lse_out, void *ws, size_t ws_bytes,
                                   os_path path, hipStream_t stream);
 
+/* Softmax / log-softmax over masked rows: row i takes part only through its
+ * first n_i columns, n_i = N lowered to row_len[i] (clipped at 0) when
+ * row_len (int32 [M] device array, nullable) is given, and to
+ * i + causal_offset + 1 when causal_offset >= 0 (a causal mask; a negative
+ * value means no causal mask).  Masked columns are not read; they behave as
+ * -inf elements: y = 0 (softmax) or -inf (log-softmax) there, and a row with
+ * n_i = 0 is all NaN with m = -inf, d = 0, lse = -inf.  ("Softmax 数值稳定性与
+ * IO-Aware Attention" §9.2 lists mask boundaries among the edge cases.)
+ * Everything else as os_softmax_fwd_path / os_log_softmax_fwd_path. */
+os_status os_softmax_fwd_masked(const void *x, int64_t ld_x, void *y,
+                                int64_t ld_y, int64_t M, int64_t N,
+                                os_dtype dt, const int32_t *row_len,
+                                int64_t causal_offset, float *m_out,
+                                float *d_out, float *lse_out, void *ws,
+                                size_t ws_bytes, os_path path,
+                                hipStream_t stream);
+
+os_status os_log_softmax_fwd_masked(const void *x, int64_t ld_x, void *y,
+                                    int64_t ld_y, int64_t M, int64_t N,
+                                    os_dtype dt, const int32_t *row_len,
+                                    int64_t causal_offset, float *m_out,
+                                    float *d_out, float *lse_out, void *ws,
+                                    size_t ws_bytes, os_path path,
+                                    hipStream_t stream);
+
 /* Cross-entropy forward from logits ("从原始Softmax到在线Softmax",
  * cross-entropy section): one read of x.
  *  labels    int64 [M] device array, required.  A negative label marks a row

@@ -108,7 +108,8 @@ def _workspace(ws, need, device):
     return ws.data_ptr(), ws.numel() * ws.element_size()
 
 
-def _fwd(fn_name, x, y, m, d, lse, ws, path, stream):
+def _fwd(fn_name, x, y, m, d, lse, ws, path, stream, row_len=None,
+         causal=None):
     torch = _torch()
     lib = _lib.load()
     dt = _dtype_code(x.dtype)
@@ -122,23 +123,44 @@ def _fwd(fn_name, x, y, m, d, lse, ws, path, stream):
     pc = _path_code(path)
     need = lib.os_softmax_workspace_bytes(M, N, dt, pc)
     wp, wb = _workspace(ws, need, x.device)
-    st = getattr(lib, fn_name)(xp, ldx, yp, ldy, M, N, dt, _vec(m, "m", M),
-                               _vec(d, "d", M), _vec(lse, "lse", M), wp, wb,
-                               pc, _stream(stream))
+    if row_len is None and causal is None:
+        st = getattr(lib, fn_name)(xp, ldx, yp, ldy, M, N, dt,
+                                   _vec(m, "m", M), _vec(d, "d", M),
+                                   _vec(lse, "lse", M), wp, wb, pc,
+                                   _stream(stream))
+    else:
+        if row_len is not None and (
+                row_len.dtype != torch.int32 or not row_len.is_cuda or
+                row_len.dim() != 1 or row_len.numel() != M or
+                row_len.stride(0) != 1):
+            raise ValueError("row_len must be a contiguous int32 GPU vector "
+                             "of M")
+        fn_name = fn_name.replace("_path", "_masked")
+        st = getattr(lib, fn_name)(
+            xp, ldx, yp, ldy, M, N, dt,
+            None if row_len is None else row_len.data_ptr(),
+            -1 if causal is None else int(causal), _vec(m, "m", M),
+            _vec(d, "d", M), _vec(lse, "lse", M), wp, wb, pc,
+            _stream(stream))
     _lib.check(fn_name, st)
     return y
 
 
 def softmax_fwd(x, y=None, *, m=None, d=None, lse=None, ws=None,
-                path="auto", stream=None):
-    """y = softmax(x) along rows; optional fp32 row statistics m, d, lse."""
-    return _fwd("os_softmax_fwd_path", x, y, m, d, lse, ws, path, stream)
+                path="auto", stream=None, row_len=None, causal=None):
+    """y = softmax(x) along rows; optional fp32 row statistics m, d, lse.
+    row_len (int32 [M] GPU tensor) and/or causal (offset >= 0) mask each
+    row to its first columns (os_softmax_fwd_masked)."""
+    return _fwd("os_softmax_fwd_path", x, y, m, d, lse, ws, path, stream,
+                row_len, causal)
 
 
 def log_softmax_fwd(x, y=None, *, m=None, d=None, lse=None, ws=None,
-                    path="auto", stream=None):
-    """y = log_softmax(x) = x - lse along rows; optional m, d, lse."""
-    return _fwd("os_log_softmax_fwd_path", x, y, m, d, lse, ws, path, stream)
+                    path="auto", stream=None, row_len=None, causal=None):
+    """y = log_softmax(x) = x - lse along rows; optional m, d, lse; masks
+    as softmax_fwd."""
+    return _fwd("os_log_softmax_fwd_path", x, y, m, d, lse, ws, path, stream,
+                row_len, causal)
 
 
 def cross_entropy_fwd(x, labels, loss=None, *, lse=None, mean=None, ws=None,

@@ -81,17 +81,19 @@ os::FwdArgs make_args(const void *x, int64_t ld_x, void *y, int64_t ld_y,
     a.N = static_cast<int>(N);
     a.mode = mode;
     a.inc_out = 1;
+    a.causal = -1;
     a.dt = dt == OS_F32 ? os::Dt::F32 : os::Dt::BF16;
     a.vec = aligned16(x, ld_x, dt) && (y == nullptr || aligned16(y, ld_y, dt));
     a.stream = stream;
     return a;
 }
 
-// softmax and log-softmax forward
+// softmax and log-softmax forward (masked when row_len or causal >= 0)
 os_status fwd(os::Mode mode, const void *x, int64_t ld_x, void *y,
               int64_t ld_y, int64_t M, int64_t N, os_dtype dt, float *m_out,
               float *d_out, float *lse_out, void *ws, size_t ws_bytes,
-              os_path path, hipStream_t stream) {
+              os_path path, hipStream_t stream,
+              const int32_t *row_len = nullptr, int64_t causal = -1) {
     os_status s = check_shape(M, N, dt);
     if (s != OS_OK) return s;
     if (!valid_path(path)) return OS_ERR_PATH;
@@ -104,6 +106,8 @@ os_status fwd(os::Mode mode, const void *x, int64_t ld_x, void *y,
     a.m_out = m_out;
     a.d_out = d_out;
     a.lse_out = lse_out;
+    a.row_len = row_len;
+    a.causal = causal < 0 ? -1 : causal;
     return launch(a, p, ws);
 }
 
@@ -154,6 +158,28 @@ os_status os_log_softmax_fwd(const void *x, int64_t ld_x, void *y,
                              void *ws, size_t ws_bytes, hipStream_t stream) {
     return fwd(os::Mode::LogProb, x, ld_x, y, ld_y, M, N, dt, m_out, d_out,
                lse_out, ws, ws_bytes, OS_PATH_AUTO, stream);
+}
+
+os_status os_softmax_fwd_masked(const void *x, int64_t ld_x, void *y,
+                                int64_t ld_y, int64_t M, int64_t N,
+                                os_dtype dt, const int32_t *row_len,
+                                int64_t causal_offset, float *m_out,
+                                float *d_out, float *lse_out, void *ws,
+                                size_t ws_bytes, os_path path,
+                                hipStream_t stream) {
+    return fwd(os::Mode::Prob, x, ld_x, y, ld_y, M, N, dt, m_out, d_out,
+               lse_out, ws, ws_bytes, path, stream, row_len, causal_offset);
+}
+
+os_status os_log_softmax_fwd_masked(const void *x, int64_t ld_x, void *y,
+                                    int64_t ld_y, int64_t M, int64_t N,
+                                    os_dtype dt, const int32_t *row_len,
+                                    int64_t causal_offset, float *m_out,
+                                    float *d_out, float *lse_out, void *ws,
+                                    size_t ws_bytes, os_path path,
+                                    hipStream_t stream) {
+    return fwd(os::Mode::LogProb, x, ld_x, y, ld_y, M, N, dt, m_out, d_out,
+               lse_out, ws, ws_bytes, path, stream, row_len, causal_offset);
 }
 
 os_status os_softmax_stats_path(const void *x, int64_t ld_x, int64_t M,

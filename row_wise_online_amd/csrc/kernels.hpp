@@ -35,6 +35,33 @@ struct StatsOut {
     float *loss;
 };
 
+// Masked rows (kernels instantiated with MASKED = true): row i takes part
+// only through its first n_i columns, n_i = N lowered to len[i] (clipped at
+// 0) when len is given and to i + causal + 1 when causal >= 0.  The other
+// columns are never read: they load as -inf, so pass 2 writes 0 (softmax)
+// or -inf (log-softmax) there, and a row with n_i = 0 is all NaN like a row
+// of only -inf.
+struct Mask {
+    const int32_t *len;
+    int64_t causal;
+};
+
+template <bool MASKED>
+__device__ __forceinline__ int valid_cols(const Mask &mk, int64_t row, int N) {
+    if constexpr (!MASKED) {
+        return N;
+    } else {
+        int n = N;
+        if (mk.len) {
+            const int l = mk.len[row];
+            n = min(n, l < 0 ? 0 : l);
+        }
+        if (mk.causal >= 0 && row + mk.causal + 1 < n)
+            n = static_cast<int>(row + mk.causal + 1);
+        return n;
+    }
+}
+
 // The cross-entropy target of a row (kernels instantiated with CE = true).
 // It is fetched before the row's own loads are issued: the label, then the
 // element at the label clamped into the row (no branch, so nothing waits
@@ -162,10 +189,10 @@ struct ResidentRow {
 };
 
 template <class Tr, bool VEC, int WAVES, int SPL, bool NT, Out OUT,
-          bool CE = false>
+          bool CE = false, bool MASKED = false>
 __global__ __launch_bounds__(kWave *WAVES) void resident_kernel(
     const typename Tr::elem_t *x, int64_t ldx, typename Tr::elem_t *y,
-    int64_t ldy, int N, StatsOut so) {
+    int64_t ldy, int N, StatsOut so, Mask mk) {
     using R = ResidentRow<Tr, VEC, WAVES, SPL, NT, OUT>;
     __shared__ float2 lds[WAVES];
     const int lane = threadIdx.x & (kWave - 1);
@@ -176,7 +203,7 @@ __global__ __launch_bounds__(kWave *WAVES) void resident_kernel(
 
     const Target<Tr> tg = fetch_target<Tr, CE>(so, row, xr, N);
     float v[R::EPL];
-    R::load(xr, N, base, v);
+    R::load(xr, valid_cols<MASKED>(mk, row, N), base, v);
     float ml;
     const State st = R::reduce(v, wr, lane, lds, ml);
     R::write(y + row * ldy, N, base, st, ml, v);
@@ -193,10 +220,10 @@ __global__ __launch_bounds__(kWave *WAVES) void resident_kernel(
 // the reads of cells (i & 1) before any wave writes them again in i+2.
 // ---------------------------------------------------------------------------
 template <class Tr, bool VEC, int WAVES, int SPL, bool NT, Out OUT,
-          bool CE = false>
+          bool CE = false, bool MASKED = false>
 __global__ __launch_bounds__(kWave *WAVES) void resident_persistent_kernel(
     const typename Tr::elem_t *x, int64_t ldx, typename Tr::elem_t *y,
-    int64_t ldy, int64_t M, int N, StatsOut so) {
+    int64_t ldy, int64_t M, int N, StatsOut so, Mask mk) {
     using R = ResidentRow<Tr, VEC, WAVES, SPL, NT, OUT>;
     __shared__ float2 lds[2][WAVES];
     const int lane = threadIdx.x & (kWave - 1);
@@ -205,12 +232,13 @@ __global__ __launch_bounds__(kWave *WAVES) void resident_persistent_kernel(
     const int base = wr * kWave + lane;
 
     float cur[R::EPL], nxt[R::EPL];
-    R::load(x + static_cast<int64_t>(blockIdx.x) * ldx, N, base, cur);
+    R::load(x + static_cast<int64_t>(blockIdx.x) * ldx,
+            valid_cols<MASKED>(mk, blockIdx.x, N), base, cur);
     int it = 0;
     for (int64_t row = blockIdx.x; row < M; row += step, ++it) {
         const int64_t rn = row + step;
         const Target<Tr> tg = fetch_target<Tr, CE>(so, row, x + row * ldx, N);
-        if (rn < M) R::load(x + rn * ldx, N, base, nxt);
+        if (rn < M) R::load(x + rn * ldx, valid_cols<MASKED>(mk, rn, N), base, nxt);
         float ml;
         const State st = R::reduce(cur, wr, lane, lds[it & 1], ml);
         R::write(y + row * ldy, N, base, st, ml, cur);
@@ -282,14 +310,15 @@ struct Tiles {
     }
 
     // Pass 2 over [0, n) for the row state st: Prob writes e^(x - m) / d,
-    // LogProb writes (x - m) - log d.  Tile t+1 is read before tile t is
-    // written, which is safe in place (they are different elements).  REV
-    // walks the tiles last to first: after a pass 1 that went first to last,
-    // the most recently read lines come first, while they are most likely
-    // still in the Infinity Cache.
+    // LogProb writes (x - m) - log d.  Only [0, nl) is read (nl <= n; the
+    // rest loads as -inf: masked columns).  Tile t+1 is read before tile t
+    // is written, which is safe in place (they are different elements).
+    // REV walks the tiles last to first: after a pass 1 that went first to
+    // last, the most recently read lines come first, while they are most
+    // likely still in the Infinity Cache.
     template <Out OUT, bool REV>
     __device__ __forceinline__ static void normalize(const elem_t *p, elem_t *q,
-                                                     int n, int base,
+                                                     int nl, int n, int base,
                                                      const State &st) {
         static_assert(OUT != Out::None, "pass 2 writes something");
         const float r = safe_ref(st.m);
@@ -298,11 +327,11 @@ struct Tiles {
         const int nt = num_tiles(n);
         float cur[K], nxt[K];
         const int t0 = REV ? nt - 1 : 0;
-        load_tile(p, t0, base, n, tile_full(t0, n), cur);
+        load_tile(p, t0, base, nl, tile_full(t0, nl), cur);
         for (int i = 0; i < nt; ++i) {
             const int t = REV ? nt - 1 - i : i;
             const int tn = REV ? t - 1 : t + 1;
-            if (i + 1 < nt) load_tile(p, tn, base, n, tile_full(tn, n), nxt);
+            if (i + 1 < nt) load_tile(p, tn, base, nl, tile_full(tn, nl), nxt);
             if constexpr (OUT == Out::Prob) {
 #pragma unroll
                 for (int k = 0; k < K; ++k) cur[k] = (cur[k] - r) * kLog2e;
@@ -335,10 +364,10 @@ using StreamingNT = TwoPass<true, true, true, false>;
 // pass-1-only statistics kernel (one read of x).
 // ---------------------------------------------------------------------------
 template <class Tr, bool VEC, int WAVES, int U, Out OUT, class Pol = StreamingNT,
-          bool CE = false>
+          bool CE = false, bool MASKED = false>
 __global__ __launch_bounds__(kWave *WAVES) void stream_kernel(
     const typename Tr::elem_t *x, int64_t ldx, typename Tr::elem_t *y,
-    int64_t ldy, int N, StatsOut so) {
+    int64_t ldy, int N, StatsOut so, Mask mk) {
     using T = Tiles<Tr, VEC, WAVES, U, Pol::nt1>;
     using T2 = Tiles<Tr, VEC, WAVES, U, Pol::nt2, Pol::nts>;
     __shared__ float2 lds[WAVES];
@@ -349,13 +378,14 @@ __global__ __launch_bounds__(kWave *WAVES) void stream_kernel(
     const typename Tr::elem_t *xr = x + row * ldx;
 
     const Target<Tr> tg = fetch_target<Tr, CE>(so, row, xr, N);
+    const int nv = valid_cols<MASKED>(mk, row, N);
     float m = kNegInf, d = 0.0f;
-    T::fold(xr, N, base, m, d);
+    T::fold(xr, nv, base, m, d);
     State st = wave_merge(m, d);
     st = block_merge<WAVES>(st, wave, lane, lds);
 
     if constexpr (OUT != Out::None) {
-        T2::template normalize<OUT, Pol::rev>(xr, y + row * ldy, N, base, st);
+        T2::template normalize<OUT, Pol::rev>(xr, y + row * ldy, nv, N, base, st);
     }
     if (threadIdx.x == 0) write_row_stats<Tr, CE>(so, row, st, tg, N);
 }
@@ -366,10 +396,11 @@ __global__ __launch_bounds__(kWave *WAVES) void stream_kernel(
 // partial results).  Row i is cut into P chunks of C elements (the last one
 // shorter); workgroup b handles row b / P, chunk b % P.
 // ---------------------------------------------------------------------------
-template <class Tr, bool VEC, int WAVES, int U, class Pol = StreamingNT>
+template <class Tr, bool VEC, int WAVES, int U, class Pol = StreamingNT,
+          bool MASKED = false>
 __global__ __launch_bounds__(kWave *WAVES) void split_partial_kernel(
     const typename Tr::elem_t *x, int64_t ldx, int N, int P, int C,
-    float *ws_m, float *ws_d) {
+    float *ws_m, float *ws_d, Mask mk) {
     using T = Tiles<Tr, VEC, WAVES, U, Pol::nt1>;
     __shared__ float2 lds[WAVES];
     const int lane = threadIdx.x & (kWave - 1);
@@ -378,7 +409,9 @@ __global__ __launch_bounds__(kWave *WAVES) void split_partial_kernel(
     const int64_t row = b / P;
     const int p = static_cast<int>(b - row * P);
     const int c0 = p * C;
-    const int n = min(C, N - c0);
+    // may be <= 0 for a chunk past a masked row's end: nothing is read and
+    // the chunk's state is the identity
+    const int n = min(C, valid_cols<MASKED>(mk, row, N) - c0);
 
     float m = kNegInf, d = 0.0f;
     T::fold(x + row * ldx + c0, n, wave * kWave + lane, m, d);
@@ -390,11 +423,12 @@ __global__ __launch_bounds__(kWave *WAVES) void split_partial_kernel(
     }
 }
 
-template <class Tr, bool VEC, int WAVES, int U, Out OUT, class Pol = StreamingNT>
+template <class Tr, bool VEC, int WAVES, int U, Out OUT, class Pol = StreamingNT,
+          bool MASKED = false>
 __global__ __launch_bounds__(kWave *WAVES) void split_normalize_kernel(
     const typename Tr::elem_t *x, int64_t ldx, typename Tr::elem_t *y,
     int64_t ldy, int N, int P, int C, const float *row_m,
-    const float *row_d) {
+    const float *row_d, Mask mk) {
     using T = Tiles<Tr, VEC, WAVES, U, Pol::nt2, Pol::nts>;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
@@ -403,9 +437,10 @@ __global__ __launch_bounds__(kWave *WAVES) void split_normalize_kernel(
     const int p = static_cast<int>(b - row * P);
     const int c0 = p * C;
     const int n = min(C, N - c0);
+    const int nl = min(n, valid_cols<MASKED>(mk, row, N) - c0);
     const State st{row_m[row], row_d[row]};
     T::template normalize<OUT, Pol::rev>(x + row * ldx + c0, y + row * ldy + c0,
-                                         n, wave * kWave + lane, st);
+                                         nl, n, wave * kWave + lane, st);
 }
 
 // ---------------------------------------------------------------------------

@@ -26,9 +26,15 @@ struct FwdArgs {
     // cross-entropy (Mode::Stats only): loss[row] against labels[row]
     const int64_t *labels;
     float *loss;
+    // masked rows (Mode::Prob / LogProb only): valid lengths (nullable) and
+    // a causal offset (< 0: none)
+    const int32_t *row_len;
+    int64_t causal;
     Dt dt;
     bool vec;         // 16-byte vector access is legal for x (and y)
     hipStream_t stream;
+
+    bool masked() const { return row_len != nullptr || causal >= 0; }
 };
 
 // Resident single-read path: rows of up to kResidentMaxN elements.

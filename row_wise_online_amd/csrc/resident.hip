@@ -15,29 +15,29 @@ StatsOut stats_of(const FwdArgs &a) {
     return StatsOut{a.m_out, a.d_out, a.lse_out, a.inc_out, a.labels, a.loss};
 }
 
-template <class Tr, bool VEC, int WAVES, int EPL, Out OUT, bool CE>
+template <class Tr, bool VEC, int WAVES, int EPL, Out OUT, bool CE, bool MK>
 void run(const FwdArgs &a) {
     constexpr int W = VEC ? Tr::E : 1;
     static_assert(EPL % W == 0, "a lane holds whole slots");
     constexpr int SPL = EPL / W;
     using E = typename Tr::elem_t;
-    resident_kernel<Tr, VEC, WAVES, SPL, true, OUT, CE>
+    resident_kernel<Tr, VEC, WAVES, SPL, true, OUT, CE, MK>
         <<<dim3(static_cast<unsigned>(a.M)), dim3(kWave * WAVES), 0, a.stream>>>(
             static_cast<const E *>(a.x), a.ldx, static_cast<E *>(a.y), a.ldy,
-            a.N, stats_of(a));
+            a.N, stats_of(a), Mask{a.row_len, a.causal});
 }
 
-template <class Tr, bool VEC, int WAVES, int EPL, Out OUT, bool CE>
+template <class Tr, bool VEC, int WAVES, int EPL, Out OUT, bool CE, bool MK>
 void run_persistent(const FwdArgs &a) {
     constexpr int W = VEC ? Tr::E : 1;
     static_assert(EPL % W == 0, "a lane holds whole slots");
     constexpr int SPL = EPL / W;
     const int64_t g = a.M < kPersistentWgs ? a.M : kPersistentWgs;
     using E = typename Tr::elem_t;
-    resident_persistent_kernel<Tr, VEC, WAVES, SPL, true, OUT, CE>
+    resident_persistent_kernel<Tr, VEC, WAVES, SPL, true, OUT, CE, MK>
         <<<dim3(static_cast<unsigned>(g)), dim3(kWave * WAVES), 0, a.stream>>>(
             static_cast<const E *>(a.x), a.ldx, static_cast<E *>(a.y), a.ldy,
-            a.M, a.N, stats_of(a));
+            a.M, a.N, stats_of(a), Mask{a.row_len, a.causal});
 }
 
 // Variant ladder by row length (elements), measured on MI355X (interleaved
@@ -45,34 +45,41 @@ void run_persistent(const FwdArgs &a) {
 // columns (bf16 32768 x 1024: 5.87 TB/s); 8 waves x 8 values per lane for
 // 4096 columns (fp32: 5.9 TB/s, ahead of 4 x 16 and 2 x 32); 8 waves x 64
 // values per lane, persistent, for 32768 columns (fp32: 6.07 TB/s).
-template <class Tr, bool VEC, Out OUT, bool CE = false>
+template <class Tr, bool VEC, Out OUT, bool CE = false, bool MK = false>
 void dispatch(const FwdArgs &a) {
     const int N = a.N;
     constexpr bool kSmallOk = !VEC || Tr::E <= 4;  // EPL 4 holds whole slots
     if (kSmallOk && N <= 256) {
-        if constexpr (kSmallOk) run<Tr, VEC, 1, 4, OUT, CE>(a);
+        if constexpr (kSmallOk) run<Tr, VEC, 1, 4, OUT, CE, MK>(a);
     } else if (N <= 512) {
-        run<Tr, VEC, 1, 8, OUT, CE>(a);
+        run<Tr, VEC, 1, 8, OUT, CE, MK>(a);
     } else if (N <= 1024) {
-        run<Tr, VEC, 1, 16, OUT, CE>(a);
+        run<Tr, VEC, 1, 16, OUT, CE, MK>(a);
     } else if (N <= 2048) {
-        run<Tr, VEC, 4, 8, OUT, CE>(a);
+        run<Tr, VEC, 4, 8, OUT, CE, MK>(a);
     } else if (N <= 4096) {
-        run<Tr, VEC, 8, 8, OUT, CE>(a);
+        run<Tr, VEC, 8, 8, OUT, CE, MK>(a);
     } else if (N <= 8192) {
-        run<Tr, VEC, 8, 16, OUT, CE>(a);
+        run<Tr, VEC, 8, 16, OUT, CE, MK>(a);
     } else if (N <= 16384) {
-        run<Tr, VEC, 8, 32, OUT, CE>(a);
+        run<Tr, VEC, 8, 32, OUT, CE, MK>(a);
     } else {
-        run_persistent<Tr, VEC, 8, 64, OUT, CE>(a);
+        run_persistent<Tr, VEC, 8, 64, OUT, CE, MK>(a);
     }
 }
 
 template <class Tr, bool VEC>
 void by_mode(const FwdArgs &a) {
+    const bool mk = a.masked();
     switch (a.mode) {
-        case Mode::Prob: dispatch<Tr, VEC, Out::Prob>(a); break;
-        case Mode::LogProb: dispatch<Tr, VEC, Out::LogProb>(a); break;
+        case Mode::Prob:
+            if (mk) dispatch<Tr, VEC, Out::Prob, false, true>(a);
+            else dispatch<Tr, VEC, Out::Prob>(a);
+            break;
+        case Mode::LogProb:
+            if (mk) dispatch<Tr, VEC, Out::LogProb, false, true>(a);
+            else dispatch<Tr, VEC, Out::LogProb>(a);
+            break;
         default:
             if (a.labels) dispatch<Tr, VEC, Out::None, true>(a);
             else dispatch<Tr, VEC, Out::None>(a);

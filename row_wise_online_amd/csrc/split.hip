@@ -41,7 +41,7 @@ WsLayout layout(void *ws, int64_t M, int P) {
     return l;
 }
 
-template <class Tr, bool VEC, class Pol>
+template <class Tr, bool VEC, class Pol, bool MK>
 void run(const FwdArgs &a, void *ws) {
     using E = typename Tr::elem_t;
     constexpr int U = tile_slots<Tr, VEC>();
@@ -51,8 +51,9 @@ void run(const FwdArgs &a, void *ws) {
     const dim3 block(kWave * kSplitWaves);
     const E *x = static_cast<const E *>(a.x);
 
-    split_partial_kernel<Tr, VEC, kSplitWaves, U, Pol><<<grid, block, 0, a.stream>>>(
-        x, a.ldx, a.N, plan.P, plan.C, l.part_m, l.part_d);
+    const Mask mk{a.row_len, a.causal};
+    split_partial_kernel<Tr, VEC, kSplitWaves, U, Pol, MK><<<grid, block, 0, a.stream>>>(
+        x, a.ldx, a.N, plan.P, plan.C, l.part_m, l.part_d, mk);
 
     // Row states go to the workspace (read by the normalise kernel) and to
     // whichever of the caller's m / d / lse / cross-entropy are asked for,
@@ -73,21 +74,22 @@ void run(const FwdArgs &a, void *ws) {
     if (a.mode != Mode::Stats) {
         E *y = static_cast<E *>(a.y);
         if (a.mode == Mode::Prob) {
-            split_normalize_kernel<Tr, VEC, kSplitWaves, U, Out::Prob, Pol>
+            split_normalize_kernel<Tr, VEC, kSplitWaves, U, Out::Prob, Pol, MK>
                 <<<grid, block, 0, a.stream>>>(x, a.ldx, y, a.ldy, a.N, plan.P,
-                                               plan.C, l.row_m, l.row_d);
+                                               plan.C, l.row_m, l.row_d, mk);
         } else {
-            split_normalize_kernel<Tr, VEC, kSplitWaves, U, Out::LogProb, Pol>
+            split_normalize_kernel<Tr, VEC, kSplitWaves, U, Out::LogProb, Pol, MK>
                 <<<grid, block, 0, a.stream>>>(x, a.ldx, y, a.ldy, a.N, plan.P,
-                                               plan.C, l.row_m, l.row_d);
+                                               plan.C, l.row_m, l.row_d, mk);
         }
     }
 }
 
 template <class Tr, bool VEC>
 void by_mode(const FwdArgs &a, void *ws) {
-    if (a.mode == Mode::Stats) run<Tr, VEC, StatsPolicy>(a, ws);
-    else run<Tr, VEC, SplitPolicy>(a, ws);
+    if (a.mode == Mode::Stats) run<Tr, VEC, StatsPolicy, false>(a, ws);
+    else if (a.masked()) run<Tr, VEC, SplitPolicy, true>(a, ws);
+    else run<Tr, VEC, SplitPolicy, false>(a, ws);
 }
 
 }  // namespace

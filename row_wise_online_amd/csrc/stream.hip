@@ -23,22 +23,30 @@ constexpr int tile_slots() {
     return VEC ? 32 / Tr::E : 16;
 }
 
-template <class Tr, bool VEC, Out OUT, class Pol, bool CE = false>
+template <class Tr, bool VEC, Out OUT, class Pol, bool CE = false,
+          bool MK = false>
 void run(const FwdArgs &a) {
     using E = typename Tr::elem_t;
     constexpr int U = tile_slots<Tr, VEC>();
     const StatsOut so{a.m_out, a.d_out, a.lse_out, a.inc_out, a.labels, a.loss};
-    stream_kernel<Tr, VEC, kStreamWaves, U, OUT, Pol, CE>
+    stream_kernel<Tr, VEC, kStreamWaves, U, OUT, Pol, CE, MK>
         <<<dim3(static_cast<unsigned>(a.M)), dim3(kWave * kStreamWaves), 0, a.stream>>>(
             static_cast<const E *>(a.x), a.ldx, static_cast<E *>(a.y), a.ldy,
-            a.N, so);
+            a.N, so, Mask{a.row_len, a.causal});
 }
 
 template <class Tr, bool VEC>
 void by_mode(const FwdArgs &a) {
+    const bool mk = a.masked();
     switch (a.mode) {
-        case Mode::Prob: run<Tr, VEC, Out::Prob, StreamPolicy>(a); break;
-        case Mode::LogProb: run<Tr, VEC, Out::LogProb, StreamPolicy>(a); break;
+        case Mode::Prob:
+            if (mk) run<Tr, VEC, Out::Prob, StreamPolicy, false, true>(a);
+            else run<Tr, VEC, Out::Prob, StreamPolicy>(a);
+            break;
+        case Mode::LogProb:
+            if (mk) run<Tr, VEC, Out::LogProb, StreamPolicy, false, true>(a);
+            else run<Tr, VEC, Out::LogProb, StreamPolicy>(a);
+            break;
         default:
             if (a.labels) run<Tr, VEC, Out::None, StatsPolicy, true>(a);
             else run<Tr, VEC, Out::None, StatsPolicy>(a);

@@ -180,3 +180,22 @@ def test_cross_entropy_empty_without_mean_is_noop(lib):
 def test_stats_resident_path_limit(lib):
     # the register-resident statistics kernel takes rows up to 32768
     assert _stats(lib, M=4, N=40000, ldx=40000, path=1) == 7
+
+
+def _masked(lib, fn, x=FAKE, ldx=8, y=FAKE, ldy=8, M=4, N=8, dt=0, row_len=NUL,
+            causal=-1, path=0):
+    return getattr(lib, fn)(x, ldx, y, ldy, M, N, dt, row_len, causal, NUL,
+                            NUL, NUL, NUL, 0, path, NUL)
+
+
+@pytest.mark.parametrize("fn", ["os_softmax_fwd_masked",
+                                "os_log_softmax_fwd_masked"])
+@pytest.mark.parametrize("kw,status", [
+    (dict(M=-1), 2), (dict(N=0), 2), (dict(ldx=7), 3), (dict(dt=9), 4),
+    (dict(x=NUL), 1), (dict(y=NUL), 1), (dict(path=8), 6),
+    (dict(N=40000, ldx=40000, ldy=40000, path=1), 7),
+    (dict(M=16, N=1 << 22, ldx=1 << 22, ldy=1 << 22, path=3, causal=5), 5),
+])
+def test_masked_validation(lib, fn, kw, status):
+    assert _masked(lib, fn, **kw) == status
+    assert _masked(lib, fn, x=NUL, y=NUL, M=0, causal=3) == 0

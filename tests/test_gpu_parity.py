@@ -523,3 +523,81 @@ def test_cross_entropy_workloads(name):
     lh = loss.cpu().numpy().astype(np.float64)
     keep = lab >= 0
     assert abs(mean.item() - lh[keep].mean()) <= 1e-5 * abs(lh[keep].mean())
+
+
+# ---------------------------------------------------------------------------
+# Masked rows: valid lengths and causal offsets
+# ---------------------------------------------------------------------------
+
+def _lengths(M, N, seed):
+    rng = np.random.default_rng(seed)
+    rl = rng.integers(0, N + 1, size=M).astype(np.int32)
+    rl[0] = 0                      # fully masked row
+    if M > 1:
+        rl[1] = N + 100            # longer than the row: no mask
+    if M > 2:
+        rl[2] = -7                 # negative: fully masked
+    if M > 3:
+        rl[3] = 1
+    return rl
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("path", ["resident", "stream", "split"])
+def test_masked_paths(path, dtype):
+    shapes = [(7, 65), (9, 1000), (6, 4096), (5, 8191), (5, 32768)]
+    if path != "resident":
+        shapes += [(5, 70001)]
+    for i, (M, N) in enumerate(shapes):
+        for misalign in (False, True):
+            x_h = _input(M, N, dtype, seed=500 + i, misalign=misalign)
+            x = to_device(x_h)
+            for case, (rl, causal) in enumerate([
+                    (_lengths(M, N, 500 + i), None),
+                    (None, 0), (None, N // 3),
+                    (_lengths(M, N, 600 + i), N // 2)]):
+                what = (f"masked {path} {dtype} {M}x{N} misalign={misalign} "
+                        f"case={case}")
+                rl_t = None if rl is None else torch.from_numpy(rl).cuda()
+                y = empty_like_rows(x)
+                ly = empty_like_rows(x)
+                m = torch.empty(M, device="cuda")
+                d = torch.empty(M, device="cuda")
+                lse = torch.empty(M, device="cuda")
+                rw.softmax_fwd(x, y, m=m, d=d, lse=lse, path=path,
+                               row_len=rl_t, causal=causal)
+                rw.log_softmax_fwd(x, ly, path=path, row_len=rl_t,
+                                   causal=causal)
+                torch.cuda.synchronize()
+                y_ref, ly_ref, m_ref, d_ref, l_ref = oracle.softmax_masked(
+                    x_h, rl, -1 if causal is None else causal)
+                yh = to_host(y)
+                ok = ~np.isnan(y_ref[:, 0])          # rows with columns
+                yf = yh.astype(np.float64) if yh.dtype == np.float32 else \
+                    oracle.bf16_bits_to_f64(yh)
+                assert np.all(np.isnan(yf[~ok])), what
+                check_y(yh[ok], y_ref[ok], what)
+                check_log(to_host(ly), ly_ref, what)
+                mh, dh, lh = m.cpu().numpy(), d.cpu().numpy(), lse.cpu().numpy()
+                check_m(mh, m_ref, what)
+                assert np.all(dh[~ok] == 0) and np.all(lh[~ok] == -np.inf), what
+                check_d(dh[ok], d_ref[ok], what)
+                check_lse(lh[ok], l_ref[ok], what)
+
+
+@pytest.mark.parametrize("path", ["resident", "stream", "split"])
+def test_masked_in_place_and_reads(path):
+    # masked columns are never read: NaN there must not leak into the row
+    M, N = 6, 3000
+    v = np.random.default_rng(19).standard_normal((M, N)) * 2.0
+    rl = np.array([3000, 2999, 1500, 1, 64, 0], np.int32)
+    for i, n in enumerate(rl):
+        v[i, n:] = np.nan
+    x_h = wl.from_values(v)
+    x = to_device(x_h)
+    rw.softmax_fwd(x, x, path=path, row_len=torch.from_numpy(rl).cuda())
+    torch.cuda.synchronize()
+    y_ref, *_ = oracle.softmax_masked(x_h, rl)
+    yh = to_host(x)
+    check_y(yh[:5], y_ref[:5], f"masked in place {path}")
+    assert np.all(np.isnan(yh[5]))
