@@ -42,24 +42,34 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def algorithmic_bytes(w, path, n_stats, op="softmax"):
+def valid_elements(w, causal):
+    """Elements a causal mask with this offset leaves in the workload."""
+    if causal is None:
+        return w.M * w.N
+    i = __import__("numpy").arange(w.M, dtype="int64")
+    return int(__import__("numpy").minimum(w.N, i + causal + 1).sum())
+
+
+def algorithmic_bytes(w, path, n_stats, op="softmax", causal=None):
     """Bytes the path must move for one step of workload w: x read once per
-    read pass, y written once, row statistics written; the cross-entropy
-    reads x once and moves 8 B of label + 4 B of loss per row (+ 4 B mean)."""
+    read pass (only the unmasked part of each row), y written once (all of
+    it), row statistics written; the cross-entropy reads x once and moves
+    8 B of label + 4 B of loss per row (+ 4 B mean)."""
     import row_wise_online_amd as rw
     xy = w.M * w.N * w.esize
+    xr = valid_elements(w, causal) * w.esize
     if op == "cross_entropy":
         b = xy + 12 * w.M + 4
     else:
         reads = 1 if path == "resident" else 2
-        b = reads * xy + xy + 4 * w.M * n_stats
+        b = reads * xr + xy + 4 * w.M * n_stats
     if path == "split":
         b += 2 * rw.workspace_bytes(w.M, w.N, w.dtype, "split")  # states w+r
     return b
 
 
 def measure(w, steps, warmup, path="auto", rotate=True, graph=False,
-            op="softmax"):
+            op="softmax", causal=None):
     """Average device time per step (ms), the rotation depth, and the host
     time per launch (us).  Steps cycle over R buffer sets; with graph=True
     the launches are captured once in a HIP graph and replayed."""
@@ -96,7 +106,8 @@ def measure(w, steps, warmup, path="auto", rotate=True, graph=False,
                                              ws=ws, path=path)
                     for i in range(R)]
         return [rw.prepare_fwd(xs[i], ys[i], m=m, d=d, lse=lse, ws=ws,
-                               path=path, log=(op == "log_softmax"))
+                               path=path, log=(op == "log_softmax"),
+                               causal=causal)
                 for i in range(R)]
 
     start = torch.cuda.Event(enable_timing=True)
@@ -162,7 +173,7 @@ def copy_ceiling(nbytes, steps=50):
     return 2 * nbytes / (ms * 1e-3) / 1e9
 
 
-def cpu_baseline(w, n_stats, budget_s, op="softmax"):
+def cpu_baseline(w, n_stats, budget_s, op="softmax", causal=None):
     """The fp64 oracle, as it is, on this host: whole input matrices of the
     workload, repeated until about budget_s seconds have passed."""
     import numpy as np
@@ -174,6 +185,10 @@ def cpu_baseline(w, n_stats, budget_s, op="softmax"):
         fn = lambda: oracle.cross_entropy(x, labels)
         what = "cross-entropy (loss, mean)"
         b = w.M * w.N * w.esize + 12 * w.M + 4
+    elif causal is not None:
+        fn = lambda: oracle.softmax_masked(x, None, causal)
+        what = f"causal (offset {causal}) softmax and log-softmax"
+        b = (valid_elements(w, causal) + w.M * w.N) * w.esize
     elif op == "log_softmax":
         fn = lambda: oracle.log_softmax(x)
         what = "log-softmax"
@@ -211,7 +226,7 @@ def traffic_record(workload):
 
 
 def run_workload(name, steps, warmup, path="auto", want_cpu=True,
-                 cpu_budget=10.0, extras=True, op="softmax"):
+                 cpu_budget=10.0, extras=True, op="softmax", causal=None):
     import row_wise_online_amd as rw
     from row_wise_online_amd import workloads as wl
     w = wl.WORKLOADS[name]
@@ -219,18 +234,24 @@ def run_workload(name, steps, warmup, path="auto", want_cpu=True,
     n_stats = len(set(w.outputs) & {"m", "d", "lse"})
     if op == "cross_entropy":
         n_stats = 0
-    ms, R, host_us = measure(w, steps, warmup, path, op=op)
+    if causal is not None and op == "cross_entropy":
+        raise ValueError("the causal mask applies to softmax / log-softmax")
+    ms, R, host_us = measure(w, steps, warmup, path, op=op, causal=causal)
     if extras:
-        graph_ms, _, _ = measure(w, steps, warmup, path, graph=True, op=op)
+        graph_ms, _, _ = measure(w, steps, warmup, path, graph=True, op=op,
+                                 causal=causal)
         warm_ms, _, _ = measure(w, max(10, steps // 4), 3, path,
-                                rotate=False, op=op)
-    nbytes = algorithmic_bytes(w, resolved, n_stats, op)
+                                rotate=False, op=op, causal=causal)
+    nbytes = algorithmic_bytes(w, resolved, n_stats, op, causal)
     gbs = nbytes / (ms * 1e-3) / 1e9
     eff = (2 * w.M * w.N * w.esize + 4 * w.M * n_stats) / (ms * 1e-3) / 1e9
     opname = {"softmax": "softmax", "log_softmax": "log-softmax",
               "cross_entropy": "cross-entropy"}[op]
+    if causal is not None:
+        opname = f"causal (offset {causal}) {opname}"
     rec = {
-        "metric": METRIC if (name == "c2" and op == "softmax") else
+        "metric": METRIC if (name == "c2" and op == "softmax" and
+                             causal is None) else
         f"achieved HBM GB/s (% of peak) + rows/s, online {opname} fwd "
         f"{w.dtype} {w.M}x{w.N}",
         "value": round(gbs, 1),
@@ -246,6 +267,7 @@ def run_workload(name, steps, warmup, path="auto", want_cpu=True,
         "data": "synthetic (seeded numpy PCG64 normals, HBM-resident, "
                 f"{R} rotating buffer sets)",
         "config": {"workload": w.desc, "M": w.M, "N": w.N, "op": op,
+                   "causal_offset": causal,
                    "outputs": (["loss", "mean"] if op == "cross_entropy"
                                else list(w.outputs)), "path": resolved},
         "pct_of_peak": round(100.0 * gbs / PEAK_GBS, 2),
@@ -258,7 +280,8 @@ def run_workload(name, steps, warmup, path="auto", want_cpu=True,
             "peak": PEAK_GBS,
             "unit": "GB/s",
             "frac": round(gbs / PEAK_GBS, 4),
-            "traffic": traffic_record(name) if op == "softmax" else None,
+            "traffic": traffic_record(name) if (op == "softmax" and
+                                            causal is None) else None,
             "algorithmic_bytes_per_launch": nbytes,
             "kernel_launches_per_step": 1 if resolved != "split" else 3,
         },
@@ -270,7 +293,7 @@ def run_workload(name, steps, warmup, path="auto", want_cpu=True,
     rec["copy_ceiling_GBps"] = round(
         copy_ceiling(w.M * w.N * w.esize), 1)
     if want_cpu:
-        rec["cpu_baseline"] = cpu_baseline(w, n_stats, cpu_budget, op)
+        rec["cpu_baseline"] = cpu_baseline(w, n_stats, cpu_budget, op, causal)
     return rec
 
 
@@ -286,6 +309,8 @@ def main():
                     choices=["auto", "resident", "stream", "split"])
     ap.add_argument("--op", default="softmax",
                     choices=["softmax", "log_softmax", "cross_entropy"])
+    ap.add_argument("--causal", type=int, default=None,
+                    help="causal mask offset (softmax / log-softmax)")
     ap.add_argument("--all", action="store_true",
                     help="also report every workload on stderr")
     ap.add_argument("--no-cpu", action="store_true",
@@ -319,11 +344,19 @@ def main():
                                  want_cpu=False, extras=not args.no_extras,
                                  op=op)
                 print(json.dumps(r), file=sys.stderr, flush=True)
+        for name in ["c2", "c3"]:
+            print(f"[bench] causal softmax workload {name}", file=sys.stderr,
+                  flush=True)
+            r = run_workload(name, args.steps, args.warmup, "auto",
+                             want_cpu=False, extras=not args.no_extras,
+                             causal=0)
+            print(json.dumps(r), file=sys.stderr, flush=True)
     print(f"[bench] headline workload {args.workload}", file=sys.stderr,
           flush=True)
     rec = run_workload(args.workload, args.steps, args.warmup, args.path,
                        want_cpu=not args.no_cpu, cpu_budget=args.cpu_budget,
-                       extras=not args.no_extras, op=args.op)
+                       extras=not args.no_extras, op=args.op,
+                       causal=args.causal)
     print(json.dumps(rec), flush=True)
 
 

@@ -190,7 +190,7 @@ def cross_entropy_fwd(x, labels, loss=None, *, lse=None, mean=None, ws=None,
 
 
 def prepare_fwd(x, y, *, m=None, d=None, lse=None, ws=None, path="auto",
-                stream=None, log=False):
+                stream=None, log=False, causal=None):
     """Marshal the arguments of one softmax_fwd (log=True: log_softmax_fwd)
     call once and return a function that repeats the call (same tensors,
     same stream) with only the ctypes call left per invocation -- for tight
@@ -207,9 +207,15 @@ def prepare_fwd(x, y, *, m=None, d=None, lse=None, ws=None, path="auto",
     if need and ws is None:
         raise ValueError(f"path needs a workspace of {need} bytes")
     wp, wb = _workspace(ws, need, x.device)
-    args = (xp, ldx, yp, ldy, M, N, dt, _vec(m, "m", M), _vec(d, "d", M),
-            _vec(lse, "lse", M), wp, wb, pc, _stream(stream))
+    stats = (_vec(m, "m", M), _vec(d, "d", M), _vec(lse, "lse", M))
     name = "os_log_softmax_fwd_path" if log else "os_softmax_fwd_path"
+    if causal is None:
+        args = (xp, ldx, yp, ldy, M, N, dt, *stats, wp, wb, pc,
+                _stream(stream))
+    else:
+        name = name.replace("_path", "_masked")
+        args = (xp, ldx, yp, ldy, M, N, dt, None, int(causal), *stats, wp,
+                wb, pc, _stream(stream))
     fn = getattr(lib, name)
     keep = (x, y, m, d, lse, ws)   # the tensors must outlive the closure
 
