@@ -204,6 +204,21 @@ os_status os_cross_entropy_fwd_path(const void *x, int64_t ld_x, int64_t M,
                                     size_t ws_bytes, os_path path,
                                     hipStream_t stream);
 
+/* Streaming statistics: fold the state of this column window into a
+ * running per-row state, in place.  m_io[i*inc], d_io[i*inc] (fp32,
+ * required) hold the running (m, d) of the columns seen so far -- start from
+ * the identity (-inf, 0) -- and receive the merge of it with this window's
+ * state ("Softmax 数值稳定性与 IO-Aware Attention" §4.1: chunk the row, take
+ * each chunk's state, merge repeatedly; "从原始Softmax到在线Softmax": the state
+ * is updated block by block).  lse_out (nullable) receives the LSE of the
+ * merged state.  Calls on the same stream apply in order.  Paths, workspace
+ * and errors as os_softmax_stats_path. */
+os_status os_softmax_stats_update(const void *x, int64_t ld_x, int64_t M,
+                                  int64_t N, os_dtype dt, float *m_io,
+                                  float *d_io, int64_t inc, float *lse_out,
+                                  void *ws, size_t ws_bytes, os_path path,
+                                  hipStream_t stream);
+
 /* Merge K partial states per row ("5.2 CUDA Online Softmax 实现优化" §4.1):
  * row i's states are (m_in[i*ld_in + k], d_in[i*ld_in + k]), k < K, fp32.
  * (-inf, 0) is an exact identity.  Writes m_out[i], d_out[i] (required) and

@@ -14,6 +14,7 @@ Same names as the C ABI, without the ``os_`` prefix:
 * ``cross_entropy_fwd(x, labels, loss=None, lse=None, mean=None, ws=None,
   path="auto")``
 * ``softmax_stats(x, m, d, lse=None, inc=1, ws=None, path="auto")``
+* ``softmax_stats_update(x, m, d, lse=None, inc=1, ws=None, path="auto")``
 * ``state_merge(m_in, d_in, m_out, d_out, lse_out=None)``
 * ``workspace_bytes(M, N, dtype, path="auto")``, ``select_path(M, N, dtype)``
 """
@@ -22,6 +23,7 @@ from ._lib import OsError, PATHS, PATH_NAMES  # noqa: F401
 
 __all__ = ["softmax_fwd", "log_softmax_fwd", "cross_entropy_fwd",
            "prepare_fwd", "prepare_cross_entropy", "softmax_stats",
+           "softmax_stats_update",
            "state_merge", "workspace_bytes", "select_path", "OsError", "load"]
 
 
@@ -273,6 +275,24 @@ def softmax_stats(x, m, d, lse=None, *, inc=1, ws=None, path="auto",
                                    inc, _vec(lse, "lse", M, inc), wp, wb, pc,
                                    _stream(stream))
     _lib.check("os_softmax_stats_path", st)
+
+
+def softmax_stats_update(x, m, d, lse=None, *, inc=1, ws=None, path="auto",
+                         stream=None):
+    """Merge the state of the column window x into the running per-row
+    state (m, d) in place (start from m = -inf, d = 0)."""
+    lib = _lib.load()
+    dt = _dtype_code(x.dtype)
+    xp, ldx = _matrix(x, "x")
+    M, N = x.shape
+    pc = _path_code(path)
+    need = lib.os_softmax_workspace_bytes(M, N, dt, pc)
+    wp, wb = _workspace(ws, need, x.device)
+    st = lib.os_softmax_stats_update(xp, ldx, M, N, dt, _vec(m, "m", M, inc),
+                                     _vec(d, "d", M, inc), inc,
+                                     _vec(lse, "lse", M, inc), wp, wb, pc,
+                                     _stream(stream))
+    _lib.check("os_softmax_stats_update", st)
 
 
 def state_merge(m_in, d_in, m_out, d_out, lse_out=None, *, stream=None):

@@ -53,6 +53,8 @@ SIGNATURES = {
                                 _vp, _vp, _sz, _vp]),
     "os_softmax_stats_path": (_i32, [_vp, _i64, _i64, _i64, _i32, _vp, _vp,
                                      _i64, _vp, _vp, _sz, _i32, _vp]),
+    "os_softmax_stats_update": (_i32, [_vp, _i64, _i64, _i64, _i32, _vp, _vp,
+                                       _i64, _vp, _vp, _sz, _i32, _vp]),
     "os_state_merge": (_i32, [_vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp,
                               _vp]),
     "os_softmax_workspace_bytes": (_sz, [_i64, _i64, _i32, _i32]),

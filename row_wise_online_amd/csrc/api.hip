@@ -182,11 +182,12 @@ os_status os_log_softmax_fwd_masked(const void *x, int64_t ld_x, void *y,
                lse_out, ws, ws_bytes, path, stream, row_len, causal_offset);
 }
 
-os_status os_softmax_stats_path(const void *x, int64_t ld_x, int64_t M,
-                                int64_t N, os_dtype dt, float *m_out,
-                                float *d_out, int64_t inc_out, float *lse_out,
-                                void *ws, size_t ws_bytes, os_path path,
-                                hipStream_t stream) {
+namespace {
+
+os_status stats(const void *x, int64_t ld_x, int64_t M, int64_t N,
+                os_dtype dt, float *m_out, float *d_out, int64_t inc_out,
+                float *lse_out, void *ws, size_t ws_bytes, os_path path,
+                hipStream_t stream, bool accumulate) {
     os_status s = check_shape(M, N, dt);
     if (s != OS_OK) return s;
     if (!valid_path(path)) return OS_ERR_PATH;
@@ -201,7 +202,28 @@ os_status os_softmax_stats_path(const void *x, int64_t ld_x, int64_t M,
     a.d_out = d_out;
     a.lse_out = lse_out;
     a.inc_out = inc_out;
+    a.accumulate = accumulate;
     return launch(a, p, ws);
+}
+
+}  // namespace
+
+os_status os_softmax_stats_path(const void *x, int64_t ld_x, int64_t M,
+                                int64_t N, os_dtype dt, float *m_out,
+                                float *d_out, int64_t inc_out, float *lse_out,
+                                void *ws, size_t ws_bytes, os_path path,
+                                hipStream_t stream) {
+    return stats(x, ld_x, M, N, dt, m_out, d_out, inc_out, lse_out, ws,
+                 ws_bytes, path, stream, false);
+}
+
+os_status os_softmax_stats_update(const void *x, int64_t ld_x, int64_t M,
+                                  int64_t N, os_dtype dt, float *m_io,
+                                  float *d_io, int64_t inc, float *lse_out,
+                                  void *ws, size_t ws_bytes, os_path path,
+                                  hipStream_t stream) {
+    return stats(x, ld_x, M, N, dt, m_io, d_io, inc, lse_out, ws, ws_bytes,
+                 path, stream, true);
 }
 
 os_status os_softmax_stats(const void *x, int64_t ld_x, int64_t M, int64_t N,

@@ -33,6 +33,10 @@ struct StatsOut {
     int64_t inc;
     const int64_t *labels;
     float *loss;
+    // accumulate: m and d already hold a running state (the identity is
+    // (-inf, 0)); the row's state is merged into it in place and lse is that
+    // of the merged state
+    bool accumulate;
 };
 
 // Masked rows (kernels instantiated with MASKED = true): row i takes part
@@ -93,9 +97,10 @@ __device__ __forceinline__ Target<Tr> fetch_target(const StatsOut &o,
 // so that the large common part m cancels before rounding.
 template <class Tr, bool CE>
 __device__ __forceinline__ void write_row_stats(const StatsOut &o, int64_t row,
-                                                const State &st,
-                                                const Target<Tr> &t, int N) {
+                                                State st, const Target<Tr> &t,
+                                                int N) {
     const int64_t k = row * o.inc;
+    if (o.accumulate) merge_into(st.m, st.d, o.m[k], o.d[k]);
     const float logd = __builtin_logf(st.d);
     if (o.m) o.m[k] = st.m;
     if (o.d) o.d[k] = st.d;

@@ -23,6 +23,7 @@ struct FwdArgs {
     float *d_out;
     float *lse_out;
     int64_t inc_out;
+    bool accumulate;  // m_out / d_out hold a running state to merge into
     // cross-entropy (Mode::Stats only): loss[row] against labels[row]
     const int64_t *labels;
     float *loss;

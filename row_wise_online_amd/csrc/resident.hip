@@ -12,7 +12,8 @@ namespace {
 constexpr int64_t kPersistentWgs = 512;
 
 StatsOut stats_of(const FwdArgs &a) {
-    return StatsOut{a.m_out, a.d_out, a.lse_out, a.inc_out, a.labels, a.loss};
+    return StatsOut{a.m_out, a.d_out, a.lse_out, a.inc_out, a.labels, a.loss,
+                    a.accumulate};
 }
 
 template <class Tr, bool VEC, int WAVES, int EPL, Out OUT, bool CE, bool MK>

@@ -58,7 +58,8 @@ void run(const FwdArgs &a, void *ws) {
     // Row states go to the workspace (read by the normalise kernel) and to
     // whichever of the caller's m / d / lse / cross-entropy are asked for,
     // in one merge launch.
-    const StatsOut so{a.m_out, a.d_out, a.lse_out, a.inc_out, a.labels, a.loss};
+    const StatsOut so{a.m_out, a.d_out, a.lse_out, a.inc_out, a.labels, a.loss,
+                      a.accumulate};
     const dim3 mgrid(static_cast<unsigned>((a.M + kMergeRows - 1) / kMergeRows));
     const dim3 mblock(kWave * kMergeRows);
     if (a.labels) {
@@ -120,7 +121,7 @@ void launch_split(const FwdArgs &a, void *ws) {
 void launch_state_merge(const float *m_in, const float *d_in, int64_t ld,
                         int64_t M, int K, float *m_out, float *d_out,
                         float *lse_out, int64_t inc, hipStream_t stream) {
-    const StatsOut so{nullptr, nullptr, lse_out, inc, nullptr, nullptr};
+    const StatsOut so{nullptr, nullptr, lse_out, inc, nullptr, nullptr, false};
     state_merge_kernel<kMergeRows, F32, false>
         <<<dim3(static_cast<unsigned>((M + kMergeRows - 1) / kMergeRows)),
            dim3(kWave * kMergeRows), 0, stream>>>(m_in, d_in, ld, M, K, m_out,

@@ -28,7 +28,8 @@ template <class Tr, bool VEC, Out OUT, class Pol, bool CE = false,
 void run(const FwdArgs &a) {
     using E = typename Tr::elem_t;
     constexpr int U = tile_slots<Tr, VEC>();
-    const StatsOut so{a.m_out, a.d_out, a.lse_out, a.inc_out, a.labels, a.loss};
+    const StatsOut so{a.m_out, a.d_out, a.lse_out, a.inc_out, a.labels, a.loss,
+                      a.accumulate};
     stream_kernel<Tr, VEC, kStreamWaves, U, OUT, Pol, CE, MK>
         <<<dim3(static_cast<unsigned>(a.M)), dim3(kWave * kStreamWaves), 0, a.stream>>>(
             static_cast<const E *>(a.x), a.ldx, static_cast<E *>(a.y), a.ldy,

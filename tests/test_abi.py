@@ -199,3 +199,13 @@ def _masked(lib, fn, x=FAKE, ldx=8, y=FAKE, ldy=8, M=4, N=8, dt=0, row_len=NUL,
 def test_masked_validation(lib, fn, kw, status):
     assert _masked(lib, fn, **kw) == status
     assert _masked(lib, fn, x=NUL, y=NUL, M=0, causal=3) == 0
+
+
+def test_stats_update_validation(lib):
+    f = lambda **kw: lib.os_softmax_stats_update(
+        kw.get("x", FAKE), kw.get("ldx", 8), kw.get("M", 4), kw.get("N", 8), 0,
+        kw.get("m", FAKE), kw.get("d", FAKE), kw.get("inc", 1), NUL, NUL, 0,
+        kw.get("path", 0), NUL)
+    assert f(M=-1) == 2 and f(N=0) == 2 and f(inc=0) == 3 and f(ldx=2) == 3
+    assert f(m=NUL) == 1 and f(d=NUL) == 1 and f(x=NUL) == 1 and f(path=6) == 6
+    assert f(x=NUL, m=NUL, d=NUL, M=0) == 0

@@ -601,3 +601,47 @@ def test_masked_in_place_and_reads(path):
     yh = to_host(x)
     check_y(yh[:5], y_ref[:5], f"masked in place {path}")
     assert np.all(np.isnan(yh[5]))
+
+
+# ---------------------------------------------------------------------------
+# Streaming statistics: windows folded into a running state
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("path", ["auto", "resident", "stream", "split"])
+def test_stats_update_streams_windows(path, dtype):
+    M, N = 9, 40000
+    x_h = wl.normal(M, N, scale=3.0, seed=21, dtype=dtype)
+    x = to_device(x_h)
+    rng = np.random.default_rng(21)
+    cuts = np.sort(rng.choice(np.arange(1, N), size=7, replace=False))
+    edges = [0, *cuts.tolist(), N]
+    inc = 2
+    m = torch.full((M * inc,), float("-inf"), device="cuda")
+    d = torch.zeros(M * inc, device="cuda")
+    lse = torch.empty(M * inc, device="cuda")
+    for a, b in zip(edges[:-1], edges[1:]):
+        p = path
+        if path == "resident" and b - a > 32768:
+            p = "stream"
+        rw.softmax_stats_update(x[:, a:b], m, d, lse, inc=inc, path=p)
+    torch.cuda.synchronize()
+    _, m_ref, d_ref, l_ref = oracle.softmax(x_h, want_y=False)
+    what = f"stream windows {path} {dtype}"
+    check_m(m.cpu().numpy()[::inc], m_ref, what)
+    check_d(d.cpu().numpy()[::inc], d_ref, what)
+    check_lse(lse.cpu().numpy()[::inc], l_ref, what)
+
+
+def test_stats_update_from_identity_equals_stats():
+    x_h = wl.normal(33, 2000, scale=2.0, seed=22)
+    x = to_device(x_h)
+    m = torch.full((33,), float("-inf"), device="cuda")
+    d = torch.zeros(33, device="cuda")
+    rw.softmax_stats_update(x, m, d)
+    m2 = torch.empty(33, device="cuda")
+    d2 = torch.empty(33, device="cuda")
+    rw.softmax_stats(x, m2, d2)
+    torch.cuda.synchronize()
+    # merging into the identity leaves the window state unchanged
+    assert torch.equal(m, m2) and torch.equal(d, d2)
