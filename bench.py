@@ -60,6 +60,8 @@ def algorithmic_bytes(w, path, n_stats, op="softmax", causal=None):
     xr = valid_elements(w, causal) * w.esize
     if op == "cross_entropy":
         b = xy + 12 * w.M + 4
+    elif op == "stats":
+        b = xy + 12 * w.M
     else:
         reads = 1 if path == "resident" else 2
         b = reads * xr + xy + 4 * w.M * n_stats
@@ -85,10 +87,11 @@ def measure(w, steps, warmup, path="auto", rotate=True, graph=False,
     else:
         x0 = torch.from_numpy(x_host.view(np.int16)).view(tdt).cuda()
     ce = op == "cross_entropy"
-    per_set = (1 if ce else 2) * w.M * w.N * w.esize
+    one_read = op in ("cross_entropy", "stats")
+    per_set = (1 if one_read else 2) * w.M * w.N * w.esize
     R = max(2, -(-ROTATE_BYTES // per_set)) if rotate else 1
     xs = [x0] + [x0.clone() for _ in range(R - 1)]
-    ys = [None if ce else torch.empty_like(x0) for _ in range(R)]
+    ys = [None if one_read else torch.empty_like(x0) for _ in range(R)]
     want = set(w.outputs)
     stat = lambda k: torch.empty(w.M, device="cuda") if k in want else None
     m, d, lse = stat("m"), stat("d"), stat("lse")
@@ -100,7 +103,15 @@ def measure(w, steps, warmup, path="auto", rotate=True, graph=False,
         loss = torch.empty(w.M, device="cuda")
         mean = torch.empty(1, device="cuda")
 
+    if op == "stats":
+        m = torch.empty(w.M, device="cuda")
+        d = torch.empty(w.M, device="cuda")
+        lse = torch.empty(w.M, device="cuda")
+
     def prepared():
+        if op == "stats":
+            return [rw.prepare_stats(xs[i], m, d, lse, ws=ws, path=path)
+                    for i in range(R)]
         if ce:
             return [rw.prepare_cross_entropy(xs[i], labels, loss, mean=mean,
                                              ws=ws, path=path)
@@ -185,6 +196,10 @@ def cpu_baseline(w, n_stats, budget_s, op="softmax", causal=None):
         fn = lambda: oracle.cross_entropy(x, labels)
         what = "cross-entropy (loss, mean)"
         b = w.M * w.N * w.esize + 12 * w.M + 4
+    elif op == "stats":
+        fn = lambda: oracle.softmax(x, want_y=False)
+        what = "row statistics (m, d, lse)"
+        b = w.M * w.N * w.esize + 12 * w.M
     elif causal is not None:
         fn = lambda: oracle.softmax_masked(x, None, causal)
         what = f"causal (offset {causal}) softmax and log-softmax"
@@ -234,6 +249,8 @@ def run_workload(name, steps, warmup, path="auto", want_cpu=True,
     n_stats = len(set(w.outputs) & {"m", "d", "lse"})
     if op == "cross_entropy":
         n_stats = 0
+    if op == "stats":
+        n_stats = 3
     if causal is not None and op == "cross_entropy":
         raise ValueError("the causal mask applies to softmax / log-softmax")
     ms, R, host_us = measure(w, steps, warmup, path, op=op, causal=causal)
@@ -246,7 +263,8 @@ def run_workload(name, steps, warmup, path="auto", want_cpu=True,
     gbs = nbytes / (ms * 1e-3) / 1e9
     eff = (2 * w.M * w.N * w.esize + 4 * w.M * n_stats) / (ms * 1e-3) / 1e9
     opname = {"softmax": "softmax", "log_softmax": "log-softmax",
-              "cross_entropy": "cross-entropy"}[op]
+              "cross_entropy": "cross-entropy",
+              "stats": "row statistics (m, d, lse)"}[op]
     if causal is not None:
         opname = f"causal (offset {causal}) {opname}"
     rec = {
@@ -269,6 +287,7 @@ def run_workload(name, steps, warmup, path="auto", want_cpu=True,
         "config": {"workload": w.desc, "M": w.M, "N": w.N, "op": op,
                    "causal_offset": causal,
                    "outputs": (["loss", "mean"] if op == "cross_entropy"
+                               else ["m", "d", "lse"] if op == "stats"
                                else list(w.outputs)), "path": resolved},
         "pct_of_peak": round(100.0 * gbs / PEAK_GBS, 2),
         "rows_per_s": round(w.M / (ms * 1e-3), 1),
@@ -308,7 +327,8 @@ def main():
     ap.add_argument("--path", default="auto",
                     choices=["auto", "resident", "stream", "split"])
     ap.add_argument("--op", default="softmax",
-                    choices=["softmax", "log_softmax", "cross_entropy"])
+                    choices=["softmax", "log_softmax", "cross_entropy",
+                             "stats"])
     ap.add_argument("--causal", type=int, default=None,
                     help="causal mask offset (softmax / log-softmax)")
     ap.add_argument("--all", action="store_true",
@@ -336,7 +356,7 @@ def main():
     rw.load()
 
     if args.all:
-        for op in ["softmax", "log_softmax", "cross_entropy"]:
+        for op in ["softmax", "log_softmax", "cross_entropy", "stats"]:
             for name in ["c1", "c2", "c3", "c4", "c5"]:
                 print(f"[bench] {op} workload {name}", file=sys.stderr,
                       flush=True)

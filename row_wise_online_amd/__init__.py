@@ -22,7 +22,8 @@ from . import _lib
 from ._lib import OsError, PATHS, PATH_NAMES  # noqa: F401
 
 __all__ = ["softmax_fwd", "log_softmax_fwd", "cross_entropy_fwd",
-           "prepare_fwd", "prepare_cross_entropy", "softmax_stats",
+           "prepare_fwd", "prepare_cross_entropy", "prepare_stats",
+           "softmax_stats",
            "softmax_stats_update",
            "state_merge", "workspace_bytes", "select_path", "OsError", "load"]
 
@@ -256,6 +257,30 @@ def prepare_cross_entropy(x, labels, loss, *, lse=None, mean=None, ws=None,
         st = fn(*args)
         if st:
             _lib.check("os_cross_entropy_fwd_path", st)
+    call.tensors = keep
+    return call
+
+
+def prepare_stats(x, m, d, lse=None, *, ws=None, path="auto", stream=None):
+    """softmax_stats's counterpart of prepare_fwd (inc = 1)."""
+    lib = _lib.load()
+    dt = _dtype_code(x.dtype)
+    xp, ldx = _matrix(x, "x")
+    M, N = x.shape
+    pc = _path_code(path)
+    need = lib.os_softmax_workspace_bytes(M, N, dt, pc)
+    if need and ws is None:
+        raise ValueError(f"path needs a workspace of {need} bytes")
+    wp, wb = _workspace(ws, need, x.device)
+    args = (xp, ldx, M, N, dt, _vec(m, "m", M), _vec(d, "d", M), 1,
+            _vec(lse, "lse", M), wp, wb, pc, _stream(stream))
+    fn = lib.os_softmax_stats_path
+    keep = (x, m, d, lse, ws)
+
+    def call():
+        st = fn(*args)
+        if st:
+            _lib.check("os_softmax_stats_path", st)
     call.tensors = keep
     return call
 
