@@ -48,6 +48,14 @@ def _load():
         lib.oracle_softmax_masked.argtypes = [vp, i64, i64, i64, i32, vp, i64,
                                               dp, dp, dp, dp, dp]
         lib.oracle_softmax_masked.restype = i32
+        lib.oracle_attention.argtypes = [vp, i64, vp, i64, vp, i64, i32, i64,
+                                         i64, i64, ctypes.c_double, i64, vp,
+                                         i64, dp, dp]
+        lib.oracle_attention.restype = i32
+        lib.oracle_attention_online.argtypes = [vp, i64, vp, i64, vp, i64, i32,
+                                                i64, i64, i64, ctypes.c_double,
+                                                i64, i64, vp, i64, dp, dp]
+        lib.oracle_attention_online.restype = i32
         _lib = lib
     return _lib
 
@@ -185,6 +193,62 @@ def softmax_masked(x, row_len=None, causal=-1):
     if rc != 0:
         raise ValueError("oracle_softmax_masked rejected its arguments")
     return y, log_y, m, d, lse
+
+
+def _attn_inputs(q, k, v):
+    (q, cq), (k, ck), (v, cv) = _as_input(q), _as_input(k), _as_input(v)
+    if not (cq == ck == cv):
+        raise TypeError("q, k and v must share one dtype")
+    if k.shape != v.shape or q.shape[1] != k.shape[1]:
+        raise ValueError("q [Sq, D], k and v [Sk, D]")
+    ld = lambda a: a.strides[0] // a.itemsize
+    return q, k, v, cq, ld(q), ld(k), ld(v)
+
+
+def attention(q, k, v, scale=None, causal=-1, rows=None, online_block=None):
+    """Attention of one (batch, head) slice: q [Sq, D], k and v [Sk, D]
+    (fp32, or uint16 bf16 bits).  scale defaults to 1/sqrt(D); causal >= 0
+    admits key j for query i when j <= i + causal.  rows: the query rows to
+    evaluate (default all).  online_block: evaluate by the tiled online
+    recurrence with key blocks of that size instead of the definition.
+    Returns (o fp64 [nrows, D], lse fp64 [nrows])."""
+    q, k, v, code, ldq, ldk, ldv = _attn_inputs(q, k, v)
+    Sq, D = q.shape
+    Sk = k.shape[0]
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    r = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    n = Sq if r is None else r.shape[0]
+    o = np.empty((n, D), np.float64)
+    lse = np.empty(n, np.float64)
+    lib = _load()
+    if online_block is None:
+        rc = lib.oracle_attention(_ptr(q), ldq, _ptr(k), ldk, _ptr(v), ldv,
+                                  code, Sq, Sk, D, float(scale), int(causal),
+                                  _ptr(r), n, _ptr(o), _ptr(lse))
+    else:
+        rc = lib.oracle_attention_online(_ptr(q), ldq, _ptr(k), ldk, _ptr(v),
+                                         ldv, code, Sq, Sk, D, float(scale),
+                                         int(causal), int(online_block),
+                                         _ptr(r), n, _ptr(o), _ptr(lse))
+    if rc != 0:
+        raise ValueError("oracle_attention rejected its arguments")
+    return o, lse
+
+
+def attention_bhsd(q, k, v, scale=None, causal=-1, rows=None):
+    """attention() for every (batch, head) of q [B, H, Sq, D] and
+    k, v [B, H, Sk, D] (any layout whose last axis is contiguous).
+    Returns (o fp64 [B, H, nrows, D], lse fp64 [B, H, nrows])."""
+    B, H = q.shape[:2]
+    n = q.shape[2] if rows is None else len(rows)
+    o = np.empty((B, H, n, q.shape[3]), np.float64)
+    lse = np.empty((B, H, n), np.float64)
+    for b in range(B):
+        for h in range(H):
+            o[b, h], lse[b, h] = attention(q[b, h], k[b, h], v[b, h], scale,
+                                           causal, rows)
+    return o, lse
 
 
 # ---------------------------------------------------------------------------

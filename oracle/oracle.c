@@ -27,7 +27,11 @@
  *       cross-entropy loss and the hand-worked loss example).
  *  [P5] "FlashAttention：为什么加速推理的同时还能节省显存": the 3-pass
  *       safe_softmax and the 2-pass online_safe_softmax listings (used as a
- *       description of what is computed, not copied).
+ *       description of what is computed, not copied); the attention
+ *       o = softmax(q K^T / sqrt(d)) V per query and its tiled online form.
+ *  [P1] §8.2 and [P3] FlashAttention section: attention with the running
+ *       (m, l, o~) state per query, o~ rescaled by e^(m_old - m_new) when a
+ *       key block raises the max; [P4] §7 the same loop per query tile.
  *
  * Readings where the pages are silent (each also listed in the design notes):
  *  - An element equal to -inf has weight e^(-inf) = 0; it changes neither
@@ -46,6 +50,7 @@
 #include <math.h>
 #include <stddef.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include "oracle.h"
@@ -304,5 +309,151 @@ int oracle_softmax_masked(const void *x, int64_t ld, int64_t M, int64_t N,
         if (d_out) d_out[i] = d;
         if (lse_out) lse_out[i] = lse;
     }
+    return ORACLE_OK;
+}
+
+/* ---- attention ------------------------------------------------------------
+ * [P1] §8.2, [P3] FlashAttention section and worked attention example,
+ * [P4] §7, [P5] attention listings: for query row i of one (batch, head)
+ * slice, the scores against the admitted keys are s_j = scale * (q_i . k_j),
+ * P = softmax(s) (three-pass safe form), o_i = sum_j P_j v_j, and
+ * lse_i = m + log sum_j e^(s_j - m).  The pages use scale = 1/sqrt(d).
+ *
+ * Readings: key j is admitted for query i when j < Sk and, if causal >= 0,
+ * j <= i + causal (a causal offset of Sk - Sq aligns the last query with the
+ * last key; 0 is the square self-attention mask).  With causal >= 0 and
+ * Sk >= 1 every query admits key 0, so no row is empty.  Non-finite scores
+ * follow the softmax readings above (a NaN or +inf score gives a NaN row).
+ *
+ * rows (nullable): the query rows to evaluate, nrows of them, in that order
+ * (all Sq rows when NULL, nrows ignored).  o: fp64 [nrows][D]; lse
+ * (nullable): fp64 [nrows].  Q, K, V rows have strides ldq, ldk, ldv. */
+static int attn_args(const void *q, int64_t ldq, const void *k, int64_t ldk,
+                     const void *v, int64_t ldv, int dtype, int64_t Sq,
+                     int64_t Sk, int64_t D, const int64_t *rows,
+                     int64_t nrows)
+{
+    if (Sq < 0 || Sk < 1 || D < 1) return ORACLE_EINVAL;
+    if (ldq < D || ldk < D || ldv < D) return ORACLE_EINVAL;
+    if (dtype != ORACLE_F32 && dtype != ORACLE_BF16) return ORACLE_EINVAL;
+    if (!q || !k || !v) return ORACLE_EINVAL;
+    if (rows) {
+        for (int64_t r = 0; r < nrows; ++r)
+            if (rows[r] < 0 || rows[r] >= Sq) return ORACLE_EINVAL;
+    }
+    return ORACLE_OK;
+}
+
+static int64_t admitted_keys(int64_t i, int64_t Sk, int64_t causal)
+{
+    if (causal < 0) return Sk;
+    const int64_t last = i + causal;            /* the last admitted key */
+    return (last + 1 < Sk) ? last + 1 : Sk;
+}
+
+/* s_j = scale * sum_c q_ic k_jc, the dot product summed in index order. */
+static double attn_score(const void *q, int64_t ldq, const void *k,
+                         int64_t ldk, int dtype, int64_t i, int64_t j,
+                         int64_t D, double scale)
+{
+    double dot = 0.0;
+    for (int64_t c = 0; c < D; ++c)
+        dot = dot + load_elem(q, dtype, i * ldq + c) *
+                    load_elem(k, dtype, j * ldk + c);
+    return scale * dot;
+}
+
+int oracle_attention(const void *q, int64_t ldq, const void *k, int64_t ldk,
+                     const void *v, int64_t ldv, int dtype, int64_t Sq,
+                     int64_t Sk, int64_t D, double scale, int64_t causal,
+                     const int64_t *rows, int64_t nrows, double *o,
+                     double *lse)
+{
+    int rc = attn_args(q, ldq, k, ldk, v, ldv, dtype, Sq, Sk, D, rows, nrows);
+    if (rc != ORACLE_OK) return rc;
+    if (!rows) nrows = Sq;
+    if (nrows > 0 && !o) return ORACLE_EINVAL;
+    double *s = (double *)malloc((size_t)Sk * sizeof(double));
+    if (!s) return ORACLE_EINVAL;
+    for (int64_t r = 0; r < nrows; ++r) {
+        const int64_t i = rows ? rows[r] : r;
+        const int64_t n = admitted_keys(i, Sk, causal);
+        /* pass 1: the scores and their max */
+        double m = -INFINITY;
+        for (int64_t j = 0; j < n; ++j) {
+            s[j] = attn_score(q, ldq, k, ldk, dtype, i, j, D, scale);
+            if (s[j] > m) m = s[j];
+        }
+        /* pass 2: the normaliser */
+        double l = 0.0;
+        for (int64_t j = 0; j < n; ++j) {
+            double t = (s[j] == -INFINITY) ? 0.0 : exp(s[j] - m);
+            l = l + t;
+        }
+        /* pass 3: the probabilities, then the weighted sum of value rows */
+        for (int64_t c = 0; c < D; ++c) o[r * D + c] = 0.0;
+        for (int64_t j = 0; j < n; ++j) {
+            double t = (s[j] == -INFINITY) ? 0.0 : exp(s[j] - m);
+            double p = t / l;
+            for (int64_t c = 0; c < D; ++c)
+                o[r * D + c] = o[r * D + c] + p * load_elem(v, dtype, j * ldv + c);
+        }
+        if (lse) lse[r] = m + log(l);
+    }
+    free(s);
+    return ORACLE_OK;
+}
+
+/* The tiled online form of the same attention, per query row ([P3] the
+ * recurrence for m, l and the unnormalised output; [P4] §7 loop over K/V
+ * tiles): keys are taken in blocks of Bc; a block with maximum m_blk moves
+ * the running max to m_new = max(m, m_blk), the old l and o~ are scaled by
+ * alpha = e^(m - m_new), the block adds sum e^(s_j - m_new) to l and
+ * sum e^(s_j - m_new) v_j to o~, and o = o~ / l at the end.  The pages state
+ * this equals the definition up to rounding; the pins check it. */
+int oracle_attention_online(const void *q, int64_t ldq, const void *k,
+                            int64_t ldk, const void *v, int64_t ldv, int dtype,
+                            int64_t Sq, int64_t Sk, int64_t D, double scale,
+                            int64_t causal, int64_t Bc, const int64_t *rows,
+                            int64_t nrows, double *o, double *lse)
+{
+    int rc = attn_args(q, ldq, k, ldk, v, ldv, dtype, Sq, Sk, D, rows, nrows);
+    if (rc != ORACLE_OK) return rc;
+    if (Bc < 1) return ORACLE_EINVAL;
+    if (!rows) nrows = Sq;
+    if (nrows > 0 && !o) return ORACLE_EINVAL;
+    double *s = (double *)malloc((size_t)Bc * sizeof(double));
+    double *acc = (double *)malloc((size_t)D * sizeof(double));
+    if (!s || !acc) { free(s); free(acc); return ORACLE_EINVAL; }
+    for (int64_t r = 0; r < nrows; ++r) {
+        const int64_t i = rows ? rows[r] : r;
+        const int64_t n = admitted_keys(i, Sk, causal);
+        double m = -INFINITY, l = 0.0;
+        for (int64_t c = 0; c < D; ++c) acc[c] = 0.0;
+        for (int64_t j0 = 0; j0 < n; j0 += Bc) {
+            const int64_t nb = (n - j0 < Bc) ? n - j0 : Bc;
+            double m_blk = -INFINITY;
+            for (int64_t t = 0; t < nb; ++t) {
+                s[t] = attn_score(q, ldq, k, ldk, dtype, i, j0 + t, D, scale);
+                if (s[t] > m_blk) m_blk = s[t];
+            }
+            const double m_new = (m_blk > m) ? m_blk : m;
+            if (m_new == -INFINITY) continue;          /* nothing admitted yet */
+            const double alpha = (m == -INFINITY) ? 0.0 : exp(m - m_new);
+            l = alpha * l;
+            for (int64_t c = 0; c < D; ++c) acc[c] = alpha * acc[c];
+            for (int64_t t = 0; t < nb; ++t) {
+                double e = (s[t] == -INFINITY) ? 0.0 : exp(s[t] - m_new);
+                l = l + e;
+                for (int64_t c = 0; c < D; ++c)
+                    acc[c] = acc[c] + e * load_elem(v, dtype, (j0 + t) * ldv + c);
+            }
+            m = m_new;
+        }
+        for (int64_t c = 0; c < D; ++c) o[r * D + c] = acc[c] / l;
+        if (lse) lse[r] = m + log(l);
+    }
+    free(s);
+    free(acc);
     return ORACLE_OK;
 }

@@ -50,6 +50,22 @@ int oracle_softmax_masked(const void *x, int64_t ld, int64_t M, int64_t N,
                           double *y, double *log_y, double *m, double *d,
                           double *lse);
 
+/* Attention of one (batch, head) slice: o = softmax(scale q K^T) V and
+ * lse per selected query row (rows nullable = all Sq rows); causal >= 0
+ * admits key j for query i when j <= i + causal. */
+int oracle_attention(const void *q, int64_t ldq, const void *k, int64_t ldk,
+                     const void *v, int64_t ldv, int dtype, int64_t Sq,
+                     int64_t Sk, int64_t D, double scale, int64_t causal,
+                     const int64_t *rows, int64_t nrows, double *o,
+                     double *lse);
+
+/* The same by the tiled online recurrence over key blocks of Bc. */
+int oracle_attention_online(const void *q, int64_t ldq, const void *k,
+                            int64_t ldk, const void *v, int64_t ldv, int dtype,
+                            int64_t Sq, int64_t Sk, int64_t D, double scale,
+                            int64_t causal, int64_t Bc, const int64_t *rows,
+                            int64_t nrows, double *o, double *lse);
+
 #ifdef __cplusplus
 }
 #endif

@@ -21,6 +21,21 @@ c3     32768 x 1024 bf16   2 N(0,1)
 c4     1024 x 32768 fp32   0.01 j + 0.1 N(0,1)  (ascending in j)
 c5     16 x 4194304 fp32   N(0,1), then x[i, c_i] = 20 for a seeded c_i
 =====  ===========  =====  ============================================
+
+Attention inputs (the online softmax inside key tiles): Q, K and V are
+drawn in that order, each [B, H, S, D] in row-major order, as
+``q_scale`` N(0,1) for Q and N(0,1) for K and V, rounded to bf16 as above.
+With the default scale 1/sqrt(D) the scores are then about N(0, q_scale^2).
+The named attention workloads:
+
+=====  ===============================  ======  =======================
+name   B x H x Sq x Sk x D              causal  values
+=====  ===============================  ======  =======================
+a1     2 x 3 x 300 x 333 x 128          no      N(0,1)
+a2     1 x 1 x 131072 x 131072 x 128    no      N(0,1)
+a3     1 x 1 x 131072 x 131072 x 128    0       N(0,1)
+a4     1 x 1 x 131072 x 131072 x 64     no      N(0,1)
+=====  ===============================  ======  =======================
 """
 from dataclasses import dataclass, field
 
@@ -139,3 +154,63 @@ def from_values(v, dtype="f32", ld=None):
     if v.ndim == 1:
         v = v[None, :]
     return _store(v, dtype, ld)
+
+
+@dataclass(frozen=True)
+class AttnWorkload:
+    name: str
+    B: int
+    H: int
+    Sq: int
+    Sk: int
+    D: int
+    causal: int           # -1: none; >= 0: key j admitted when j <= i + causal
+    seed: int
+    desc: str = ""
+
+    def flops(self) -> float:
+        """2 Sq Sk D multiply-adds for each of Q K^T and P V, per head; a
+        causal mask with offset c admits sum_i min(Sk, i + c + 1) keys."""
+        if self.causal < 0:
+            pairs = self.Sq * self.Sk
+        else:
+            i = np.arange(self.Sq, dtype=np.int64)
+            pairs = int(np.minimum(self.Sk, i + self.causal + 1).sum())
+        return 4.0 * self.B * self.H * pairs * self.D
+
+
+ATTN_WORKLOADS = {
+    "a1": AttnWorkload("a1", 2, 3, 300, 333, 128, -1, 2001,
+                       "bf16 2x3 heads, 300 queries x 333 keys, d=128"),
+    "a2": AttnWorkload("a2", 1, 1, 131072, 131072, 128, -1, 2002,
+                       "bf16 one head, 131072 queries x 131072 keys, d=128"),
+    "a3": AttnWorkload("a3", 1, 1, 131072, 131072, 128, 0, 2003,
+                       "bf16 one head, 131072^2, d=128, causal"),
+    "a4": AttnWorkload("a4", 1, 1, 131072, 131072, 64, -1, 2004,
+                       "bf16 one head, 131072^2, d=64"),
+}
+
+
+def attention_inputs(B, H, Sq, Sk, D, *, seed=0, q_scale=1.0, layout="bhsd"):
+    """Seeded bf16 Q [B,H,Sq,D], K and V [B,H,Sk,D] (uint16 bit arrays).
+
+    layout "bhsd" stores each tensor densely in that order; "bshd" stores
+    it as [B,S,H,D] and returns the [B,H,S,D] view (same values)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for S, sc in ((Sq, q_scale), (Sk, 1.0), (Sk, 1.0)):
+        v = sc * rng.standard_normal((B, H, S, D))
+        bits = f32_to_bf16_bits(v.astype(np.float32))
+        if layout == "bshd":
+            buf = np.ascontiguousarray(bits.transpose(0, 2, 1, 3))
+            bits = buf.transpose(0, 2, 1, 3)
+        elif layout != "bhsd":
+            raise ValueError(layout)
+        out.append(bits)
+    return tuple(out)
+
+
+def attention_workload(name: str):
+    """(q, k, v) of a named attention workload."""
+    w = ATTN_WORKLOADS[name]
+    return attention_inputs(w.B, w.H, w.Sq, w.Sk, w.D, seed=w.seed)

@@ -44,7 +44,28 @@ MUTATIONS = {
     "causal offset off by one":
         ("if (causal >= 0 && i + causal + 1 < n) n = i + causal + 1;",
          "if (causal >= 0 && i + causal < n) n = i + causal;"),
+    "attention scale dropped":
+        ("    return scale * dot;", "    return dot;"),
+    "attention key row stride replaced by the query's":
+        ("load_elem(k, dtype, j * ldk + c);", "load_elem(k, dtype, j * ldq + c);"),
+    "attention probabilities not normalised":
+        ("double p = t / l;", "double p = t;"),
+    "attention value rows reversed":
+        ("p * load_elem(v, dtype, j * ldv + c);",
+         "p * load_elem(v, dtype, (n - 1 - j) * ldv + c);"),
+    "attention causal mask off by one":
+        ("return (last + 1 < Sk) ? last + 1 : Sk;",
+         "return (last < Sk) ? last : Sk;"),
+    "attention lse without max":
+        ("if (lse) lse[r] = m + log(l);", "if (lse) lse[r] = log(l);"),
+    "online output rescale dropped":
+        ("for (int64_t c = 0; c < D; ++c) acc[c] = alpha * acc[c];",
+         "for (int64_t c = 0; c < D; ++c) acc[c] = acc[c];"),
+    "online normaliser rescale dropped":
+        ("            l = alpha * l;", "            l = l;"),
 }
+
+PIN_FILES = ("test_oracle.py", "test_oracle_attention.py")
 
 
 @pytest.mark.parametrize("name", sorted(MUTATIONS))
@@ -62,8 +83,8 @@ def test_pins_catch_planted_mistake(name, tmp_path):
                    check=True)
     env = dict(os.environ, ORACLE_LIB=str(lib))
     r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x",
-                        "-p", "no:cacheprovider",
-                        os.path.join(ROOT, "tests", "test_oracle.py")],
+                        "-p", "no:cacheprovider"] +
+                       [os.path.join(ROOT, "tests", f) for f in PIN_FILES],
                        cwd=ROOT, env=env, capture_output=True, text=True,
                        timeout=600)
     assert r.returncode != 0, f"pins did not catch: {name}\n{r.stdout[-2000:]}"
