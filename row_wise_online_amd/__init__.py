@@ -17,7 +17,12 @@ Same names as the C ABI, without the ``os_`` prefix:
 * ``softmax_stats_update(x, m, d, lse=None, inc=1, ws=None, path="auto")``
 * ``state_merge(m_in, d_in, m_out, d_out, lse_out=None)``
 * ``workspace_bytes(M, N, dtype, path="auto")``, ``select_path(M, N, dtype)``
+* ``attention_fwd(q, k, v, o=None, lse=None, scale=None, causal_offset=-1)``
+  (``include/os_attention.h``), and ``prepare_attention`` for launch loops
 """
+import ctypes
+import math
+
 from . import _lib
 from ._lib import OsError, PATHS, PATH_NAMES  # noqa: F401
 
@@ -25,7 +30,8 @@ __all__ = ["softmax_fwd", "log_softmax_fwd", "cross_entropy_fwd",
            "prepare_fwd", "prepare_cross_entropy", "prepare_stats",
            "softmax_stats",
            "softmax_stats_update",
-           "state_merge", "workspace_bytes", "select_path", "OsError", "load"]
+           "state_merge", "workspace_bytes", "select_path", "OsError", "load",
+           "attention_fwd", "prepare_attention"]
 
 
 def load():
@@ -336,3 +342,71 @@ def state_merge(m_in, d_in, m_out, d_out, lse_out=None, *, stream=None):
                             _vec(d_out, "d_out", M),
                             _vec(lse_out, "lse_out", M), _stream(stream))
     _lib.check("os_state_merge", st)
+
+
+def _bhsd(t, name):
+    """Pointer and (batch, head, row) element strides of a [B, H, S, D] GPU
+    tensor whose last axis is contiguous."""
+    if t.dim() != 4 or t.stride(3) != 1:
+        raise ValueError(f"{name} must be [B, H, S, D] with a contiguous last axis")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    return t.data_ptr(), (ctypes.c_int64 * 3)(t.stride(0), t.stride(1),
+                                              t.stride(2))
+
+
+def prepare_attention(q, k, v, o, *, lse=None, scale=None, causal_offset=-1,
+                      stream=None):
+    """Marshal one os_attention_fwd call (q, k, v bf16 [B, H, S, D]; o bf16
+    or fp32 of q's shape; lse fp32 [B, H, Sq] dense or None) and return a
+    function that repeats it on the same tensors and stream."""
+    torch = _torch()
+    lib = _lib.load()
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        if t.dtype != torch.bfloat16:
+            raise TypeError(f"{n} must be bfloat16")
+    B, H, Sq, D = q.shape
+    Sk = k.shape[2]
+    if k.shape != (B, H, Sk, D) or v.shape != k.shape:
+        raise ValueError("k and v must be [B, H, Sk, D] matching q")
+    if o.shape != q.shape:
+        raise ValueError("o must have q's shape")
+    od = _dtype_code(o.dtype)
+    ptrs = [_bhsd(t, n) for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"))]
+    lp = None
+    if lse is not None:
+        if (lse.dtype != torch.float32 or not lse.is_cuda
+                or lse.shape != (B, H, Sq) or not lse.is_contiguous()):
+            raise ValueError("lse must be a dense float32 GPU tensor [B, H, Sq]")
+        lp = lse.data_ptr()
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    args = (ptrs[0][0], ptrs[1][0], ptrs[2][0], ptrs[3][0], lp, B, H, Sq, Sk,
+            D, ptrs[0][1], ptrs[1][1], ptrs[2][1], ptrs[3][1], od,
+            float(scale), int(causal_offset), _stream(stream))
+    fn = lib.os_attention_fwd
+    keep = (q, k, v, o, lse, ptrs)
+
+    def call():
+        st = fn(*args)
+        if st:
+            _lib.check("os_attention_fwd", st)
+    call.tensors = keep
+    return call
+
+
+def attention_fwd(q, k, v, o=None, *, lse=None, scale=None, causal_offset=-1,
+                  out_dtype=None, stream=None):
+    """o = softmax(scale q k^T) v per (batch, head), with the online softmax
+    inside key tiles (os_attention_fwd).  q, k, v: bf16 [B, H, S, D] GPU
+    tensors with a contiguous last axis (any other strides); scale defaults
+    to 1/sqrt(D); causal_offset >= 0 admits key j for query i when
+    j <= i + causal_offset.  Returns o (allocated as out_dtype, default
+    bf16, when not given)."""
+    torch = _torch()
+    if o is None:
+        o = torch.empty(q.shape, dtype=out_dtype or torch.bfloat16,
+                        device=q.device)
+    prepare_attention(q, k, v, o, lse=lse, scale=scale,
+                      causal_offset=causal_offset, stream=stream)()
+    return o

@@ -1,4 +1,5 @@
-"""ctypes view of the C ABI in ``include/os_softmax.h``.
+"""ctypes view of the C ABI in ``include/os_softmax.h`` and
+``include/os_attention.h``.
 
 Argument marshalling only: this module loads ``libos_softmax.so`` (built by
 ``row_wise_online_amd/build.py``) and declares each exported function's
@@ -60,6 +61,9 @@ SIGNATURES = {
     "os_softmax_workspace_bytes": (_sz, [_i64, _i64, _i32, _i32]),
     "os_softmax_select_path": (_i32, [_i64, _i64, _i32]),
     "os_status_string": (ctypes.c_char_p, [_i32]),
+    "os_attention_fwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64,
+                                _i64, _i64, _vp, _vp, _vp, _vp, _i32,
+                                ctypes.c_float, _i64, _vp]),
 }
 
 _lib = None

@@ -209,3 +209,41 @@ def test_stats_update_validation(lib):
     assert f(M=-1) == 2 and f(N=0) == 2 and f(inc=0) == 3 and f(ldx=2) == 3
     assert f(m=NUL) == 1 and f(d=NUL) == 1 and f(x=NUL) == 1 and f(path=6) == 6
     assert f(x=NUL, m=NUL, d=NUL, M=0) == 0
+
+
+def _attn(lib, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=NUL, B=1, H=2, Sq=10,
+          Sk=12, D=64, qs=(1280, 640, 64), ks=(1536, 768, 64),
+          vs=(1536, 768, 64), os_=(1280, 640, 64), od=1, scale=0.125,
+          causal=-1):
+    arr = lambda s: None if s is None else (ctypes.c_int64 * 3)(*s)
+    return lib.os_attention_fwd(q, k, v, o, lse, B, H, Sq, Sk, D, arr(qs),
+                                arr(ks), arr(vs), arr(os_), od, scale, causal,
+                                NUL)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(D=96), 7), (dict(D=32), 7), (dict(scale=0.0), 7),
+    (dict(scale=-0.5), 7), (dict(scale=float("inf")), 7),
+    (dict(scale=float("nan")), 7), (dict(od=2), 4), (dict(od=-1), 4),
+    (dict(Sk=0), 2), (dict(Sq=-1), 2), (dict(B=-1), 2), (dict(H=-3), 2),
+    (dict(Sq=1 << 31), 2), (dict(Sk=1 << 31), 2),
+    (dict(qs=None), 1), (dict(os_=None), 1),
+    (dict(ks=(1536, -768, 64)), 3), (dict(vs=(1536, 768, 32)), 3),
+    (dict(qs=(1280, 640, 68)), 3), (dict(os_=(1280, 644, 64)), 3),
+    (dict(q=ctypes.c_void_p(0x1002)), 3), (dict(o=ctypes.c_void_p(0x1008)), 3),
+    (dict(q=NUL), 1), (dict(v=NUL), 1), (dict(o=NUL), 1),
+])
+def test_attention_validation(lib, kw, status):
+    assert _attn(lib, **kw) == status
+
+
+def test_attention_fp32_output_stride_rule(lib):
+    # an fp32 output needs 16-byte strides (multiples of 4 elements): 68 is
+    # fine for fp32 but not for bf16; the call still fails later on a NULL q
+    assert _attn(lib, q=NUL, od=0, os_=(1360, 680, 68)) == 1
+    assert _attn(lib, q=NUL, od=1, os_=(1360, 680, 68)) == 3
+
+
+def test_attention_empty_is_noop(lib):
+    for kw in (dict(B=0), dict(H=0), dict(Sq=0)):
+        assert _attn(lib, q=NUL, k=NUL, v=NUL, o=NUL, **kw) == 0
