@@ -13,6 +13,12 @@ GB/s: the bytes the path must move (x read once per read pass, y written
 once, row statistics written) divided by the step time.
 
 ``--all`` also prints one JSON line per workload to stderr.
+
+``--op attention`` (workloads a2, a3, a4) times one ``os_attention_fwd``
+call per step instead: the attention forward with the online softmax inside
+key tiles; ``value`` is then TFLOP/s (4 Sq Sk D per head for Q K^T and P V,
+over the admitted key pairs only under a causal mask), against the MI355X
+dense bf16 matrix-core peak.
 """
 import argparse
 import glob
@@ -29,6 +35,7 @@ if ROOT not in sys.path:
 METRIC = ("achieved HBM GB/s (% of peak) + rows/s, online softmax fwd fp32 "
           "4096×4096")
 PEAK_GBS = 8000.0           # MI355X HBM3E, published peak
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published peak
 ROTATE_BYTES = 1 << 30      # rotating working set, 4x the Infinity Cache
 
 
@@ -353,19 +360,145 @@ def run_workload(name, steps, warmup, path="auto", want_cpu=True,
     return rec
 
 
+def measure_attention(w, steps, warmup, graph=False):
+    """Average device time per attention step (ms) and host time per launch
+    (us) on the seeded inputs of attention workload w (bf16 output, fp32
+    lse), timed with HIP events on the launch stream."""
+    import numpy as np
+    import torch
+    import row_wise_online_amd as rw
+    from row_wise_online_amd import workloads as wl
+    dev = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    q, k, v = (dev(a) for a in wl.attention_workload(w.name))
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.Sq), dtype=torch.float32, device="cuda")
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    if not graph:
+        call = rw.prepare_attention(q, k, v, o, lse=lse,
+                                    causal_offset=w.causal)
+        for _ in range(warmup):
+            call()
+        torch.cuda.synchronize()
+        start.record()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            call()
+        host_us = (time.perf_counter() - t0) / steps * 1e6
+        end.record()
+        end.synchronize()
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / steps, host_us
+    g = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        call = rw.prepare_attention(q, k, v, o, lse=lse,
+                                    causal_offset=w.causal,
+                                    stream=torch.cuda.current_stream())
+        for _ in range(steps):
+            call()
+    g.replay()
+    torch.cuda.synchronize()
+    start.record()
+    t0 = time.perf_counter()
+    g.replay()
+    host_us = (time.perf_counter() - t0) / steps * 1e6
+    end.record()
+    end.synchronize()
+    torch.cuda.synchronize()
+    del g
+    return start.elapsed_time(end) / steps, host_us
+
+
+def cpu_baseline_attention(w, budget_s):
+    """The fp64 attention oracle, as it is, on this host: whole query rows
+    of the workload (each against all its admitted keys), one at a time,
+    until about budget_s seconds have passed."""
+    import numpy as np
+    import oracle
+    from row_wise_online_amd import workloads as wl
+    q, k, v = wl.attention_workload(w.name)
+    rng = np.random.default_rng(w.seed)
+    rows = rng.integers(0, w.Sq, size=4096)
+    flops, n, t0 = 0.0, 0, time.perf_counter()
+    while True:
+        i = int(rows[n % len(rows)])
+        oracle.attention(q[0, 0], k[0, 0], v[0, 0], causal=w.causal, rows=[i])
+        keys = w.Sk if w.causal < 0 else min(w.Sk, i + w.causal + 1)
+        flops += 4.0 * keys * w.D
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    return {"value": round(flops / el / 1e12, 8), "unit": "TFLOP/s",
+            "cores": 1, "kind": "oracle",
+            "sample": f"{n} random query rows of {w.Sq}x{w.Sk} d={w.D} "
+                      f"(head 0), fp64 definition oracle, 1 thread, "
+                      f"{el:.1f} s"}
+
+
+def run_attention(name, steps, warmup, want_cpu=True, cpu_budget=10.0,
+                  extras=True):
+    from row_wise_online_amd import workloads as wl
+    w = wl.ATTN_WORKLOADS[name]
+    ms, host_us = measure_attention(w, steps, warmup)
+    flops = w.flops()
+    tf = flops / (ms * 1e-3) / 1e12
+    rec = {
+        "metric": f"attention fwd TFLOP/s, online softmax inside key tiles, "
+                  f"bf16 {w.B}x{w.H}x{w.Sq}x{w.Sk} d={w.D}"
+                  + (" causal" if w.causal >= 0 else ""),
+        "value": round(tf, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded numpy PCG64 normals, HBM-resident)",
+        "config": {"workload": w.desc, "B": w.B, "H": w.H, "Sq": w.Sq,
+                   "Sk": w.Sk, "D": w.D, "causal_offset": w.causal,
+                   "outputs": ["o (bf16)", "lse (fp32)"], "op": "attention"},
+        "host_us_per_launch": round(host_us, 2),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(tf, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic_record(name),
+            "algorithmic_flops_per_launch": flops,
+            "kernel_launches_per_step": 1,
+        },
+        "kernel_source": kernel_source_hash(),
+    }
+    if extras:
+        gms, _ = measure_attention(w, steps, 1, graph=True)
+        rec["graph_replay_TFLOPs"] = round(flops / (gms * 1e-3) / 1e12, 2)
+    if want_cpu:
+        rec["cpu_baseline"] = cpu_baseline_attention(w, cpu_budget)
+    return rec
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default 1000; 20 for attention)")
     # the clocks take ~10 ms of sustained launches to settle after setup
-    ap.add_argument("--warmup", type=int, default=2000)
-    ap.add_argument("--workload", default="c2",
-                    choices=["c1", "c2", "c3", "c4", "c5"])
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed steps (default 2000; 3 for attention)")
+    ap.add_argument("--workload", default=None,
+                    choices=["c1", "c2", "c3", "c4", "c5", "a2", "a3", "a4"],
+                    help="default c2 (a2 for --op attention)")
     ap.add_argument("--path", default="auto",
                     choices=["auto", "resident", "stream", "split"])
     ap.add_argument("--op", default="softmax",
                     choices=["softmax", "log_softmax", "cross_entropy",
-                             "stats"])
+                             "stats", "attention"])
     ap.add_argument("--causal", type=int, default=None,
                     help="causal mask offset (softmax / log-softmax)")
     ap.add_argument("--all", action="store_true",
@@ -384,6 +517,18 @@ def main():
               "communication, see the design notes); use --gpus 1",
               file=sys.stderr)
         sys.exit(2)
+
+    att = args.op == "attention"
+    if args.workload is None:
+        args.workload = "a2" if att else "c2"
+    if att != args.workload.startswith("a"):
+        print("--op attention takes workloads a2, a3, a4; the row-wise ops "
+              "c1..c5", file=sys.stderr)
+        sys.exit(2)
+    if args.steps is None:
+        args.steps = 20 if att else 1000
+    if args.warmup is None:
+        args.warmup = 3 if att else 2000
 
     import torch
     import row_wise_online_amd as rw
@@ -408,8 +553,22 @@ def main():
                              want_cpu=False, extras=not args.no_extras,
                              causal=0)
             print(json.dumps(r), file=sys.stderr, flush=True)
+        if not att:
+            for name in ["a2", "a3", "a4"]:
+                print(f"[bench] attention workload {name}", file=sys.stderr,
+                      flush=True)
+                r = run_attention(name, 20, 3, want_cpu=False,
+                                  extras=not args.no_extras)
+                print(json.dumps(r), file=sys.stderr, flush=True)
     print(f"[bench] headline workload {args.workload}", file=sys.stderr,
           flush=True)
+    if att:
+        rec = run_attention(args.workload, args.steps, args.warmup,
+                            want_cpu=not args.no_cpu,
+                            cpu_budget=args.cpu_budget,
+                            extras=not args.no_extras)
+        print(json.dumps(rec), flush=True)
+        return
     rec = run_workload(args.workload, args.steps, args.warmup, args.path,
                        want_cpu=not args.no_cpu, cpu_budget=args.cpu_budget,
                        extras=not args.no_extras, op=args.op,
