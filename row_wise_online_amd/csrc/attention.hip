@@ -6,9 +6,11 @@
 // 与 IO-Aware Attention" §7: the loop over K/V tiles).
 //
 // Work split.  One workgroup = 4 waves = 128 query rows of one (batch,
-// head); each wave owns 32 rows.  K and V tiles of 64 keys are staged in LDS
-// (double-buffered, one barrier per tile; the next tile's global loads are
-// issued before the current tile's math).
+// head); each wave owns 32 rows.  K and V tiles of 64 keys stream through
+// LDS rings of two tiles each, filled by direct-to-LDS buffer loads
+// (buffer_load_dwordx4 ... lds): no VGPR staging, and lanes past the last
+// key read as zero because each tile's buffer descriptor covers only the
+// keys that exist.  One barrier per tile.
 //
 // Products on v_mfma_f32_32x32x16_bf16 (lane l: operand row/column l % 32,
 // k = 8 (l / 32) + j for j < 8; result register r: row 8 (r / 4) +
@@ -27,9 +29,21 @@
 //                 V^T slice, gathered from the row-major V tile by two
 //                 ds_read_b64_tr_b16 (LDS transpose reads) per operand.
 //
-// The softmax runs in base 2: t = s * c with c = scale * log2(e), the
-// running max m2 is kept in the same units, p = 2^(s c - m2), and
-// lse = (m2 + log2 l) ln 2.
+// Software pipeline.  While the exponentials of tile j run on the VALU, the
+// matrix cores compute the scores of tile j + 1; the P.V products of tile j
+// then overlap the second half of tile j's exponentials and tile j + 1's row
+// max.  sched_group_barrier fixes the interleaving of each phase.
+//
+// Online state in base 2: t = s c with c = scale log2(e); the reference
+// point m2 of each row moves only when a tile's max exceeds it by more than
+// kTau (a lazy rescale: every p = 2^(t - m2) stays below 2^kTau, and the
+// result does not depend on which reference point is used, since o and l
+// are both taken relative to it); lse = (m2 + log2 l) ln 2.
+//
+// LDS layouts (rows of 2D bytes, no padding): 16-byte chunk c of row r of a
+// K tile sits in slot c ^ fk(r), of a V tile in slot c ^ fv(r).  With these
+// XOR swizzles the 64 lanes of a K operand read (32 rows x 32 bytes) and of
+// a V^T transpose read (8 rows x 64 bytes) spread evenly over the banks.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -46,7 +60,9 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
 typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kWaves = 4;
 constexpr int kRowsPerWave = 32;
@@ -54,20 +70,25 @@ constexpr int kBlockM = kWaves * kRowsPerWave;   // query rows per workgroup
 constexpr int kBlockN = 64;                      // keys per tile
 constexpr int kThreads = kWaves * kWave;
 constexpr float kLn2 = 0.69314718055994531f;
+constexpr float kTau = 8.0f;                     // lazy-rescale threshold (log2 units)
+// Buffer descriptor word 3 for raw (unswizzled, stride 0) dword buffers.
+constexpr int kRsrcWord3 = 0x00020000;
+// Row strides (elements) below this keep a tile's byte offsets in 32 bits.
+constexpr int64_t kMaxRowStride = int64_t(1) << 23;
 
-// LDS tile geometry (elements).  Row pitches are padded so that the MFMA
-// operand reads spread over all banks: K rows by 32 bytes (a 32-row
-// ds_read_b128 touches 8 distinct 32-byte bank groups), V rows by 64 bytes
-// (the 8 rows of a transpose read fall on 4 distinct 64-byte groups).
 template <int D>
 struct Geo {
-    static constexpr int KP = D + 16;
-    static constexpr int VP = D + 32;
-    static constexpr int KT = kBlockN * KP;
-    static constexpr int VT = kBlockN * VP;
-    static constexpr int kChunksPerRow = D / 8;                      // 16 B each
-    static constexpr int kChunks = kBlockN * kChunksPerRow / kThreads;  // per thread
-    static constexpr int kLdsElems = 2 * (KT + VT);
+    static constexpr int RB = 2 * D;                    // bytes per row
+    static constexpr int TILE = kBlockN * RB;           // bytes per K or V tile
+    static constexpr int CPR = D / 8;                   // 16-byte chunks per row
+    static constexpr int RPB = 1024 / RB;               // rows per 1 KB wave load
+    static constexpr int NDMA = TILE / 1024 / kWaves;   // wave loads per tile
+    static constexpr int kLdsBytes = 4 * TILE;          // K ring (2) + V ring (2)
+    static constexpr int KRING = 0, VRING = 2 * TILE;
+    __device__ static int fk(int r) { return D == 128 ? (r & 7) : ((r >> 1) & 7); }
+    __device__ static int fv(int r) {
+        return D == 128 ? 4 * ((r >> 1) & 3) : 4 * ((r >> 1) & 1);
+    }
 };
 
 struct Params {
@@ -76,7 +97,7 @@ struct Params {
     float *lse;
     int64_t qs[3], ks[3], vs[3], os[3];
     int H, BH, Sq, Sk, nqb;
-    int causal;      // < 0: no mask; else key j admitted for query i if j <= i + causal
+    int causal;      // key j admitted for query i if j <= i + causal (CAUSAL only)
     float c;         // scale * log2(e)
 };
 
@@ -96,40 +117,321 @@ __device__ __forceinline__ bf16x8 as_bf16x8(const uint4 &u) {
     return __builtin_bit_cast(bf16x8, u);
 }
 
-template <int D>
-struct Tile {
-    uint4 k[Geo<D>::kChunks], v[Geo<D>::kChunks];
+__device__ __forceinline__ bf16x8 cvt8(const f32x16 &s, int r0) {
+    f32x8 x = {s[r0 + 0], s[r0 + 1], s[r0 + 2], s[r0 + 3],
+               s[r0 + 4], s[r0 + 5], s[r0 + 6], s[r0 + 7]};
+    return __builtin_convertvector(x, bf16x8);
+}
 
-    // Global -> registers for keys [k0, k0 + 64): rows past Sk read as zero
-    // (never from memory), so they add nothing to P.V.
-    __device__ __forceinline__ void load(const uint16_t *kh, int64_t kss,
-                                         const uint16_t *vh, int64_t vss,
-                                         int k0, int Sk, int tid) {
+// Direct-to-LDS load of one 64-key tile (K or V) of one head: wave w writes
+// 1 KB blocks w, w + 4, ...; lane l's 16 bytes land at block + 16 l.  Block
+// i of the wave holds rows 4 i RPB (>= 16) further down than block 0 and
+// the swizzle of a row depends only on its low four bits, which that step
+// leaves alone, so one per-lane offset (row and chunk within block 0) plus
+// a uniform offset per block addresses every load.  Keys at or past
+// Sk lie outside the descriptor and arrive as zeros.
+template <int D>
+__device__ __forceinline__ void load_tile(const uint16_t *head, int64_t row_bytes,
+                                          int k0, int Sk, lds_char *dst,
+                                          uint32_t off, int w) {
+    using G = Geo<D>;
+    int rows = Sk - k0;
+    rows = rows < 0 ? 0 : (rows > kBlockN ? kBlockN : rows);
+    // every field of the descriptor is wave-uniform; say so, so that it is
+    // built in scalar registers
+    const uint64_t a = reinterpret_cast<uint64_t>(head) + uint64_t(int64_t(k0) * row_bytes);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(a));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(a >> 32));
+    const int nrec = __builtin_amdgcn_readfirstlane(int(rows * row_bytes));
+    char *base = reinterpret_cast<char *>((uint64_t(hi) << 32) | lo);
+    __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(base, 0, nrec, kRsrcWord3);
+    const int step = int(kWaves * G::RPB * row_bytes);
 #pragma unroll
-        for (int i = 0; i < Geo<D>::kChunks; ++i) {
-            const int ch = tid + i * kThreads;
-            const int row = ch / Geo<D>::kChunksPerRow;
-            const int col = (ch % Geo<D>::kChunksPerRow) * 8;
-            const int key = k0 + row;
-            if (key < Sk) {
-                k[i] = *reinterpret_cast<const uint4 *>(kh + key * kss + col);
-                v[i] = *reinterpret_cast<const uint4 *>(vh + key * vss + col);
-            } else {
-                k[i] = make_uint4(0, 0, 0, 0);
-                v[i] = make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < G::NDMA; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rs, (lds_void *)(dst + (i * kWaves + w) * 1024), 16, off, i * step, 0, 0);
+}
+
+__device__ __forceinline__ void wait_loads() {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+template <int D, bool CAUSAL, bool OUT_BF16>
+struct Kernel {
+    using G = Geo<D>;
+    static constexpr int NT = D / 16;      // 16-wide d steps of q.k
+    static constexpr int NDB = D / 32;     // 32-wide d blocks of the output
+
+    lds_char *lds;
+    const Params &p;
+    int w, lane, half, l32;
+    int wrow0, qrow, Sk;
+    const uint16_t *kh, *vh;
+    int64_t krb, vrb;                 // row strides in bytes
+    uint32_t dk, dv;                  // per-lane DMA source offsets (block 0)
+    uint32_t koff[4];                 // per-lane K operand offsets (d steps t % 4)
+    uint32_t voff[NDB];               // per-lane V^T transpose-read offsets
+    bf16x8 qf[NT];
+    f32x16 acc[NDB];
+    f32x16 sc[2], sn[2];              // scores of the current and next tile
+    float m2, l, mrow;
+
+    __device__ __forceinline__ Kernel(lds_char *lds_, const Params &p_) : lds(lds_), p(p_) {}
+
+    __device__ __forceinline__ bool needs_mask(int kt) const {
+        const int k0 = kt * kBlockN;
+        bool m = k0 + kBlockN > Sk;
+        if (CAUSAL) m = m || int64_t(k0) + kBlockN - 1 > int64_t(wrow0) + p.causal;
+        return m;
+    }
+
+    __device__ __forceinline__ void mask(f32x16 (&s)[2], int kt) const {
+        const int k0 = kt * kBlockN;
+        int64_t lim = Sk;
+        if (CAUSAL) {
+            const int64_t c = int64_t(qrow) + p.causal + 1;
+            lim = c < lim ? c : lim;
+        }
+        const int64_t rem = lim - k0 - 4 * half;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                if (32 * kb + 8 * (r >> 2) + (r & 3) >= rem) s[kb][r] = kNegInf;
+    }
+
+    __device__ __forceinline__ float rowmax(const f32x16 (&s)[2]) const {
+        float mx = kNegInf;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+        return swap_halves_max(mx);
+    }
+
+    // S^T = K Q^T for the tile in K-ring slot kbuf
+    template <int KBUF>
+    __device__ __forceinline__ void qk(f32x16 (&s)[2]) const {
+        const lds_char *kt = lds + G::KRING + KBUF * G::TILE;
+        s[0] = f32x16{};
+        s[1] = f32x16{};
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                const bf16x8 kf = *(const lds_bf16x8 *)(kt + koff[t & 3] + 128 * (t >> 2) +
+                                                       kb * 32 * G::RB);
+                s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[t], s[kb], 0, 0, 0);
             }
+    }
+
+    // O^T += V^T P^T for 16-key steps st of the tile in V-ring slot VBUF
+    template <int VBUF, int ST0, int ST1>
+    __device__ __forceinline__ void pv(const bf16x8 (&pf)[4]) {
+        const lds_char *vt = lds + G::VRING + VBUF * G::TILE;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int st = ST0; st <= ST1; ++st) {
+                const lds_char *a = vt + voff[db] + 16 * st * G::RB;
+                const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)a);
+                const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                    (lds_bf16x4 *)(a + 8 * G::RB));
+                const bf16x8 vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[st], acc[db], 0, 0, 0);
+            }
+    }
+
+    // exponentials of one 32-key block of the current tile, in place
+    __device__ __forceinline__ float expblock(f32x16 &s) const {
+        float rs = 0.0f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const float e = exp2_fast(fmaf(s[r], p.c, -m2));
+            s[r] = e;
+            rs += e;
+        }
+        return rs;
+    }
+
+    // One tile j (PAR = j & 1): the scores of tile j are in sc and its row
+    // max in mrow; K of tile j + 1 and V of tile j are resident after the
+    // barrier.  NEXT: tile j + 1 exists.
+    template <int PAR, bool NEXT>
+    __device__ __forceinline__ void step(int j, int nkt) {
+        wait_loads();
+        __syncthreads();
+        // refill the slots freed by tile j - 1: K of tile j + 2, V of tile j + 1
+        load_tile<D>(kh, krb, (j + 2) * kBlockN, Sk, lds + G::KRING + PAR * G::TILE, dk, w);
+        load_tile<D>(vh, vrb, (j + 1) * kBlockN, Sk, lds + G::VRING + (PAR ^ 1) * G::TILE, dv, w);
+
+        // lazy max update: move the reference point only past kTau
+        const float cand = mrow * p.c;
+        const bool up = cand > m2 + kTau;
+        const float m2n = up ? cand : m2;
+        const float alpha = exp2_fast(m2 - m2n);
+        m2 = m2n;
+        if (wave_any(up)) {
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) acc[db] *= alpha;
+            l *= alpha;
+        }
+
+        // phase A: scores of tile j + 1 on the matrix cores, exponentials of
+        // the first 32 keys of tile j on the VALU
+        bf16x8 pf[4];
+        float rs = expblock(sc[0]);
+        pf[0] = cvt8(sc[0], 0);
+        pf[1] = cvt8(sc[0], 8);
+        if (NEXT) {
+            qk<PAR ^ 1>(sn);
+#pragma unroll
+            for (int i = 0; i < 2 * NT; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 56 / (2 * NT) + 1, 0);
+            }
+        }
+        // phase B1: P.V of the first 32 keys, exponentials of the rest
+        pv<PAR, 0, 1>(pf);
+        rs += expblock(sc[1]);
+        pf[2] = cvt8(sc[1], 0);
+        pf[3] = cvt8(sc[1], 8);
+        l += rs;
+#pragma unroll
+        for (int i = 0; i < 2 * NDB; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+            __builtin_amdgcn_sched_group_barrier(0x002, 56 / (2 * NDB) + 1, 1);
+        }
+        if (NEXT && needs_mask(j + 1)) mask(sn, j + 1);
+        // phase B2: P.V of the last 32 keys, row max of tile j + 1
+        pv<PAR, 2, 3>(pf);
+        if (NEXT) {
+            mrow = rowmax(sn);
+#pragma unroll
+            for (int i = 0; i < 2 * NDB; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 2);
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);
+                __builtin_amdgcn_sched_group_barrier(0x002, 3, 2);
+            }
+            sc[0] = sn[0];
+            sc[1] = sn[1];
         }
     }
 
-    __device__ __forceinline__ void store(uint16_t *ks, uint16_t *vs,
-                                          int tid) const {
+    __device__ __forceinline__ void run() {
+        const int tid = threadIdx.x;
+        lane = tid & (kWave - 1);
+        w = __builtin_amdgcn_readfirstlane(tid / kWave);
+        half = lane >> 5;
+        l32 = lane & 31;
+        const int g16 = lane & 15;
+        const int grp = (lane >> 4) & 1;
+
+        // the longest causal query blocks first; heads fastest
+        const int bh = blockIdx.x % p.BH;
+        const int qb = p.nqb - 1 - blockIdx.x / p.BH;
+        const int b = bh / p.H, h = bh % p.H;
+        const int q0 = qb * kBlockM;
+        wrow0 = q0 + w * kRowsPerWave;
+        qrow = wrow0 + l32;
+        Sk = p.Sk;
+
+        const uint16_t *qh = p.q + b * p.qs[0] + h * p.qs[1];
+        kh = p.k + b * p.ks[0] + h * p.ks[1];
+        vh = p.v + b * p.vs[0] + h * p.vs[1];
+        krb = p.ks[2] * 2;
+        vrb = p.vs[2] * 2;
+
+        // per-lane offsets: DMA sources, K operand reads, V^T transpose reads
+        {
+            const int r = w * G::RPB + lane / G::CPR;
+            const int slot = lane % G::CPR;
+            dk = uint32_t(r * krb + 16 * (slot ^ G::fk(r)));
+            dv = uint32_t(r * vrb + 16 * (slot ^ G::fv(r)));
+        }
+        // chunk 2 t + half of row l32 sits in slot (2 t + half) ^ fk(l32) =
+        // 2 (t ^ (fk >> 1)) + (half ^ (fk & 1)); fk < 8 touches only the low
+        // two bits of t, so the d steps t and t + 4 differ by 128 bytes
 #pragma unroll
-        for (int i = 0; i < Geo<D>::kChunks; ++i) {
-            const int ch = tid + i * kThreads;
-            const int row = ch / Geo<D>::kChunksPerRow;
-            const int col = (ch % Geo<D>::kChunksPerRow) * 8;
-            *reinterpret_cast<uint4 *>(ks + row * Geo<D>::KP + col) = k[i];
-            *reinterpret_cast<uint4 *>(vs + row * Geo<D>::VP + col) = v[i];
+        for (int t = 0; t < 4; ++t)
+            koff[t] = uint32_t(l32 * G::RB + 16 * ((2 * t + half) ^ G::fk(l32)));
+        const int vrow = 4 * half + (g16 >> 2);
+        const int x = 2 * grp + ((g16 & 3) >> 1);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+            voff[db] = uint32_t(vrow * G::RB + 16 * ((4 * db + x) ^ G::fv(vrow)) +
+                                8 * (g16 & 1));
+
+        // the wave's Q fragment: row qrow, d = 16 t + 8 half + (0..7)
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            uint4 u = make_uint4(0, 0, 0, 0);
+            if (qrow < p.Sq)
+                u = *reinterpret_cast<const uint4 *>(qh + qrow * p.qs[2] + 16 * t +
+                                                     8 * half);
+            qf[t] = as_bf16x8(u);
+        }
+
+        // keys this workgroup needs: all, or up to the causal limit of its last row
+        int kend = Sk;
+        if (CAUSAL) {
+            const int64_t lim = int64_t(q0) + kBlockM + p.causal;
+            kend = lim < Sk ? int(lim) : Sk;
+        }
+        const int nkt = (kend + kBlockN - 1) / kBlockN;
+
+        m2 = kNegInf;
+        l = 0.0f;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
+
+        // prologue: K of tiles 0 and 1, V of tile 0; scores and max of tile 0
+        load_tile<D>(kh, krb, 0, Sk, lds + G::KRING, dk, w);
+        load_tile<D>(kh, krb, kBlockN, Sk, lds + G::KRING + G::TILE, dk, w);
+        load_tile<D>(vh, vrb, 0, Sk, lds + G::VRING, dv, w);
+        wait_loads();
+        __syncthreads();
+        qk<0>(sc);
+        if (needs_mask(0)) mask(sc, 0);
+        mrow = rowmax(sc);
+
+        int j = 0;
+        for (; j + 2 < nkt; j += 2) {
+            step<0, true>(j, nkt);
+            step<1, true>(j + 1, nkt);
+        }
+        if (j + 1 < nkt) {
+            step<0, true>(j, nkt);
+            ++j;
+            step<1, false>(j, nkt);
+        } else {
+            step<0, false>(j, nkt);
+        }
+        wait_loads();
+
+        // epilogue: o = o~ / l, lse = (m2 + log2 l) ln 2
+        const float lt = swap_halves_sum(l);
+        if (qrow < p.Sq) {
+            const float inv = 1.0f / lt;
+            const int64_t obase = b * p.os[0] + h * p.os[1] + int64_t(qrow) * p.os[2];
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int rg = 0; rg < 4; ++rg) {
+                    const int d = 32 * db + 8 * rg + 4 * half;
+                    f32x4 xo = {acc[db][4 * rg + 0] * inv, acc[db][4 * rg + 1] * inv,
+                                acc[db][4 * rg + 2] * inv, acc[db][4 * rg + 3] * inv};
+                    if (OUT_BF16) {
+                        bf16x4 y = __builtin_convertvector(xo, bf16x4);
+                        *reinterpret_cast<bf16x4 *>(static_cast<uint16_t *>(p.o) + obase + d) = y;
+                    } else {
+                        *reinterpret_cast<f32x4 *>(static_cast<float *>(p.o) + obase + d) = xo;
+                    }
+                }
+            if (p.lse != nullptr && half == 0)
+                p.lse[int64_t(bh) * p.Sq + qrow] = (m2 + __builtin_amdgcn_logf(lt)) * kLn2;
         }
     }
 };
@@ -137,187 +439,9 @@ struct Tile {
 template <int D, bool CAUSAL, bool OUT_BF16>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_kernel(Params p) {
-    using G = Geo<D>;
-    constexpr int NT = D / 16;      // 16-wide d steps of q.k
-    constexpr int NDB = D / 32;     // 32-wide d blocks of the output
-    __shared__ __attribute__((aligned(16))) uint16_t smem[G::kLdsElems];
-    uint16_t *k_lds = smem;                  // [2][64][KP]
-    uint16_t *v_lds = smem + 2 * G::KT;      // [2][64][VP]
-
-    const int tid = threadIdx.x;
-    const int lane = tid & (kWave - 1);
-    const int w = tid / kWave;
-    const int half = lane >> 5;              // which 8-wide k slice of an operand
-    const int l32 = lane & 31;               // operand row / column
-    const int g16 = lane & 15;               // lane within a 16-lane group
-    const int grp = (lane >> 4) & 1;         // 16-row half of a 32-row V^T slice
-
-    // the longest causal query blocks first; heads fastest
-    const int bh = blockIdx.x % p.BH;
-    const int qb = p.nqb - 1 - blockIdx.x / p.BH;
-    const int b = bh / p.H, h = bh % p.H;
-    const int q0 = qb * kBlockM;
-    const int wrow0 = q0 + w * kRowsPerWave;   // the wave's first query row
-    const int qrow = wrow0 + l32;               // this lane's query row
-
-    const uint16_t *qh = p.q + b * p.qs[0] + h * p.qs[1];
-    const uint16_t *kh = p.k + b * p.ks[0] + h * p.ks[1];
-    const uint16_t *vh = p.v + b * p.vs[0] + h * p.vs[1];
-
-    // the wave's Q fragment: row qrow, d = 16 t + 8 half + (0..7)
-    bf16x8 qf[NT];
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-        uint4 u = make_uint4(0, 0, 0, 0);
-        if (qrow < p.Sq)
-            u = *reinterpret_cast<const uint4 *>(qh + qrow * p.qs[2] + 16 * t +
-                                                 8 * half);
-        qf[t] = as_bf16x8(u);
-    }
-
-    // keys this workgroup needs: all, or up to the causal limit of its last row
-    int kend = p.Sk;
-    if (CAUSAL) {
-        const int64_t lim = int64_t(q0) + kBlockM + p.causal;
-        kend = lim < p.Sk ? int(lim) : p.Sk;
-    }
-    const int nkt = (kend + kBlockN - 1) / kBlockN;
-    // a wave whose rows are all past Sq, or (causal) past which a tile lies,
-    // skips the math but still loads its share of every tile
-    const bool wave_live = wrow0 < p.Sq;
-    const int64_t wave_last_key = int64_t(wrow0) + kRowsPerWave - 1 + p.causal;
-
-    float m2 = kNegInf;   // running max of s * c
-    float l = 0.0f;       // this lane's share of the running sum (its 32 keys per tile)
-    f32x16 acc[NDB];
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
-
-    Tile<D> tile;
-    tile.load(kh, p.ks[2], vh, p.vs[2], 0, p.Sk, tid);
-    tile.store(k_lds, v_lds, tid);
-    __syncthreads();
-
-    for (int kt = 0; kt < nkt; ++kt) {
-        const int buf = kt & 1;
-        const int k0 = kt * kBlockN;
-        if (kt + 1 < nkt)
-            tile.load(kh, p.ks[2], vh, p.vs[2], k0 + kBlockN, p.Sk, tid);
-
-        const bool live = wave_live && (!CAUSAL || int64_t(k0) <= wave_last_key);
-        if (live) {
-            const uint16_t *kt_lds = k_lds + buf * G::KT;
-            const uint16_t *vt_lds = v_lds + buf * G::VT;
-            // ---- S^T = K Q^T for two 32-key blocks ----
-            f32x16 s[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-            for (int t = 0; t < NT; ++t) {
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-                    const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(
-                        kt_lds + (32 * kb + l32) * G::KP + 16 * t + 8 * half);
-                    s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[t],
-                                                                     s[kb], 0, 0, 0);
-                }
-            }
-            // ---- mask keys past Sk and (causal) past the row's limit ----
-            const bool tail = k0 + kBlockN > p.Sk;
-            const bool diag = CAUSAL && int64_t(k0) + kBlockN - 1 > int64_t(wrow0) + p.causal;
-            if (tail || diag) {
-                const int64_t row_last = int64_t(qrow) + p.causal;
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * half + (r & 3);
-                        bool out = key >= p.Sk;
-                        if (CAUSAL) out = out || key > row_last;
-                        if (out) s[kb][r] = kNegInf;
-                    }
-            }
-            // ---- online softmax update of this row ----
-            float mx = kNegInf;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-            mx = swap_halves_max(mx);
-            const float m2n = fmaxf(m2, mx * p.c);
-            const float alpha = exp2_fast(m2 - m2n);   // 0 on the first tile
-            float rs = 0.0f;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float e = exp2_fast(fmaf(s[kb][r], p.c, -m2n));
-                    s[kb][r] = e;
-                    rs += e;
-                }
-            l = l * alpha + rs;
-            m2 = m2n;
-            if (wave_any(alpha != 1.0f)) {
-#pragma unroll
-                for (int db = 0; db < NDB; ++db) acc[db] *= alpha;
-            }
-            // ---- probabilities as the bf16 B operand, one per 16-key step ----
-            bf16x8 pf[4];
-#pragma unroll
-            for (int st = 0; st < 4; ++st) {
-                const int kb = st >> 1, r0 = 8 * (st & 1);
-                f32x8 x = {s[kb][r0 + 0], s[kb][r0 + 1], s[kb][r0 + 2], s[kb][r0 + 3],
-                           s[kb][r0 + 4], s[kb][r0 + 5], s[kb][r0 + 6], s[kb][r0 + 7]};
-                pf[st] = __builtin_convertvector(x, bf16x8);
-            }
-            // ---- O^T += V^T P^T ----
-            // transpose read: lane x of a 16-lane group supplies the address
-            // of row (base + x / 4), columns 4 (x % 4) .. + 3; lane i then
-            // receives column i of those 4 rows.
-            const lds_char *vb = (const lds_char *)(vt_lds);
-#pragma unroll
-            for (int db = 0; db < NDB; ++db) {
-#pragma unroll
-                for (int st = 0; st < 4; ++st) {
-                    const int row = 16 * st + 4 * half + (g16 >> 2);
-                    const int col = 32 * db + 16 * grp + 4 * (g16 & 3);
-                    const lds_char *a0 = vb + 2 * (row * G::VP + col);
-                    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                        (lds_bf16x4 *)a0);
-                    const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                        (lds_bf16x4 *)(a0 + 2 * 8 * G::VP));
-                    const bf16x8 vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3,
-                                                              4, 5, 6, 7);
-                    acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[st],
-                                                                       acc[db], 0, 0, 0);
-                }
-            }
-        }
-        if (kt + 1 < nkt)
-            tile.store(k_lds + (buf ^ 1) * G::KT, v_lds + (buf ^ 1) * G::VT, tid);
-        __syncthreads();
-    }
-
-    // ---- epilogue: o = o~ / l, lse = (m2 + log2 l) ln 2 ----
-    const float lt = swap_halves_sum(l);
-    if (qrow < p.Sq) {
-        const float inv = 1.0f / lt;
-        const int64_t obase = b * p.os[0] + h * p.os[1] + int64_t(qrow) * p.os[2];
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-            for (int rg = 0; rg < 4; ++rg) {
-                const int d = 32 * db + 8 * rg + 4 * half;
-                f32x4 x = {acc[db][4 * rg + 0] * inv, acc[db][4 * rg + 1] * inv,
-                           acc[db][4 * rg + 2] * inv, acc[db][4 * rg + 3] * inv};
-                if (OUT_BF16) {
-                    bf16x4 y = __builtin_convertvector(x, bf16x4);
-                    *reinterpret_cast<bf16x4 *>(static_cast<uint16_t *>(p.o) + obase + d) = y;
-                } else {
-                    *reinterpret_cast<f32x4 *>(static_cast<float *>(p.o) + obase + d) = x;
-                }
-            }
-        if (p.lse != nullptr && half == 0)
-            p.lse[int64_t(bh) * p.Sq + qrow] = (m2 + __builtin_amdgcn_logf(lt)) * kLn2;
-    }
+    __shared__ __attribute__((aligned(1024))) char smem[Geo<D>::kLdsBytes];
+    Kernel<D, CAUSAL, OUT_BF16> k((lds_char *)smem, p);
+    k.run();
 }
 
 template <int D, bool CAUSAL, bool OUT_BF16>
@@ -366,6 +490,8 @@ extern "C" os_status os_attention_fwd(
         }
         if (st[t][2] < D) return OS_ERR_STRIDE;
     }
+    if (k_strides[2] >= kMaxRowStride || v_strides[2] >= kMaxRowStride)
+        return OS_ERR_UNSUPPORTED;
     if (B == 0 || H == 0 || Sq == 0) return OS_OK;
     if (!q || !k || !v || !o) return OS_ERR_NULL;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
