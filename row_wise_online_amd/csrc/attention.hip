@@ -41,9 +41,12 @@
 // are both taken relative to it); lse = (m2 + log2 l) ln 2.
 //
 // LDS layouts (rows of 2D bytes, no padding): 16-byte chunk c of row r of a
-// K tile sits in slot c ^ fk(r), of a V tile in slot c ^ fv(r).  With these
-// XOR swizzles the 64 lanes of a K operand read (32 rows x 32 bytes) and of
-// a V^T transpose read (8 rows x 64 bytes) spread evenly over the banks.
+// K tile sits in slot c ^ fk(r), of a V tile in slot c ^ fv(r).  LDS serves
+// 256 bytes per clock: a 128-bit read 16 lanes at a time, a 64-bit read 32
+// lanes at a time.  The swizzles give the 16 K rows of each 16-lane group of
+// an operand read, and the 4 V rows of each 32-lane group of a transpose
+// read, disjoint banks, so neither read conflicts (rocprofv3 counts zero
+// SQ_LDS_BANK_CONFLICT cycles for this kernel).
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -85,9 +88,9 @@ struct Geo {
     static constexpr int NDMA = TILE / 1024 / kWaves;   // wave loads per tile
     static constexpr int kLdsBytes = 4 * TILE;          // K ring (2) + V ring (2)
     static constexpr int KRING = 0, VRING = 2 * TILE;
-    __device__ static int fk(int r) { return D == 128 ? (r & 7) : ((r >> 1) & 7); }
+    __device__ static int fk(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
     __device__ static int fv(int r) {
-        return D == 128 ? 4 * ((r >> 1) & 3) : 4 * ((r >> 1) & 1);
+        return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
     }
 };
 
@@ -169,7 +172,7 @@ struct Kernel {
     const uint16_t *kh, *vh;
     int64_t krb, vrb;                 // row strides in bytes
     uint32_t dk, dv;                  // per-lane DMA source offsets (block 0)
-    uint32_t koff[4];                 // per-lane K operand offsets (d steps t % 4)
+    uint32_t koff[NT];                // per-lane K operand offsets
     uint32_t voff[NDB];               // per-lane V^T transpose-read offsets
     bf16x8 qf[NT];
     f32x16 acc[NDB];
@@ -201,12 +204,12 @@ struct Kernel {
     }
 
     __device__ __forceinline__ float rowmax(const f32x16 (&s)[2]) const {
-        float mx = kNegInf;
+        float mx[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-        return swap_halves_max(mx);
+            for (int r = 0; r < 16; ++r) mx[r & 3] = fmaxf(mx[r & 3], s[kb][r]);
+        return swap_halves_max(fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3])));
     }
 
     // S^T = K Q^T for the tile in K-ring slot kbuf
@@ -219,8 +222,7 @@ struct Kernel {
         for (int t = 0; t < NT; ++t)
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
-                const bf16x8 kf = *(const lds_bf16x8 *)(kt + koff[t & 3] + 128 * (t >> 2) +
-                                                       kb * 32 * G::RB);
+                const bf16x8 kf = *(const lds_bf16x8 *)(kt + koff[t] + kb * 32 * G::RB);
                 s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[t], s[kb], 0, 0, 0);
             }
     }
@@ -244,14 +246,14 @@ struct Kernel {
 
     // exponentials of one 32-key block of the current tile, in place
     __device__ __forceinline__ float expblock(f32x16 &s) const {
-        float rs = 0.0f;
+        float rs[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const float e = exp2_fast(fmaf(s[r], p.c, -m2));
             s[r] = e;
-            rs += e;
+            rs[r & 3] += e;
         }
-        return rs;
+        return (rs[0] + rs[1]) + (rs[2] + rs[3]);
     }
 
     // One tile j (PAR = j & 1): the scores of tile j are in sc and its row
@@ -298,6 +300,9 @@ struct Kernel {
         pf[2] = cvt8(sc[1], 0);
         pf[3] = cvt8(sc[1], 8);
         l += rs;
+        // keep this block's exponentials here, beside the P.V products they
+        // overlap, rather than sunk past the mask test below
+        asm volatile("" : "+v"(pf[2]), "+v"(pf[3]), "+v"(l));
 #pragma unroll
         for (int i = 0; i < 2 * NDB; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
@@ -351,11 +356,9 @@ struct Kernel {
             dk = uint32_t(r * krb + 16 * (slot ^ G::fk(r)));
             dv = uint32_t(r * vrb + 16 * (slot ^ G::fv(r)));
         }
-        // chunk 2 t + half of row l32 sits in slot (2 t + half) ^ fk(l32) =
-        // 2 (t ^ (fk >> 1)) + (half ^ (fk & 1)); fk < 8 touches only the low
-        // two bits of t, so the d steps t and t + 4 differ by 128 bytes
+        // chunk 2 t + half of row 32 kb + l32 sits in slot (2 t + half) ^ fk(l32)
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
+        for (int t = 0; t < NT; ++t)
             koff[t] = uint32_t(l32 * G::RB + 16 * ((2 * t + half) ^ G::fk(l32)));
         const int vrow = 4 * half + (g16 >> 2);
         const int x = 2 * grp + ((g16 & 3) >> 1);
