@@ -62,6 +62,24 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+template <int I>
+struct IC {
+    static constexpr int value = I;
+};
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for_impl(F &&f) {
+    if constexpr (I < N) {
+        f(IC<I>{});
+        static_for_impl<I + 1, N>(f);
+    }
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F &&f) {
+    static_for_impl<0, N>(f);
+}
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
 typedef __attribute__((address_space(3))) char lds_char;
@@ -227,21 +245,48 @@ struct Kernel {
             }
     }
 
-    // O^T += V^T P^T for 16-key steps st of the tile in V-ring slot VBUF
+    // O^T += V^T P^T for 16-key steps ST0..ST1 of the tile in V-ring slot
+    // VBUF.  The transpose reads are issued as inline asm, two operands
+    // ahead of the product that uses them, with explicit lgkmcnt waits: the
+    // compiler would otherwise precede the first of them with a wait for
+    // every direct-to-LDS load in flight (it cannot tell that they touch
+    // other LDS), i.e. for the next tiles' loads issued at the top of the
+    // step.  LDS operations complete in order, so waiting until at most
+    // 2 n remain, with n operands issued after this one, is enough; any
+    // LDS operation the compiler adds only makes its own waits stricter.
+    template <int VBUF, int ST0, int I>
+    __device__ __forceinline__ void tr_issue(u32x2 *lo, u32x2 *hi, uint32_t base) const {
+        constexpr int st = ST0 + I / NDB, db = I % NDB;
+        constexpr int off = G::VRING + VBUF * G::TILE + 16 * st * G::RB;
+        const uint32_t a = base + voff[db];
+        asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(lo[I]) : "v"(a), "n"(off));
+        asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2"
+                     : "=v"(hi[I]) : "v"(a), "n"(off + 8 * G::RB));
+    }
+
+    template <int VBUF, int ST0, int N, int I>
+    __device__ __forceinline__ void pv_rec(const bf16x8 (&pf)[4], u32x2 *lo, u32x2 *hi,
+                                           uint32_t base) {
+        if constexpr (I < N) {
+            constexpr int st = ST0 + I / NDB, db = I % NDB;
+            if constexpr (I + 2 < N) tr_issue<VBUF, ST0, I + 2>(lo, hi, base);
+            constexpr int later = (N - 1 - I) < 2 ? (N - 1 - I) : 2;  // operands issued after I
+            asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(lo[I]), "+v"(hi[I]) : "n"(2 * later));
+            const u32x4 u = {lo[I][0], lo[I][1], hi[I][0], hi[I][1]};
+            const bf16x8 vf = __builtin_bit_cast(bf16x8, u);
+            acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[st], acc[db], 0, 0, 0);
+            pv_rec<VBUF, ST0, N, I + 1>(pf, lo, hi, base);
+        }
+    }
+
     template <int VBUF, int ST0, int ST1>
     __device__ __forceinline__ void pv(const bf16x8 (&pf)[4]) {
-        const lds_char *vt = lds + G::VRING + VBUF * G::TILE;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-            for (int st = ST0; st <= ST1; ++st) {
-                const lds_char *a = vt + voff[db] + 16 * st * G::RB;
-                const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)a);
-                const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                    (lds_bf16x4 *)(a + 8 * G::RB));
-                const bf16x8 vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-                acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[st], acc[db], 0, 0, 0);
-            }
+        constexpr int N = (ST1 - ST0 + 1) * NDB;     // operands (MFMAs) in this call
+        const uint32_t base = uint32_t(reinterpret_cast<uintptr_t>(lds));
+        u32x2 lo[N], hi[N];
+        tr_issue<VBUF, ST0, 0>(lo, hi, base);
+        if constexpr (N > 1) tr_issue<VBUF, ST0, 1>(lo, hi, base);
+        pv_rec<VBUF, ST0, N, 0>(pf, lo, hi, base);
     }
 
     // exponentials of one 32-key block of the current tile, in place
@@ -305,7 +350,6 @@ struct Kernel {
         asm volatile("" : "+v"(pf[2]), "+v"(pf[3]), "+v"(l));
 #pragma unroll
         for (int i = 0; i < 2 * NDB; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
             __builtin_amdgcn_sched_group_barrier(0x002, 56 / (2 * NDB) + 1, 1);
         }
@@ -316,7 +360,6 @@ struct Kernel {
             mrow = rowmax(sn);
 #pragma unroll
             for (int i = 0; i < 2 * NDB; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x100, 2, 2);
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);
                 __builtin_amdgcn_sched_group_barrier(0x002, 3, 2);
             }
