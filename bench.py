@@ -39,12 +39,22 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published peak
 ROTATE_BYTES = 1 << 30      # rotating working set, 4x the Infinity Cache
 
 
-def kernel_source_hash():
+def kernel_source_hash(family="softmax"):
+    """Hash of the sources one kernel family is built from: "softmax" (every
+    csrc file but the attention kernel) or "attention" (the attention kernel
+    and the shared header).  A committed counter record applies only while
+    this hash is unchanged."""
     h = hashlib.sha256()
     for p in sorted(glob.glob(os.path.join(ROOT, "row_wise_online_amd",
                                            "csrc", "*"))):
+        name = os.path.basename(p)
+        is_attn = name.startswith("attention")
+        if family == "softmax" and is_attn:
+            continue
+        if family == "attention" and not (is_attn or name == "common.hpp"):
+            continue
         with open(p, "rb") as f:
-            h.update(os.path.basename(p).encode())
+            h.update(name.encode())
             h.update(f.read())
     return h.hexdigest()[:16]
 
@@ -262,7 +272,8 @@ def traffic_record(workload):
         return None
     with open(p) as f:
         rec = json.load(f).get(workload)
-    if not rec or rec.get("kernel_hash") != kernel_source_hash():
+    family = "attention" if workload.startswith("a") else "softmax"
+    if not rec or rec.get("kernel_hash") != kernel_source_hash(family):
         return None
     return rec.get("bytes_per_launch")
 
@@ -473,11 +484,13 @@ def run_attention(name, steps, warmup, want_cpu=True, cpu_budget=10.0,
             "algorithmic_flops_per_launch": flops,
             "kernel_launches_per_step": 1,
         },
-        "kernel_source": kernel_source_hash(),
+        "kernel_source": kernel_source_hash("attention"),
     }
     if extras:
         gms, _ = measure_attention(w, steps, 1, graph=True)
         rec["graph_replay_TFLOPs"] = round(flops / (gms * 1e-3) / 1e12, 2)
+    # a plain copy of Q's size: the calibration kernel for the HBM counters
+    rec["copy_ceiling_GBps"] = round(copy_ceiling(w.B * w.H * w.Sq * w.D * 2), 1)
     if want_cpu:
         rec["cpu_baseline"] = cpu_baseline_attention(w, cpu_budget)
     return rec
