@@ -6,7 +6,9 @@
 // 与 IO-Aware Attention" §7: the loop over K/V tiles).
 //
 // Work split.  One workgroup = 4 waves = 128 query rows of one (batch,
-// head); each wave owns 32 rows.  K and V tiles of 64 keys stream through
+// head) (under a causal mask, two such blocks in turn: the pair {n - 1 - i,
+// i} of the n query blocks, so every workgroup has the same work); each
+// wave owns 32 rows.  K and V tiles of 64 keys stream through
 // LDS rings of two tiles each, filled by direct-to-LDS buffer loads
 // (buffer_load_dwordx4 ... lds): no VGPR staging, and lanes past the last
 // key read as zero because each tile's buffer descriptor covers only the
@@ -377,16 +379,13 @@ struct Kernel {
         const int g16 = lane & 15;
         const int grp = (lane >> 4) & 1;
 
-        // the longest causal query blocks first; heads fastest
+        // heads fastest.  Under a causal mask query block i needs about i
+        // key tiles, so a workgroup takes the pair {n - 1 - i, i} (all pairs
+        // then cost the same and fit in one round of residency).
         const int bh = blockIdx.x % p.BH;
-        const int qb = p.nqb - 1 - blockIdx.x / p.BH;
+        const int i = blockIdx.x / p.BH;
         const int b = bh / p.H, h = bh % p.H;
-        const int q0 = qb * kBlockM;
-        wrow0 = q0 + w * kRowsPerWave;
-        qrow = wrow0 + l32;
         Sk = p.Sk;
-
-        const uint16_t *qh = p.q + b * p.qs[0] + h * p.qs[1];
         kh = p.k + b * p.ks[0] + h * p.ks[1];
         vh = p.v + b * p.vs[0] + h * p.vs[1];
         krb = p.ks[2] * 2;
@@ -409,6 +408,25 @@ struct Kernel {
         for (int db = 0; db < NDB; ++db)
             voff[db] = uint32_t(vrow * G::RB + 16 * ((4 * db + x) ^ G::fv(vrow)) +
                                 8 * (g16 & 1));
+
+        const uint16_t *qh = p.q + b * p.qs[0] + h * p.qs[1];
+        if (CAUSAL) {
+            const int qa = p.nqb - 1 - i;
+            block(qa, bh, qh, b, h);
+            if (i != qa) {
+                __syncthreads();       // every wave is done with the LDS rings
+                block(i, bh, qh, b, h);
+            }
+        } else {
+            block(p.nqb - 1 - i, bh, qh, b, h);
+        }
+    }
+
+    // one block of 128 query rows against all the keys it admits
+    __device__ __forceinline__ void block(int qb, int bh, const uint16_t *qh, int b, int h) {
+        const int q0 = qb * kBlockM;
+        wrow0 = q0 + w * kRowsPerWave;
+        qrow = wrow0 + l32;
 
         // the wave's Q fragment: row qrow, d = 16 t + 8 half + (0..7)
 #pragma unroll
@@ -564,7 +582,8 @@ extern "C" os_status os_attention_fwd(
     const bool causal = causal_offset >= 0 && causal_offset < Sk - 1;
     p.causal = causal ? int(causal_offset) : 0;
     p.c = float(double(scale) * 1.4426950408889634);
-    const int64_t blocks = nqb * B * H;
+    // causal: one workgroup per pair of query blocks {nqb - 1 - i, i}
+    const int64_t blocks = (causal ? (nqb + 1) / 2 : nqb) * B * H;
     if (D == 64) launch<64>(p, causal, o_dtype == OS_BF16, blocks, stream);
     else launch<128>(p, causal, o_dtype == OS_BF16, blocks, stream);
     return hipGetLastError() == hipSuccess ? OS_OK : OS_ERR_HIP;
