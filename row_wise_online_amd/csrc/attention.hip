@@ -5,11 +5,13 @@
 // e^(m_old - m_new) whenever a key block raises the max; "Softmax 数值稳定性
 // 与 IO-Aware Attention" §7: the loop over K/V tiles).
 //
-// Work split.  One workgroup = 4 waves = 128 query rows of one (batch,
+// Work split.  One workgroup = 8 waves = 256 query rows of one (batch,
 // head) (under a causal mask, two such blocks in turn: the pair {n - 1 - i,
 // i} of the n query blocks, so every workgroup has the same work); each
-// wave owns 32 rows.  K and V tiles of 64 keys stream through
-// LDS rings of two tiles each, filled by direct-to-LDS buffer loads
+// wave owns 32 rows, and each K/V tile in LDS feeds all 8.  At ~240 VGPRs
+// two waves fit per SIMD, i.e. one workgroup per CU.  K and V tiles of 64
+// keys stream through LDS rings of two tiles each, filled by direct-to-LDS
+// buffer loads
 // (buffer_load_dwordx4 ... lds): no VGPR staging, and lanes past the last
 // key read as zero because each tile's buffer descriptor covers only the
 // keys that exist.  One barrier per tile.
@@ -87,7 +89,7 @@ typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
 typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
 constexpr int kRowsPerWave = 32;
 constexpr int kBlockM = kWaves * kRowsPerWave;   // query rows per workgroup
 constexpr int kBlockN = 64;                      // keys per tile
@@ -147,12 +149,12 @@ __device__ __forceinline__ bf16x8 cvt8(const f32x16 &s, int r0) {
 }
 
 // Direct-to-LDS load of one 64-key tile (K or V) of one head: wave w writes
-// 1 KB blocks w, w + 4, ...; lane l's 16 bytes land at block + 16 l.  Block
-// i of the wave holds rows 4 i RPB (>= 16) further down than block 0 and
-// the swizzle of a row depends only on its low four bits, which that step
-// leaves alone, so one per-lane offset (row and chunk within block 0) plus
-// a uniform offset per block addresses every load.  Keys at or past
-// Sk lie outside the descriptor and arrive as zeros.
+// 1 KB blocks w, w + kWaves, ...; lane l's 16 bytes land at block + 16 l.
+// Block i of the wave holds rows kWaves i RPB (>= 16) further down than
+// block 0, and the swizzle of a row depends only on its low four bits,
+// which that step leaves alone, so one per-lane offset (row and chunk
+// within block 0) plus a uniform offset per block addresses every load.
+// Keys at or past Sk lie outside the descriptor and arrive as zeros.
 template <int D>
 __device__ __forceinline__ void load_tile(const uint16_t *head, int64_t row_bytes,
                                           int k0, int Sk, lds_char *dst,
