@@ -15,7 +15,7 @@
  * and "Softmax 数值稳定性与 IO-Aware Attention：从在线归一化到
  * FlashAttention" §7 (the loop over K/V tiles that never writes the score
  * matrix to memory).  The score matrix is never stored: each workgroup
- * keeps 128 query rows in registers, streams K and V tiles of 64 keys
+ * keeps 256 query rows in registers, streams K and V tiles of 64 keys
  * through LDS, and carries (m, l, o~) per row.
  *
  * Arithmetic: Q, K, V are bfloat16; q.k and P.V are bf16 matrix-core
@@ -62,12 +62,14 @@ extern "C" {
  * Returns OS_OK after enqueueing one kernel (nothing when B, H or Sq is 0),
  * or, before any HIP call:
  *  OS_ERR_NULL        a pointer the call needs is NULL;
- *  OS_ERR_SHAPE       B, H or Sq < 0, Sk < 1, Sq or Sk >= 2^31, or more
- *                     than 2^31 - 1 query blocks of 128 rows;
+ *  OS_ERR_SHAPE       B, H or Sq < 0, Sk < 1, Sq or Sk > 2^30, or more
+ *                     than 2^31 - 1 workgroups (query blocks of 256 rows,
+ *                     times B H);
  *  OS_ERR_STRIDE      a negative stride, a row stride < D, or a base or
  *                     stride not 16-byte aligned (all of q, k, v, o);
  *  OS_ERR_DTYPE       o_dtype is neither OS_F32 nor OS_BF16;
- *  OS_ERR_UNSUPPORTED D is not 64 or 128, or scale is not finite and > 0;
+ *  OS_ERR_UNSUPPORTED D is not 64 or 128, scale is not finite and > 0, or
+ *                     a K or V row stride is 2^23 elements or more;
  *  OS_ERR_HIP         the launch failed.
  * Deterministic: the work partition depends on the shape only and no
  * atomics are used. */

@@ -540,8 +540,11 @@ extern "C" os_status os_attention_fwd(
     os_dtype o_dtype, float scale, int64_t causal_offset, hipStream_t stream) {
     using namespace os::attn;
     constexpr int64_t kMax = (int64_t(1) << 31) - 1;
+    // sequence lengths up to 2^30 keep every row and tile index (including
+    // the look-ahead tiles past the end) inside int
+    constexpr int64_t kMaxSeq = int64_t(1) << 30;
     if (o_dtype != OS_F32 && o_dtype != OS_BF16) return OS_ERR_DTYPE;
-    if (B < 0 || H < 0 || Sq < 0 || Sk < 1 || Sq > kMax || Sk > kMax)
+    if (B < 0 || H < 0 || Sq < 0 || Sk < 1 || Sq > kMaxSeq || Sk > kMaxSeq)
         return OS_ERR_SHAPE;
     if (D != 64 && D != 128) return OS_ERR_UNSUPPORTED;
     if (!(scale > 0.0f) || !(scale <= 3.4028234663852886e38f)) return OS_ERR_UNSUPPORTED;

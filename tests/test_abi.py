@@ -226,7 +226,9 @@ def _attn(lib, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=NUL, B=1, H=2, Sq=10,
     (dict(scale=-0.5), 7), (dict(scale=float("inf")), 7),
     (dict(scale=float("nan")), 7), (dict(od=2), 4), (dict(od=-1), 4),
     (dict(Sk=0), 2), (dict(Sq=-1), 2), (dict(B=-1), 2), (dict(H=-3), 2),
-    (dict(Sq=1 << 31), 2), (dict(Sk=1 << 31), 2),
+    (dict(Sq=(1 << 30) + 1), 2), (dict(Sk=(1 << 30) + 1), 2),
+    (dict(ks=(1536 << 14, 768 << 14, 1 << 23)), 7),
+    (dict(vs=(1536 << 14, 768 << 14, 1 << 23)), 7),
     (dict(qs=None), 1), (dict(os_=None), 1),
     (dict(ks=(1536, -768, 64)), 3), (dict(vs=(1536, 768, 32)), 3),
     (dict(qs=(1280, 640, 68)), 3), (dict(os_=(1280, 644, 64)), 3),
