@@ -424,7 +424,7 @@ struct Kernel {
         }
     }
 
-    // one block of 128 query rows against all the keys it admits
+    // one block of kBlockM query rows against all the keys it admits
     __device__ __forceinline__ void block(int qb, int bh, const uint16_t *qh, int b, int h) {
         const int q0 = qb * kBlockM;
         wrow0 = q0 + w * kRowsPerWave;
