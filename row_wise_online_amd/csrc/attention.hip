@@ -10,11 +10,11 @@
 // i} of the n query blocks, so every workgroup has the same work); each
 // wave owns 32 rows, and each K/V tile in LDS feeds all 8.  At ~240 VGPRs
 // two waves fit per SIMD, i.e. one workgroup per CU.  K and V tiles of 64
-// keys stream through LDS rings of two tiles each, filled by direct-to-LDS
-// buffer loads
-// (buffer_load_dwordx4 ... lds): no VGPR staging, and lanes past the last
-// key read as zero because each tile's buffer descriptor covers only the
-// keys that exist.  One barrier per tile.
+// keys (128 at d = 64, so that a tile is 16 KiB and 32 MFMAs per wave either
+// way) stream through LDS rings of two tiles each, filled by direct-to-LDS
+// buffer loads (buffer_load_dwordx4 ... lds): no VGPR staging, and lanes
+// past the last key read as zero because each tile's buffer descriptor
+// covers only the keys that exist.  One barrier per tile.
 //
 // Products on v_mfma_f32_32x32x16_bf16 (lane l: operand row/column l % 32,
 // k = 8 (l / 32) + j for j < 8; result register r: row 8 (r / 4) +
@@ -92,7 +92,6 @@ typedef __attribute__((address_space(3))) void lds_void;
 constexpr int kWaves = 8;
 constexpr int kRowsPerWave = 32;
 constexpr int kBlockM = kWaves * kRowsPerWave;   // query rows per workgroup
-constexpr int kBlockN = 64;                      // keys per tile
 constexpr int kThreads = kWaves * kWave;
 constexpr float kLn2 = 0.69314718055994531f;
 constexpr float kTau = 8.0f;                     // lazy-rescale threshold (log2 units)
@@ -103,8 +102,13 @@ constexpr int64_t kMaxRowStride = int64_t(1) << 23;
 
 template <int D>
 struct Geo {
+    // keys per tile: a tile carries the same 32 MFMAs per wave (and the same
+    // 16 KiB per K or V tile) at d = 64 as at d = 128
+    static constexpr int BN = D == 128 ? 64 : 128;
+    static constexpr int KB = BN / 32;                  // 32-key score blocks
+    static constexpr int NST = BN / 16;                 // 16-key P.V steps
     static constexpr int RB = 2 * D;                    // bytes per row
-    static constexpr int TILE = kBlockN * RB;           // bytes per K or V tile
+    static constexpr int TILE = BN * RB;                // bytes per K or V tile
     static constexpr int CPR = D / 8;                   // 16-byte chunks per row
     static constexpr int RPB = 1024 / RB;               // rows per 1 KB wave load
     static constexpr int NDMA = TILE / 1024 / kWaves;   // wave loads per tile
@@ -148,7 +152,7 @@ __device__ __forceinline__ bf16x8 cvt8(const f32x16 &s, int r0) {
     return __builtin_convertvector(x, bf16x8);
 }
 
-// Direct-to-LDS load of one 64-key tile (K or V) of one head: wave w writes
+// Direct-to-LDS load of one key tile (K or V) of one head: wave w writes
 // 1 KB blocks w, w + kWaves, ...; lane l's 16 bytes land at block + 16 l.
 // Block i of the wave holds rows kWaves i RPB (>= 16) further down than
 // block 0, and the swizzle of a row depends only on its low four bits,
@@ -161,7 +165,7 @@ __device__ __forceinline__ void load_tile(const uint16_t *head, int64_t row_byte
                                           uint32_t off, int w) {
     using G = Geo<D>;
     int rows = Sk - k0;
-    rows = rows < 0 ? 0 : (rows > kBlockN ? kBlockN : rows);
+    rows = rows < 0 ? 0 : (rows > G::BN ? G::BN : rows);
     // every field of the descriptor is wave-uniform; say so, so that it is
     // built in scalar registers
     const uint64_t a = reinterpret_cast<uint64_t>(head) + uint64_t(int64_t(k0) * row_bytes);
@@ -198,20 +202,20 @@ struct Kernel {
     uint32_t voff[NDB];               // per-lane V^T transpose-read offsets
     bf16x8 qf[NT];
     f32x16 acc[NDB];
-    f32x16 sc[2], sn[2];              // scores of the current and next tile
+    f32x16 sc[G::KB], sn[G::KB];      // scores of the current and next tile
     float m2, l, mrow;
 
     __device__ __forceinline__ Kernel(lds_char *lds_, const Params &p_) : lds(lds_), p(p_) {}
 
     __device__ __forceinline__ bool needs_mask(int kt) const {
-        const int k0 = kt * kBlockN;
-        bool m = k0 + kBlockN > Sk;
-        if (CAUSAL) m = m || int64_t(k0) + kBlockN - 1 > int64_t(wrow0) + p.causal;
+        const int k0 = kt * G::BN;
+        bool m = k0 + G::BN > Sk;
+        if (CAUSAL) m = m || int64_t(k0) + G::BN - 1 > int64_t(wrow0) + p.causal;
         return m;
     }
 
-    __device__ __forceinline__ void mask(f32x16 (&s)[2], int kt) const {
-        const int k0 = kt * kBlockN;
+    __device__ __forceinline__ void mask(f32x16 (&s)[G::KB], int kt) const {
+        const int k0 = kt * G::BN;
         int64_t lim = Sk;
         if (CAUSAL) {
             const int64_t c = int64_t(qrow) + p.causal + 1;
@@ -219,16 +223,16 @@ struct Kernel {
         }
         const int64_t rem = lim - k0 - 4 * half;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < G::KB; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r)
                 if (32 * kb + 8 * (r >> 2) + (r & 3) >= rem) s[kb][r] = kNegInf;
     }
 
-    __device__ __forceinline__ float rowmax(const f32x16 (&s)[2]) const {
+    __device__ __forceinline__ float rowmax(const f32x16 (&s)[G::KB]) const {
         float mx[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < G::KB; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) mx[r & 3] = fmaxf(mx[r & 3], s[kb][r]);
         return swap_halves_max(fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3])));
@@ -236,14 +240,14 @@ struct Kernel {
 
     // S^T = K Q^T for the tile in K-ring slot kbuf
     template <int KBUF>
-    __device__ __forceinline__ void qk(f32x16 (&s)[2]) const {
+    __device__ __forceinline__ void qk(f32x16 (&s)[G::KB]) const {
         const lds_char *kt = lds + G::KRING + KBUF * G::TILE;
-        s[0] = f32x16{};
-        s[1] = f32x16{};
+#pragma unroll
+        for (int kb = 0; kb < G::KB; ++kb) s[kb] = f32x16{};
 #pragma unroll
         for (int t = 0; t < NT; ++t)
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
+            for (int kb = 0; kb < G::KB; ++kb) {
                 const bf16x8 kf = *(const lds_bf16x8 *)(kt + koff[t] + kb * 32 * G::RB);
                 s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[t], s[kb], 0, 0, 0);
             }
@@ -269,7 +273,7 @@ struct Kernel {
     }
 
     template <int VBUF, int ST0, int N, int I>
-    __device__ __forceinline__ void pv_rec(const bf16x8 (&pf)[4], u32x2 *lo, u32x2 *hi,
+    __device__ __forceinline__ void pv_rec(const bf16x8 (&pf)[G::NST], u32x2 *lo, u32x2 *hi,
                                            uint32_t base) {
         if constexpr (I < N) {
             constexpr int st = ST0 + I / NDB, db = I % NDB;
@@ -284,7 +288,7 @@ struct Kernel {
     }
 
     template <int VBUF, int ST0, int ST1>
-    __device__ __forceinline__ void pv(const bf16x8 (&pf)[4]) {
+    __device__ __forceinline__ void pv(const bf16x8 (&pf)[G::NST]) {
         constexpr int N = (ST1 - ST0 + 1) * NDB;     // operands (MFMAs) in this call
         const uint32_t base = uint32_t(reinterpret_cast<uintptr_t>(lds));
         u32x2 lo[N], hi[N];
@@ -313,8 +317,8 @@ struct Kernel {
         wait_loads();
         __syncthreads();
         // refill the slots freed by tile j - 1: K of tile j + 2, V of tile j + 1
-        load_tile<D>(kh, krb, (j + 2) * kBlockN, Sk, lds + G::KRING + PAR * G::TILE, dk, w);
-        load_tile<D>(vh, vrb, (j + 1) * kBlockN, Sk, lds + G::VRING + (PAR ^ 1) * G::TILE, dv, w);
+        load_tile<D>(kh, krb, (j + 2) * G::BN, Sk, lds + G::KRING + PAR * G::TILE, dk, w);
+        load_tile<D>(vh, vrb, (j + 1) * G::BN, Sk, lds + G::VRING + (PAR ^ 1) * G::TILE, dv, w);
 
         // lazy max update: move the reference point only past kTau
         const float cand = mrow * p.c;
@@ -329,46 +333,59 @@ struct Kernel {
         }
 
         // phase A: scores of tile j + 1 on the matrix cores, exponentials of
-        // the first 32 keys of tile j on the VALU
-        bf16x8 pf[4];
-        float rs = expblock(sc[0]);
-        pf[0] = cvt8(sc[0], 0);
-        pf[1] = cvt8(sc[0], 8);
+        // the first half of tile j's keys on the VALU
+        constexpr int H1 = G::KB / 2;             // score blocks per half tile
+        constexpr int NQK = NT * G::KB;           // q.k MFMAs per tile
+        constexpr int NPV = NDB * G::NST / 2;     // P.V MFMAs per half tile
+        constexpr int kVH = 28 * H1 + 1;          // VALU per half: 16 fma, exp, add + 8 cvt per block
+        bf16x8 pf[G::NST];
+        float rs = 0.0f;
+#pragma unroll
+        for (int kb = 0; kb < H1; ++kb) {
+            rs += expblock(sc[kb]);
+            pf[2 * kb] = cvt8(sc[kb], 0);
+            pf[2 * kb + 1] = cvt8(sc[kb], 8);
+        }
         if (NEXT) {
             qk<PAR ^ 1>(sn);
 #pragma unroll
-            for (int i = 0; i < 2 * NT; ++i) {
+            for (int i = 0; i < NQK; ++i) {
                 __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x002, 56 / (2 * NT) + 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, kVH / NQK + 1, 0);
             }
         }
-        // phase B1: P.V of the first 32 keys, exponentials of the rest
-        pv<PAR, 0, 1>(pf);
-        rs += expblock(sc[1]);
-        pf[2] = cvt8(sc[1], 0);
-        pf[3] = cvt8(sc[1], 8);
-        l += rs;
-        // keep this block's exponentials here, beside the P.V products they
-        // overlap, rather than sunk past the mask test below
-        asm volatile("" : "+v"(pf[2]), "+v"(pf[3]), "+v"(l));
+        // phase B1: P.V of the first half, exponentials of the rest
+        pv<PAR, 0, G::NST / 2 - 1>(pf);
 #pragma unroll
-        for (int i = 0; i < 2 * NDB; ++i) {
+        for (int kb = H1; kb < G::KB; ++kb) {
+            rs += expblock(sc[kb]);
+            pf[2 * kb] = cvt8(sc[kb], 0);
+            pf[2 * kb + 1] = cvt8(sc[kb], 8);
+        }
+        l += rs;
+        // keep these exponentials here, beside the P.V products they
+        // overlap, rather than sunk past the mask test below
+#pragma unroll
+        for (int st = G::NST / 2; st < G::NST; ++st) asm volatile("" : "+v"(pf[st]));
+        asm volatile("" : "+v"(l));
+#pragma unroll
+        for (int i = 0; i < NPV; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-            __builtin_amdgcn_sched_group_barrier(0x002, 56 / (2 * NDB) + 1, 1);
+            __builtin_amdgcn_sched_group_barrier(0x002, kVH / NPV + 1, 1);
         }
         if (NEXT && needs_mask(j + 1)) mask(sn, j + 1);
-        // phase B2: P.V of the last 32 keys, row max of tile j + 1
-        pv<PAR, 2, 3>(pf);
+        // phase B2: P.V of the second half, row max of tile j + 1
+        pv<PAR, G::NST / 2, G::NST - 1>(pf);
         if (NEXT) {
             mrow = rowmax(sn);
 #pragma unroll
-            for (int i = 0; i < 2 * NDB; ++i) {
+            for (int i = 0; i < NPV; ++i) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);
-                __builtin_amdgcn_sched_group_barrier(0x002, 3, 2);
+                __builtin_amdgcn_sched_group_barrier(0x002, (8 * G::KB + 4) / NPV + 1, 2);
             }
-            sc[0] = sn[0];
-            sc[1] = sn[1];
+#pragma unroll
+            for (int kb = 0; kb < G::KB; ++kb) sc[kb] = sn[kb];
         }
     }
 
@@ -446,7 +463,7 @@ struct Kernel {
             const int64_t lim = int64_t(q0) + kBlockM + p.causal;
             kend = lim < Sk ? int(lim) : Sk;
         }
-        const int nkt = (kend + kBlockN - 1) / kBlockN;
+        const int nkt = (kend + G::BN - 1) / G::BN;
 
         m2 = kNegInf;
         l = 0.0f;
@@ -455,7 +472,7 @@ struct Kernel {
 
         // prologue: K of tiles 0 and 1, V of tile 0; scores and max of tile 0
         load_tile<D>(kh, krb, 0, Sk, lds + G::KRING, dk, w);
-        load_tile<D>(kh, krb, kBlockN, Sk, lds + G::KRING + G::TILE, dk, w);
+        load_tile<D>(kh, krb, G::BN, Sk, lds + G::KRING + G::TILE, dk, w);
         load_tile<D>(vh, vrb, 0, Sk, lds + G::VRING, dv, w);
         wait_loads();
         __syncthreads();
