@@ -14,7 +14,7 @@ once, row statistics written) divided by the step time.
 
 ``--all`` also prints one JSON line per workload to stderr.
 
-``--op attention`` (workloads a2, a3, a4) times one ``os_attention_fwd``
+``--op attention`` (workloads a2, a3, a4, a5) times one ``os_attention_fwd``
 call per step instead: the attention forward with the online softmax inside
 key tiles; ``value`` is then TFLOP/s (4 Sq Sk D per head for Q K^T and P V,
 over the admitted key pairs only under a causal mask), against the MI355X
@@ -505,7 +505,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=None,
                     help="untimed steps (default 2000; 3 for attention)")
     ap.add_argument("--workload", default=None,
-                    choices=["c1", "c2", "c3", "c4", "c5", "a2", "a3", "a4"],
+                    choices=["c1", "c2", "c3", "c4", "c5", "a2", "a3", "a4",
+                             "a5"],
                     help="default c2 (a2 for --op attention)")
     ap.add_argument("--path", default="auto",
                     choices=["auto", "resident", "stream", "split"])
@@ -535,7 +536,7 @@ def main():
     if args.workload is None:
         args.workload = "a2" if att else "c2"
     if att != args.workload.startswith("a"):
-        print("--op attention takes workloads a2, a3, a4; the row-wise ops "
+        print("--op attention takes workloads a2..a5; the row-wise ops "
               "c1..c5", file=sys.stderr)
         sys.exit(2)
     if args.steps is None:
@@ -567,7 +568,7 @@ def main():
                              causal=0)
             print(json.dumps(r), file=sys.stderr, flush=True)
         if not att:
-            for name in ["a2", "a3", "a4"]:
+            for name in ["a2", "a3", "a4", "a5"]:
                 print(f"[bench] attention workload {name}", file=sys.stderr,
                       flush=True)
                 r = run_attention(name, 20, 3, want_cpu=False,

@@ -16,7 +16,7 @@
  * FlashAttention" §7 (the loop over K/V tiles that never writes the score
  * matrix to memory).  The score matrix is never stored: each workgroup
  * keeps 256 query rows in registers, streams K and V tiles of 64 keys
- * (128 at D = 64) through LDS, and carries (m, l, o~) per row.
+ * (128 at D = 64 and 32) through LDS, and carries (m, l, o~) per row.
  *
  * Arithmetic: Q, K, V are bfloat16; q.k and P.V are bf16 matrix-core
  * products with fp32 accumulation; the softmax state is fp32.  The
@@ -54,7 +54,7 @@ extern "C" {
  *  o          [B][H][Sq][D] under o_strides, dtype o_dtype (OS_BF16,
  *             rounded to nearest even, or OS_F32); device, written.
  *  lse        fp32 [B][H][Sq] dense, nullable; device, written.
- *  D          64 or 128.
+ *  D          32, 64 or 128.
  *  *_strides  host arrays of 3 int64 (batch, head, row), in elements,
  *             each >= 0, the row stride >= D; read during the call only.
  *  scale      multiplies q.k; finite and > 0 (the pages use 1/sqrt(D)).
@@ -68,7 +68,7 @@ extern "C" {
  *  OS_ERR_STRIDE      a negative stride, a row stride < D, or a base or
  *                     stride not 16-byte aligned (all of q, k, v, o);
  *  OS_ERR_DTYPE       o_dtype is neither OS_F32 nor OS_BF16;
- *  OS_ERR_UNSUPPORTED D is not 64 or 128, scale is not finite and > 0, or
+ *  OS_ERR_UNSUPPORTED D is not 32, 64 or 128, scale is not finite and > 0, or
  *                     a K or V row stride is 2^23 elements or more;
  *  OS_ERR_HIP         the launch failed.
  * Deterministic: the work partition depends on the shape only and no

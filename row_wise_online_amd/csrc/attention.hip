@@ -103,7 +103,8 @@ constexpr int64_t kMaxRowStride = int64_t(1) << 23;
 template <int D>
 struct Geo {
     // keys per tile: a tile carries the same 32 MFMAs per wave (and the same
-    // 16 KiB per K or V tile) at d = 64 as at d = 128
+    // 16 KiB per K or V tile) at d = 64 as at d = 128; d = 32 keeps 128 keys
+    // (8 KiB), where the score registers of two tiles would otherwise grow
     static constexpr int BN = D == 128 ? 64 : 128;
     static constexpr int KB = BN / 32;                  // 32-key score blocks
     static constexpr int NST = BN / 16;                 // 16-key P.V steps
@@ -114,9 +115,14 @@ struct Geo {
     static constexpr int NDMA = TILE / 1024 / kWaves;   // wave loads per tile
     static constexpr int kLdsBytes = 4 * TILE;          // K ring (2) + V ring (2)
     static constexpr int KRING = 0, VRING = 2 * TILE;
-    __device__ static int fk(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+    // a row is 16 (d = 128), 8 (d = 64) or 4 (d = 32) chunks; a 16-lane
+    // group of a K operand read covers 16 consecutive rows, a 32-lane group
+    // of a V transpose read 4 consecutive rows of 64 bytes
+    __device__ static int fk(int r) {
+        return D == 128 ? (r & 15) : D == 64 ? ((r >> 1) & 7) : ((r >> 2) & 3);
+    }
     __device__ static int fv(int r) {
-        return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
+        return D == 128 ? 4 * (r & 3) : D == 64 ? 4 * ((r >> 1) & 1) : 0;
     }
 };
 
@@ -563,7 +569,7 @@ extern "C" os_status os_attention_fwd(
     if (o_dtype != OS_F32 && o_dtype != OS_BF16) return OS_ERR_DTYPE;
     if (B < 0 || H < 0 || Sq < 0 || Sk < 1 || Sq > kMaxSeq || Sk > kMaxSeq)
         return OS_ERR_SHAPE;
-    if (D != 64 && D != 128) return OS_ERR_UNSUPPORTED;
+    if (D != 32 && D != 64 && D != 128) return OS_ERR_UNSUPPORTED;
     if (!(scale > 0.0f) || !(scale <= 3.4028234663852886e38f)) return OS_ERR_UNSUPPORTED;
     if (!q_strides || !k_strides || !v_strides || !o_strides) return OS_ERR_NULL;
     const int64_t nqb = (Sq + kBlockM - 1) / kBlockM;
@@ -606,7 +612,8 @@ extern "C" os_status os_attention_fwd(
     p.c = float(double(scale) * 1.4426950408889634);
     // causal: one workgroup per pair of query blocks {nqb - 1 - i, i}
     const int64_t blocks = (causal ? (nqb + 1) / 2 : nqb) * B * H;
-    if (D == 64) launch<64>(p, causal, o_dtype == OS_BF16, blocks, stream);
+    if (D == 32) launch<32>(p, causal, o_dtype == OS_BF16, blocks, stream);
+    else if (D == 64) launch<64>(p, causal, o_dtype == OS_BF16, blocks, stream);
     else launch<128>(p, causal, o_dtype == OS_BF16, blocks, stream);
     return hipGetLastError() == hipSuccess ? OS_OK : OS_ERR_HIP;
 }

@@ -35,6 +35,7 @@ a1     2 x 3 x 300 x 333 x 128          no      N(0,1)
 a2     1 x 1 x 131072 x 131072 x 128    no      N(0,1)
 a3     1 x 1 x 131072 x 131072 x 128    0       N(0,1)
 a4     1 x 1 x 131072 x 131072 x 64     no      N(0,1)
+a5     1 x 1 x 131072 x 131072 x 32     no      N(0,1)
 =====  ===============================  ======  =======================
 """
 from dataclasses import dataclass, field
@@ -188,6 +189,8 @@ ATTN_WORKLOADS = {
                        "bf16 one head, 131072^2, d=128, causal"),
     "a4": AttnWorkload("a4", 1, 1, 131072, 131072, 64, -1, 2004,
                        "bf16 one head, 131072^2, d=64"),
+    "a5": AttnWorkload("a5", 1, 1, 131072, 131072, 32, -1, 2005,
+                       "bf16 one head, 131072^2, d=32"),
 }
 
 

@@ -222,7 +222,7 @@ def _attn(lib, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=NUL, B=1, H=2, Sq=10,
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(D=96), 7), (dict(D=32), 7), (dict(scale=0.0), 7),
+    (dict(D=96), 7), (dict(D=16), 7), (dict(D=48), 7), (dict(scale=0.0), 7),
     (dict(scale=-0.5), 7), (dict(scale=float("inf")), 7),
     (dict(scale=float("nan")), 7), (dict(od=2), 4), (dict(od=-1), 4),
     (dict(Sk=0), 2), (dict(Sq=-1), 2), (dict(B=-1), 2), (dict(H=-3), 2),

@@ -129,7 +129,7 @@ def check(q, k, v, o, lse, *, causal=-1, scale=None, bf16_out=True, rows=None,
 # Small shapes: every output element against the oracle
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("D", [32, 64, 128])
 @pytest.mark.parametrize("out", ["bf16", "f32"])
 def test_a1_shape_every_element(D, out):
     w = wl.ATTN_WORKLOADS["a1"]
@@ -150,7 +150,7 @@ def test_causal_offsets(causal):
 
 @pytest.mark.parametrize("Sq,Sk", [(1, 1), (1, 64), (1, 65), (31, 7), (129, 1),
                                    (128, 64), (257, 200), (64, 1000), (5, 4097)])
-@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("D", [32, 64, 128])
 def test_ragged_shapes(Sq, Sk, D):
     q, k, v = wl.attention_inputs(1, 1, Sq, Sk, D, seed=Sq * 7 + Sk)
     print(f"ragged Sq={Sq} Sk={Sk} D={D}", flush=True)
@@ -293,7 +293,7 @@ def _sample_rows(Sq, seed):
     return sorted(set(fixed) | set(rng.integers(0, Sq, 14).tolist()))
 
 
-@pytest.mark.parametrize("name", ["a2", "a3", "a4"])
+@pytest.mark.parametrize("name", ["a2", "a3", "a4", "a5"])
 def test_full_size_sampled_rows(name):
     w = wl.ATTN_WORKLOADS[name]
     print(f"full size {name}: {w.desc}", flush=True)
