@@ -8,13 +8,12 @@
 // Work split.  One workgroup = 8 waves = 256 query rows of one (batch,
 // head) (under a causal mask, two such blocks in turn: the pair {n - 1 - i,
 // i} of the n query blocks, so every workgroup has the same work); each
-// wave owns 32 rows, and each K/V tile in LDS feeds all 8.  At ~240 VGPRs
-// two waves fit per SIMD, i.e. one workgroup per CU.  K and V tiles of 64
-// keys (128 at d = 64, so that a tile is 16 KiB and 32 MFMAs per wave either
-// way) stream through LDS rings of two tiles each, filled by direct-to-LDS
-// buffer loads (buffer_load_dwordx4 ... lds): no VGPR staging, and lanes
-// past the last key read as zero because each tile's buffer descriptor
-// covers only the keys that exist.  One barrier per tile.
+// wave owns 32 rows, and each K/V tile in LDS feeds all 8.  At up to ~240
+// VGPRs two waves fit per SIMD, i.e. one workgroup per CU.  K and V tiles of
+// 64 keys (128 at d = 32) stream through LDS rings of two tiles each, filled
+// by direct-to-LDS buffer loads (buffer_load_dwordx4 ... lds): no VGPR
+// staging, and lanes past the last key read as zero because each tile's
+// buffer descriptor covers only the keys that exist.
 //
 // Products on v_mfma_f32_32x32x16_bf16 (lane l: operand row/column l % 32,
 // k = 8 (l / 32) + j for j < 8; result register r: row 8 (r / 4) +
@@ -33,16 +32,27 @@
 //                 V^T slice, gathered from the row-major V tile by two
 //                 ds_read_b64_tr_b16 (LDS transpose reads) per operand.
 //
-// Software pipeline.  While the exponentials of tile j run on the VALU, the
-// matrix cores compute the scores of tile j + 1; the P.V products of tile j
-// then overlap the second half of tile j's exponentials and tile j + 1's row
-// max.  sched_group_barrier fixes the interleaving of each phase.
+// Ping-pong.  Each tile is worked in two halves: a VALU half (the
+// probabilities p = 2^(s c - m2), their row sum, their bf16 copies) and a
+// matrix half (O^T += V^T P^T for the tile, then the scores of the next
+// tile).  The two waves that share a SIMD (waves w and w + 4 of the
+// workgroup) run half a tile apart, so one wave's exponentials overlap the
+// other wave's MFMAs; where each group of four waves puts its barriers (both
+// execute the same number) keeps them apart.  The schedule, in barrier
+// intervals: in interval 2j group 0 does tile j's VALU half and group 1 tile
+// j - 1's matrix half; in interval 2j + 1 group 0 does tile j's matrix half
+// and group 1 tile j's VALU half.  The loads for tile t's matrix half (V of
+// tile t, K of tile t + 1) are issued by every wave at the start of interval
+// 2t - 1 and waited for before the barrier that opens interval 2t + 1; their
+// ring slot was last read in interval 2t - 2.
 //
-// Online state in base 2: t = s c with c = scale log2(e); the reference
-// point m2 of each row moves only when a tile's max exceeds it by more than
-// kTau (a lazy rescale: every p = 2^(t - m2) stays below 2^kTau, and the
-// result does not depend on which reference point is used, since o and l
-// are both taken relative to it); lse = (m2 + log2 l) ln 2.
+// Online state in base 2: t = s c with c = scale log2(e).  Each row starts
+// its reference point m2 at the max of its first tile; later it moves only
+// when some lane's sum of p exceeds 2^8 (the sum bounds every p of the
+// lane): then the exact row max is taken, o~ and l are rescaled by
+// 2^(m2_old - m2_new) and the tile's p recomputed.  Every p stays below 2^8,
+// and the result does not depend on which reference point is used, since o
+// and l are both taken relative to it; lse = (m2 + log2 l) ln 2.
 //
 // LDS layouts (rows of 2D bytes, no padding): 16-byte chunk c of row r of a
 // K tile sits in slot c ^ fk(r), of a V tile in slot c ^ fv(r).  LDS serves
@@ -94,7 +104,8 @@ constexpr int kRowsPerWave = 32;
 constexpr int kBlockM = kWaves * kRowsPerWave;   // query rows per workgroup
 constexpr int kThreads = kWaves * kWave;
 constexpr float kLn2 = 0.69314718055994531f;
-constexpr float kTau = 8.0f;                     // lazy-rescale threshold (log2 units)
+constexpr float kOver = 256.0f;                  // a row sum above this moves m2
+constexpr int kKAhead = 3;                       // K operand reads issued ahead
 // Buffer descriptor word 3 for raw (unswizzled, stride 0) dword buffers.
 constexpr int kRsrcWord3 = 0x00020000;
 // Row strides (elements) below this keep a tile's byte offsets in 32 bits.
@@ -102,10 +113,9 @@ constexpr int64_t kMaxRowStride = int64_t(1) << 23;
 
 template <int D>
 struct Geo {
-    // keys per tile: a tile carries the same 32 MFMAs per wave (and the same
-    // 16 KiB per K or V tile) at d = 64 as at d = 128; d = 32 keeps 128 keys
-    // (8 KiB), where the score registers of two tiles would otherwise grow
-    static constexpr int BN = D == 128 ? 64 : 128;
+    // keys per tile: 64, or 128 at d = 32, whose tiles would otherwise be
+    // too short to pay for their barriers
+    static constexpr int BN = D == 32 ? 128 : 64;
     static constexpr int KB = BN / 32;                  // 32-key score blocks
     static constexpr int NST = BN / 16;                 // 16-key P.V steps
     static constexpr int RB = 2 * D;                    // bytes per row
@@ -150,12 +160,6 @@ __device__ __forceinline__ float swap_halves_sum(float x) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const uint4 &u) {
     return __builtin_bit_cast(bf16x8, u);
-}
-
-__device__ __forceinline__ bf16x8 cvt8(const f32x16 &s, int r0) {
-    f32x8 x = {s[r0 + 0], s[r0 + 1], s[r0 + 2], s[r0 + 3],
-               s[r0 + 4], s[r0 + 5], s[r0 + 6], s[r0 + 7]};
-    return __builtin_convertvector(x, bf16x8);
 }
 
 // Direct-to-LDS load of one key tile (K or V) of one head: wave w writes
@@ -208,8 +212,9 @@ struct Kernel {
     uint32_t voff[NDB];               // per-lane V^T transpose-read offsets
     bf16x8 qf[NT];
     f32x16 acc[NDB];
-    f32x16 sc[G::KB], sn[G::KB];      // scores of the current and next tile
-    float m2, l, mrow;
+    f32x16 sc[G::KB];                 // scores of the tile in hand
+    bf16x8 pf[G::NST];                // its probabilities as the P.V operand
+    float m2, l;
 
     __device__ __forceinline__ Kernel(lds_char *lds_, const Params &p_) : lds(lds_), p(p_) {}
 
@@ -244,19 +249,47 @@ struct Kernel {
         return swap_halves_max(fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3])));
     }
 
-    // S^T = K Q^T for the tile in K-ring slot kbuf
+    // S^T = K Q^T for the tile in K-ring slot KBUF.  The K operands are read
+    // by inline asm PF operands ahead of their product, with explicit
+    // lgkmcnt waits (as for the V reads below).
+    template <int KBUF, int I>
+    __device__ __forceinline__ void k_issue(u32x4 *kf, uint32_t base) const {
+        constexpr int t = I / G::KB, kb = I % G::KB;
+        constexpr int off = G::KRING + KBUF * G::TILE + kb * 32 * G::RB;
+        asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(kf[I]) : "v"(base + koff[t]), "n"(off));
+    }
+
+    template <int KBUF, int N, int PF, int I>
+    __device__ __forceinline__ void qk_rec(f32x16 (&s)[G::KB], u32x4 *kf, uint32_t base) const {
+        if constexpr (I < N) {
+            constexpr int t = I / G::KB, kb = I % G::KB;
+            if constexpr (I + PF < N) k_issue<KBUF, I + PF>(kf, base);
+            constexpr int later = (N - 1 - I) < PF ? (N - 1 - I) : PF;
+            asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(kf[I]) : "n"(later));
+            s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf[I]),
+                                                             qf[t], s[kb], 0, 0, 0);
+            qk_rec<KBUF, N, PF, I + 1>(s, kf, base);
+        }
+    }
+
+    template <int KBUF, int PF, int I>
+    __device__ __forceinline__ void k_prologue(u32x4 *kf, uint32_t base) const {
+        if constexpr (I < PF) {
+            k_issue<KBUF, I>(kf, base);
+            k_prologue<KBUF, PF, I + 1>(kf, base);
+        }
+    }
+
     template <int KBUF>
     __device__ __forceinline__ void qk(f32x16 (&s)[G::KB]) const {
-        const lds_char *kt = lds + G::KRING + KBUF * G::TILE;
+        constexpr int N = NT * G::KB;
+        constexpr int PF = kKAhead < N ? kKAhead : N;
+        const uint32_t base = uint32_t(reinterpret_cast<uintptr_t>(lds));
 #pragma unroll
         for (int kb = 0; kb < G::KB; ++kb) s[kb] = f32x16{};
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-#pragma unroll
-            for (int kb = 0; kb < G::KB; ++kb) {
-                const bf16x8 kf = *(const lds_bf16x8 *)(kt + koff[t] + kb * 32 * G::RB);
-                s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[t], s[kb], 0, 0, 0);
-            }
+        u32x4 kf[N];
+        k_prologue<KBUF, PF, 0>(kf, base);
+        qk_rec<KBUF, N, PF, 0>(s, kf, base);
     }
 
     // O^T += V^T P^T for 16-key steps ST0..ST1 of the tile in V-ring slot
@@ -303,96 +336,102 @@ struct Kernel {
         pv_rec<VBUF, ST0, N, 0>(pf, lo, hi, base);
     }
 
-    // exponentials of one 32-key block of the current tile, in place
-    __device__ __forceinline__ float expblock(f32x16 &s) const {
+    // p = 2^(s c - m2) for the tile in sc, their sum (returned), and their
+    // bf16 copies in pf (8 keys each)
+    __device__ __forceinline__ float probs() {
         float rs[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const float e = exp2_fast(fmaf(s[r], p.c, -m2));
-            s[r] = e;
-            rs[r & 3] += e;
-        }
+        for (int kb = 0; kb < G::KB; ++kb)
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                f32x8 e;
+#pragma unroll
+                for (int r = 0; r < 8; ++r) {
+                    e[r] = exp2_fast(fmaf(sc[kb][8 * hh + r], p.c, -m2));
+                    rs[r & 3] += e[r];
+                }
+                pf[2 * kb + hh] = __builtin_convertvector(e, bf16x8);
+            }
         return (rs[0] + rs[1]) + (rs[2] + rs[3]);
     }
 
-    // One tile j (PAR = j & 1): the scores of tile j are in sc and its row
-    // max in mrow; K of tile j + 1 and V of tile j are resident after the
-    // barrier.  NEXT: tile j + 1 exists.
-    template <int PAR, bool NEXT>
-    __device__ __forceinline__ void step(int j, int nkt) {
-        wait_loads();
-        __syncthreads();
-        // refill the slots freed by tile j - 1: K of tile j + 2, V of tile j + 1
-        load_tile<D>(kh, krb, (j + 2) * G::BN, Sk, lds + G::KRING + PAR * G::TILE, dk, w);
-        load_tile<D>(vh, vrb, (j + 1) * G::BN, Sk, lds + G::VRING + (PAR ^ 1) * G::TILE, dv, w);
-
-        // lazy max update: move the reference point only past kTau
-        const float cand = mrow * p.c;
-        const bool up = cand > m2 + kTau;
-        const float m2n = up ? cand : m2;
-        const float alpha = exp2_fast(m2 - m2n);
-        m2 = m2n;
-        if (wave_any(up)) {
+    // VALU half of tile j: its probabilities and row sum.  The reference
+    // point m2 moves only when some lane's sum exceeds kOver, which bounds
+    // every p of that lane: then the exact row max is taken, o~ and l are
+    // rescaled and the probabilities recomputed (rare once a row's max has
+    // been seen; a NaN sum keeps its NaN, as the row is NaN anyway).
+    __device__ __forceinline__ void h1(int j) {
+        if (j > 0 && needs_mask(j)) mask(sc, j);
+        float rs = probs();
+        if (wave_any(rs > kOver)) {
+            const float m2n = fmaxf(m2, rowmax(sc) * p.c);
+            const float alpha = exp2_fast(m2 - m2n);
 #pragma unroll
             for (int db = 0; db < NDB; ++db) acc[db] *= alpha;
             l *= alpha;
-        }
-
-        // phase A: scores of tile j + 1 on the matrix cores, exponentials of
-        // the first half of tile j's keys on the VALU
-        constexpr int H1 = G::KB / 2;             // score blocks per half tile
-        constexpr int NQK = NT * G::KB;           // q.k MFMAs per tile
-        constexpr int NPV = NDB * G::NST / 2;     // P.V MFMAs per half tile
-        constexpr int kVH = 28 * H1 + 1;          // VALU per half: 16 fma, exp, add + 8 cvt per block
-        bf16x8 pf[G::NST];
-        float rs = 0.0f;
-#pragma unroll
-        for (int kb = 0; kb < H1; ++kb) {
-            rs += expblock(sc[kb]);
-            pf[2 * kb] = cvt8(sc[kb], 0);
-            pf[2 * kb + 1] = cvt8(sc[kb], 8);
-        }
-        if (NEXT) {
-            qk<PAR ^ 1>(sn);
-#pragma unroll
-            for (int i = 0; i < NQK; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x002, kVH / NQK + 1, 0);
-            }
-        }
-        // phase B1: P.V of the first half, exponentials of the rest
-        pv<PAR, 0, G::NST / 2 - 1>(pf);
-#pragma unroll
-        for (int kb = H1; kb < G::KB; ++kb) {
-            rs += expblock(sc[kb]);
-            pf[2 * kb] = cvt8(sc[kb], 0);
-            pf[2 * kb + 1] = cvt8(sc[kb], 8);
+            m2 = m2n;
+            rs = probs();
         }
         l += rs;
-        // keep these exponentials here, beside the P.V products they
-        // overlap, rather than sunk past the mask test below
-#pragma unroll
-        for (int st = G::NST / 2; st < G::NST; ++st) asm volatile("" : "+v"(pf[st]));
-        asm volatile("" : "+v"(l));
-#pragma unroll
-        for (int i = 0; i < NPV; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-            __builtin_amdgcn_sched_group_barrier(0x002, kVH / NPV + 1, 1);
+    }
+
+    // matrix half of tile j (PAR = j & 1): O^T += V^T P^T from V slot PAR,
+    // then the scores of tile j + 1 from K slot PAR ^ 1
+    template <int PAR>
+    __device__ __forceinline__ void h2() {
+        pv<PAR, 0, G::NST - 1>(pf);
+        qk<PAR ^ 1>(sc);
+    }
+
+    // the loads for tile t's matrix half: V of tile t (slot t & 1) and K of
+    // tile t + 1 (slot (t + 1) & 1)
+    __device__ __forceinline__ void dma(int t) {
+        load_tile<D>(vh, vrb, t * G::BN, Sk, lds + G::VRING + (t & 1) * G::TILE, dv, w);
+        load_tile<D>(kh, krb, (t + 1) * G::BN, Sk, lds + G::KRING + ((t + 1) & 1) * G::TILE,
+                     dk, w);
+    }
+
+    __device__ __forceinline__ void bar() {
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("s_barrier" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // The two waves of each SIMD (waves w and w + 4) run half a tile apart:
+    // group 0 does tile j's VALU half while group 1 does tile j - 1's matrix
+    // half, and the other way round, held in step by where each group puts
+    // its barriers (both execute the same number).  Tile t's loads are
+    // issued by all waves in the interval before group 0's matrix half of
+    // tile t - 1... see the schedule in block().
+    template <int GROUP, int PAR>
+    __device__ __forceinline__ void tile(int j) {
+        if (GROUP == 0) {
+            h1(j);
+            wait_loads();
+            bar();
+            dma(j + 1);
+            h2<PAR>();
+            bar();
+        } else {
+            dma(j + 1);
+            h1(j);
+            bar();
+            h2<PAR>();
+            wait_loads();
+            bar();
         }
-        if (NEXT && needs_mask(j + 1)) mask(sn, j + 1);
-        // phase B2: P.V of the second half, row max of tile j + 1
-        pv<PAR, G::NST / 2, G::NST - 1>(pf);
-        if (NEXT) {
-            mrow = rowmax(sn);
-#pragma unroll
-            for (int i = 0; i < NPV; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);
-                __builtin_amdgcn_sched_group_barrier(0x002, (8 * G::KB + 4) / NPV + 1, 2);
-            }
-#pragma unroll
-            for (int kb = 0; kb < G::KB; ++kb) sc[kb] = sn[kb];
+    }
+
+    template <int GROUP>
+    __device__ __forceinline__ void tiles(int nkt) {
+        if (GROUP == 1) bar();
+        int j = 0;
+        for (; j + 1 < nkt; j += 2) {
+            tile<GROUP, 0>(j);
+            tile<GROUP, 1>(j + 1);
         }
+        if (j < nkt) tile<GROUP, 0>(j);
+        if (GROUP == 0) bar();
     }
 
     __device__ __forceinline__ void run() {
@@ -476,28 +515,19 @@ struct Kernel {
 #pragma unroll
         for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
 
-        // prologue: K of tiles 0 and 1, V of tile 0; scores and max of tile 0
+        // prologue: K of tile 0 (slot 0), then tile 0's loads (V 0, K 1);
+        // every wave forms the scores of tile 0 and starts its reference
+        // point at their row max
         load_tile<D>(kh, krb, 0, Sk, lds + G::KRING, dk, w);
-        load_tile<D>(kh, krb, G::BN, Sk, lds + G::KRING + G::TILE, dk, w);
-        load_tile<D>(vh, vrb, 0, Sk, lds + G::VRING, dv, w);
+        dma(0);
         wait_loads();
-        __syncthreads();
+        bar();
         qk<0>(sc);
         if (needs_mask(0)) mask(sc, 0);
-        mrow = rowmax(sc);
+        m2 = rowmax(sc) * p.c;
 
-        int j = 0;
-        for (; j + 2 < nkt; j += 2) {
-            step<0, true>(j, nkt);
-            step<1, true>(j + 1, nkt);
-        }
-        if (j + 1 < nkt) {
-            step<0, true>(j, nkt);
-            ++j;
-            step<1, false>(j, nkt);
-        } else {
-            step<0, false>(j, nkt);
-        }
+        if (w < kWaves / 2) tiles<0>(nkt);
+        else tiles<1>(nkt);
         wait_loads();
 
         // epilogue: o = o~ / l, lse = (m2 + log2 l) ln 2
