@@ -16,7 +16,7 @@
  * FlashAttention" §7 (the loop over K/V tiles that never writes the score
  * matrix to memory).  The score matrix is never stored: each workgroup
  * keeps 256 query rows in registers, streams K and V tiles of 64 keys
- * (128 at D = 64 and 32) through LDS, and carries (m, l, o~) per row.
+ * (128 at D = 32) through LDS, and carries (m, l, o~) per row.
  *
  * Arithmetic: Q, K, V are bfloat16; q.k and P.V are bf16 matrix-core
  * products with fp32 accumulation; the softmax state is fp32.  The
