@@ -79,23 +79,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
-template <int I>
-struct IC {
-    static constexpr int value = I;
-};
-template <int I, int N, class F>
-__device__ __forceinline__ void static_for_impl(F &&f) {
-    if constexpr (I < N) {
-        f(IC<I>{});
-        static_for_impl<I + 1, N>(f);
-    }
-}
-template <int N, class F>
-__device__ __forceinline__ void static_for(F &&f) {
-    static_for_impl<0, N>(f);
-}
-typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
-typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
 typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -400,9 +383,10 @@ struct Kernel {
     // The two waves of each SIMD (waves w and w + 4) run half a tile apart:
     // group 0 does tile j's VALU half while group 1 does tile j - 1's matrix
     // half, and the other way round, held in step by where each group puts
-    // its barriers (both execute the same number).  Tile t's loads are
-    // issued by all waves in the interval before group 0's matrix half of
-    // tile t - 1... see the schedule in block().
+    // its barriers (both execute the same number).  The loads of tile j + 1
+    // (V of tile j + 1, K of tile j + 2) are issued in the interval in which
+    // group 0 does tile j's matrix half and group 1 its VALU half, and every
+    // wave has waited for them before the barrier that ends the next one.
     template <int GROUP, int PAR>
     __device__ __forceinline__ void tile(int j) {
         if (GROUP == 0) {
