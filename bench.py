@@ -88,12 +88,16 @@ def algorithmic_bytes(w, path, n_stats, op="softmax", causal=None):
 
 
 def measure(w, steps, warmup, path="auto", rotate=True, graph=False,
-            op="softmax", causal=None, streams=1):
-    """Average device time per step (ms), the rotation depth, and the host
-    time per launch (us).  Steps cycle over R buffer sets; with graph=True
-    the launches are captured once in a HIP graph and replayed.  With
-    streams=2 consecutive steps alternate between two default-priority
-    streams, so one step's launch can start while the previous one drains."""
+            op="softmax", causal=None, streams=1, trials=0):
+    """Average device time per step (ms), the rotation depth, the host time
+    per launch (us), and the spread of the launch time (or None).  Steps
+    cycle over R buffer sets; with graph=True the launches are captured
+    once in a HIP graph and replayed.  With streams=2 consecutive steps
+    alternate between two default-priority streams, so one step's launch
+    can start while the previous one drains.  With trials > 0 (plain
+    launches on one stream) that many further runs of up to 50 launches,
+    each between its own pair of events, follow the timed steps; their
+    per-launch times give the p10 / p50 / p90 spread."""
     import numpy as np
     import torch
     import row_wise_online_amd as rw
@@ -154,6 +158,7 @@ def measure(w, steps, warmup, path="auto", rotate=True, graph=False,
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     strm = [torch.cuda.current_stream()] + extra_streams
+    dist = None
     if not graph:
         calls = prepared()
         for i in range(warmup):
@@ -174,6 +179,23 @@ def measure(w, steps, warmup, path="auto", rotate=True, graph=False,
         end.synchronize()
         torch.cuda.synchronize()
         ms = start.elapsed_time(end) / steps
+        if trials and len(strm) == 1:
+            per = max(1, min(steps, 50))
+            evs = [(torch.cuda.Event(enable_timing=True),
+                    torch.cuda.Event(enable_timing=True))
+                   for _ in range(trials)]
+            k = 0
+            for a, b in evs:
+                a.record(strm[0])
+                for _ in range(per):
+                    calls[k % R]()
+                    k += 1
+                b.record(strm[0])
+            torch.cuda.synchronize()
+            us = sorted(a.elapsed_time(b) / per * 1e3 for a, b in evs)
+            q = lambda f: round(us[int(f * (len(us) - 1) + 0.5)], 3)
+            dist = {"trials": trials, "launches_each": per,
+                    "us_p10": q(0.1), "us_p50": q(0.5), "us_p90": q(0.9)}
     else:
         per_graph = R * max(1, 32 // R)
         g = torch.cuda.CUDAGraph()
@@ -197,7 +219,7 @@ def measure(w, steps, warmup, path="auto", rotate=True, graph=False,
         ms = start.elapsed_time(end) / (reps * per_graph)
         del g
     del xs, ys
-    return ms, R, host_us
+    return ms, R, host_us, dist
 
 
 def copy_ceiling(nbytes, steps=50):
@@ -291,12 +313,13 @@ def run_workload(name, steps, warmup, path="auto", want_cpu=True,
         n_stats = 3
     if causal is not None and op == "cross_entropy":
         raise ValueError("the causal mask applies to softmax / log-softmax")
-    ms, R, host_us = measure(w, steps, warmup, path, op=op, causal=causal)
+    ms, R, host_us, dist = measure(w, steps, warmup, path, op=op,
+                                   causal=causal, trials=20 if extras else 0)
     if extras:
-        graph_ms, _, _ = measure(w, steps, warmup, path, graph=True, op=op,
-                                 causal=causal)
-        warm_ms, _, _ = measure(w, max(10, steps // 4), 3, path,
-                                rotate=False, op=op, causal=causal)
+        graph_ms, _, _, _ = measure(w, steps, warmup, path, graph=True, op=op,
+                                    causal=causal)
+        warm_ms, _, _, _ = measure(w, max(10, steps // 4), 3, path,
+                                   rotate=False, op=op, causal=causal)
     nbytes = algorithmic_bytes(w, resolved, n_stats, op, causal)
     gbs = nbytes / (ms * 1e-3) / 1e9
     eff = (2 * w.M * w.N * w.esize + 4 * w.M * n_stats) / (ms * 1e-3) / 1e9
@@ -345,6 +368,8 @@ def run_workload(name, steps, warmup, path="auto", want_cpu=True,
         "kernel_source": kernel_source_hash(),
     }
     if extras:
+        if dist is not None:
+            rec["per_launch_us"] = dist
         rec["warm_cache_GBps"] = round(nbytes / (warm_ms * 1e-3) / 1e9, 1)
         rec["graph_replay_GBps"] = round(nbytes / (graph_ms * 1e-3) / 1e9, 1)
         if op in ("softmax", "log_softmax") and causal is None and \
@@ -355,7 +380,7 @@ def run_workload(name, steps, warmup, path="auto", want_cpu=True,
             w2 = wl.WORKLOADS[name]
             w2 = type(w2)(w2.name, w2.M, w2.N, w2.dtype, w2.seed, ("y",),
                           w2.desc)
-            ms2, _, _ = measure(w2, steps, warmup, path, op=op, streams=2)
+            ms2, _, _, _ = measure(w2, steps, warmup, path, op=op, streams=2)
             b2 = algorithmic_bytes(w2, resolved, 0, op)
             rec["two_stream"] = {
                 "GBps": round(b2 / (ms2 * 1e-3) / 1e9, 1),
