@@ -243,6 +243,42 @@ def copy_ceiling(nbytes, steps=50):
     return 2 * nbytes / (ms * 1e-3) / 1e9
 
 
+def host_threads():
+    """Host cores this process may run on, at most 16 (one GPU's share)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def cpu_baseline_parallel(w, n_stats, budget_s):
+    """The same fp64 softmax oracle called on T row blocks at once from T
+    host threads (the C call releases the interpreter lock), until about
+    budget_s seconds have passed: the oracle's rate on the host's cores."""
+    from concurrent.futures import ThreadPoolExecutor
+    import oracle
+    from row_wise_online_amd import workloads as wl
+    x = wl.generate(w.name)
+    T = min(host_threads(), w.M)
+    blocks = [x[i * w.M // T:(i + 1) * w.M // T] for i in range(T)]
+    b = 2 * w.M * w.N * w.esize + 4 * w.M * n_stats
+    with ThreadPoolExecutor(T) as ex:
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            list(ex.map(oracle.softmax, blocks))
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= budget_s or reps >= 256:
+                break
+    per = el / reps
+    return {"value": round(b / per / 1e9, 4), "unit": "GB/s", "cores": T,
+            "kind": "oracle", "rows_per_s": round(w.M / per, 1),
+            "sample": f"{reps} x full {w.M}x{w.N} {w.dtype} matrix, fp64 "
+                      f"three-pass softmax oracle on {T} row blocks from "
+                      f"{T} threads, {el:.1f} s"}
+
+
 def cpu_baseline(w, n_stats, budget_s, op="softmax", causal=None):
     """The fp64 oracle, as it is, on this host: whole input matrices of the
     workload, repeated until about budget_s seconds have passed."""
@@ -393,6 +429,9 @@ def run_workload(name, steps, warmup, path="auto", want_cpu=True,
         copy_ceiling(w.M * w.N * w.esize), 1)
     if want_cpu:
         rec["cpu_baseline"] = cpu_baseline(w, n_stats, cpu_budget, op, causal)
+        if op == "softmax" and causal is None and host_threads() > 1:
+            rec["cpu_baseline_parallel"] = cpu_baseline_parallel(
+                w, n_stats, cpu_budget / 2)
     return rec
 
 
