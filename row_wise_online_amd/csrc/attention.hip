@@ -42,9 +42,12 @@
 // intervals: in interval 2j group 0 does tile j's VALU half and group 1 tile
 // j - 1's matrix half; in interval 2j + 1 group 0 does tile j's matrix half
 // and group 1 tile j's VALU half.  The loads for tile t's matrix half (V of
-// tile t, K of tile t + 1) are issued by every wave at the start of interval
-// 2t - 1 and waited for before the barrier that opens interval 2t + 1; their
-// ring slot was last read in interval 2t - 2.
+// tile t, K of tile t + 1) are issued at the start of interval 2t - 1 and
+// waited for before the barrier that opens interval 2t + 1; their ring slot
+// was last read in interval 2t - 2.  At d = 128 every wave issues its share.
+// At d = 64 and 32, where the VALU half is the longer one, group 0 issues
+// its partners' shares too, so that group 1's VALU half carries no load
+// issue (each load instruction holds its wave for tens of cycles).
 //
 // Online state in base 2: t = s c with c = scale log2(e).  Each row starts
 // its reference point m2 at the max of its first tile; later it moves only
@@ -368,6 +371,22 @@ struct Kernel {
 
     // the loads for tile t's matrix half: V of tile t (slot t & 1) and K of
     // tile t + 1 (slot (t + 1) & 1)
+    // the same loads for wave w and its partner w + kWaves / 2 (issued by
+    // group 0 alone at d = 64 and 32).  The partner's rows lie kWaves / 2 RPB
+    // (a multiple of 16) rows further down, which leaves the swizzle alone,
+    // so its per-lane offsets are this wave's plus that many rows.
+    static constexpr bool kGroup0Loads = D != 128;
+    __device__ __forceinline__ void dma_pair(int t) {
+        constexpr int hw = kWaves / 2;
+        lds_char *vdst = lds + G::VRING + (t & 1) * G::TILE;
+        lds_char *kdst = lds + G::KRING + ((t + 1) & 1) * G::TILE;
+        load_tile<D>(vh, vrb, t * G::BN, Sk, vdst, dv, w);
+        load_tile<D>(vh, vrb, t * G::BN, Sk, vdst, dv + uint32_t(hw * G::RPB * vrb), w + hw);
+        load_tile<D>(kh, krb, (t + 1) * G::BN, Sk, kdst, dk, w);
+        load_tile<D>(kh, krb, (t + 1) * G::BN, Sk, kdst, dk + uint32_t(hw * G::RPB * krb),
+                     w + hw);
+    }
+
     __device__ __forceinline__ void dma(int t) {
         load_tile<D>(vh, vrb, t * G::BN, Sk, lds + G::VRING + (t & 1) * G::TILE, dv, w);
         load_tile<D>(kh, krb, (t + 1) * G::BN, Sk, lds + G::KRING + ((t + 1) & 1) * G::TILE,
@@ -385,19 +404,21 @@ struct Kernel {
     // half, and the other way round, held in step by where each group puts
     // its barriers (both execute the same number).  The loads of tile j + 1
     // (V of tile j + 1, K of tile j + 2) are issued in the interval in which
-    // group 0 does tile j's matrix half and group 1 its VALU half, and every
-    // wave has waited for them before the barrier that ends the next one.
+    // group 0 does tile j's matrix half and group 1 its VALU half (by group
+    // 0 alone at d = 64 and 32), and every wave has waited for its own
+    // before the barrier that ends the next one.
     template <int GROUP, int PAR>
     __device__ __forceinline__ void tile(int j) {
         if (GROUP == 0) {
             h1(j);
             wait_loads();
             bar();
-            dma(j + 1);
+            if (kGroup0Loads) dma_pair(j + 1);
+            else dma(j + 1);
             h2<PAR>();
             bar();
         } else {
-            dma(j + 1);
+            if (!kGroup0Loads) dma(j + 1);
             h1(j);
             bar();
             h2<PAR>();
