@@ -10,8 +10,9 @@
 // i} of the n query blocks, so every workgroup has the same work); each
 // wave owns 32 rows, and each K/V tile in LDS feeds all 8.  At up to ~240
 // VGPRs two waves fit per SIMD, i.e. one workgroup per CU.  K and V tiles of
-// 64 keys (128 at d = 32) stream through LDS rings of two tiles each, filled
-// by direct-to-LDS buffer loads (buffer_load_dwordx4 ... lds): no VGPR
+// 64 keys (128 at d = 32) stream through LDS rings (three tiles each at
+// d = 128, two at d = 64 and 32: 96 or 32 KiB), filled by direct-to-LDS
+// buffer loads (buffer_load_dwordx4 ... lds): no VGPR
 // staging, and lanes past the last key read as zero because each tile's
 // buffer descriptor covers only the keys that exist.
 //
@@ -42,12 +43,17 @@
 // intervals: in interval 2j group 0 does tile j's VALU half and group 1 tile
 // j - 1's matrix half; in interval 2j + 1 group 0 does tile j's matrix half
 // and group 1 tile j's VALU half.  The loads for tile t's matrix half (V of
-// tile t, K of tile t + 1) are issued at the start of interval 2t - 1 and
-// waited for before the barrier that opens interval 2t + 1; their ring slot
-// was last read in interval 2t - 2.  At d = 128 every wave issues its share.
-// At d = 64 and 32, where the VALU half is the longer one, group 0 issues
-// its partners' shares too, so that group 1's VALU half carries no load
-// issue (each load instruction holds its wave for tens of cycles).
+// tile t, K of tile t + 1) are waited for before the barrier that opens
+// interval 2t + 1; each load instruction holds its wave for tens of cycles,
+// so they go into the shorter half of an interval.
+//   d = 128 (the matrix half is the longer one): rings of three tiles; each
+//     group issues its share with its VALU half of tile t - 1, group 0 in
+//     interval 2t - 2 and group 1 in interval 2t - 1.  The slot of tile t
+//     was last read (by tile t - 3) in interval 2t - 4.
+//   d = 64 and 32 (the VALU half is the longer one): rings of two tiles;
+//     group 0 issues both groups' shares at the start of its matrix half of
+//     tile t - 1, in interval 2t - 1.  The slot was last read in interval
+//     2t - 2.
 //
 // Online state in base 2: t = s c with c = scale log2(e).  Each row starts
 // its reference point m2 at the max of its first tile; later it moves only
@@ -109,8 +115,9 @@ struct Geo {
     static constexpr int CPR = D / 8;                   // 16-byte chunks per row
     static constexpr int RPB = 1024 / RB;               // rows per 1 KB wave load
     static constexpr int NDMA = TILE / 1024 / kWaves;   // wave loads per tile
-    static constexpr int kLdsBytes = 4 * TILE;          // K ring (2) + V ring (2)
-    static constexpr int KRING = 0, VRING = 2 * TILE;
+    static constexpr int NSLOT = D == 128 ? 3 : 2;      // tiles per ring
+    static constexpr int kLdsBytes = 2 * NSLOT * TILE;  // V ring, then K ring
+    static constexpr int VRING = 0, KRING = NSLOT * TILE;
     // a row is 16 (d = 128), 8 (d = 64) or 4 (d = 32) chunks; a 16-lane
     // group of a K operand read covers 16 consecutive rows, a 32-lane group
     // of a V transpose read 4 consecutive rows of 64 bytes
@@ -237,11 +244,12 @@ struct Kernel {
 
     // S^T = K Q^T for the tile in K-ring slot KBUF.  The K operands are read
     // by inline asm PF operands ahead of their product, with explicit
-    // lgkmcnt waits (as for the V reads below).
+    // lgkmcnt waits (as for the V reads below).  koff holds KRING, which
+    // keeps the immediate offset below 64 KiB.
     template <int KBUF, int I>
     __device__ __forceinline__ void k_issue(u32x4 *kf, uint32_t base) const {
         constexpr int t = I / G::KB, kb = I % G::KB;
-        constexpr int off = G::KRING + KBUF * G::TILE + kb * 32 * G::RB;
+        constexpr int off = KBUF * G::TILE + kb * 32 * G::RB;
         asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(kf[I]) : "v"(base + koff[t]), "n"(off));
     }
 
@@ -361,16 +369,16 @@ struct Kernel {
         l += rs;
     }
 
-    // matrix half of tile j (PAR = j & 1): O^T += V^T P^T from V slot PAR,
-    // then the scores of tile j + 1 from K slot PAR ^ 1
+    // matrix half of tile j (PAR = j mod NSLOT): O^T += V^T P^T from V slot
+    // PAR, then the scores of tile j + 1 from the next K slot
     template <int PAR>
     __device__ __forceinline__ void h2() {
         pv<PAR, 0, G::NST - 1>(pf);
-        qk<PAR ^ 1>(sc);
+        qk<(PAR + 1) % G::NSLOT>(sc);
     }
 
-    // the loads for tile t's matrix half: V of tile t (slot t & 1) and K of
-    // tile t + 1 (slot (t + 1) & 1)
+    // the loads for tile t's matrix half: V of tile t (slot t mod NSLOT)
+    // and K of tile t + 1 (slot (t + 1) mod NSLOT)
     // the same loads for wave w and its partner w + kWaves / 2 (issued by
     // group 0 alone at d = 64 and 32).  The partner's rows lie kWaves / 2 RPB
     // (a multiple of 16) rows further down, which leaves the swizzle alone,
@@ -378,8 +386,8 @@ struct Kernel {
     static constexpr bool kGroup0Loads = D != 128;
     __device__ __forceinline__ void dma_pair(int t) {
         constexpr int hw = kWaves / 2;
-        lds_char *vdst = lds + G::VRING + (t & 1) * G::TILE;
-        lds_char *kdst = lds + G::KRING + ((t + 1) & 1) * G::TILE;
+        lds_char *vdst = lds + G::VRING + (t % G::NSLOT) * G::TILE;
+        lds_char *kdst = lds + G::KRING + ((t + 1) % G::NSLOT) * G::TILE;
         load_tile<D>(vh, vrb, t * G::BN, Sk, vdst, dv, w);
         load_tile<D>(vh, vrb, t * G::BN, Sk, vdst, dv + uint32_t(hw * G::RPB * vrb), w + hw);
         load_tile<D>(kh, krb, (t + 1) * G::BN, Sk, kdst, dk, w);
@@ -388,9 +396,9 @@ struct Kernel {
     }
 
     __device__ __forceinline__ void dma(int t) {
-        load_tile<D>(vh, vrb, t * G::BN, Sk, lds + G::VRING + (t & 1) * G::TILE, dv, w);
-        load_tile<D>(kh, krb, (t + 1) * G::BN, Sk, lds + G::KRING + ((t + 1) & 1) * G::TILE,
-                     dk, w);
+        load_tile<D>(vh, vrb, t * G::BN, Sk, lds + G::VRING + (t % G::NSLOT) * G::TILE, dv, w);
+        load_tile<D>(kh, krb, (t + 1) * G::BN, Sk,
+                     lds + G::KRING + ((t + 1) % G::NSLOT) * G::TILE, dk, w);
     }
 
     __device__ __forceinline__ void bar() {
@@ -403,13 +411,22 @@ struct Kernel {
     // group 0 does tile j's VALU half while group 1 does tile j - 1's matrix
     // half, and the other way round, held in step by where each group puts
     // its barriers (both execute the same number).  The loads of tile j + 1
-    // (V of tile j + 1, K of tile j + 2) are issued in the interval in which
-    // group 0 does tile j's matrix half and group 1 its VALU half (by group
-    // 0 alone at d = 64 and 32), and every wave has waited for its own
-    // before the barrier that ends the next one.
+    // (V of tile j + 1, K of tile j + 2) go with each group's VALU half of
+    // tile j at d = 128, with group 0's matrix half of tile j at d = 64 and
+    // 32 (both groups' shares); every wave has waited for its own before the
+    // barrier that opens interval 2j + 3.
     template <int GROUP, int PAR>
     __device__ __forceinline__ void tile(int j) {
-        if (GROUP == 0) {
+        if (GROUP == 0 && G::NSLOT == 3) {
+            dma(j + 1);
+            h1(j);
+            // tile j's loads (issued an interval earlier) have landed; tile
+            // j + 1's may still be in flight
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * G::NDMA) : "memory");
+            bar();
+            h2<PAR>();
+            bar();
+        } else if (GROUP == 0) {
             h1(j);
             wait_loads();
             bar();
@@ -431,11 +448,21 @@ struct Kernel {
     __device__ __forceinline__ void tiles(int nkt) {
         if (GROUP == 1) bar();
         int j = 0;
-        for (; j + 1 < nkt; j += 2) {
-            tile<GROUP, 0>(j);
-            tile<GROUP, 1>(j + 1);
+        if constexpr (G::NSLOT == 3) {
+            for (; j + 2 < nkt; j += 3) {
+                tile<GROUP, 0>(j);
+                tile<GROUP, 1>(j + 1);
+                tile<GROUP, 2>(j + 2);
+            }
+            if (j < nkt) tile<GROUP, 0>(j);
+            if (j + 1 < nkt) tile<GROUP, 1>(j + 1);
+        } else {
+            for (; j + 1 < nkt; j += 2) {
+                tile<GROUP, 0>(j);
+                tile<GROUP, 1>(j + 1);
+            }
+            if (j < nkt) tile<GROUP, 0>(j);
         }
-        if (j < nkt) tile<GROUP, 0>(j);
         if (GROUP == 0) bar();
     }
 
@@ -470,7 +497,7 @@ struct Kernel {
         // chunk 2 t + half of row 32 kb + l32 sits in slot (2 t + half) ^ fk(l32)
 #pragma unroll
         for (int t = 0; t < NT; ++t)
-            koff[t] = uint32_t(l32 * G::RB + 16 * ((2 * t + half) ^ G::fk(l32)));
+            koff[t] = uint32_t(G::KRING + l32 * G::RB + 16 * ((2 * t + half) ^ G::fk(l32)));
         const int vrow = 4 * half + (g16 >> 2);
         const int x = 2 * grp + ((g16 & 3) >> 1);
 #pragma unroll
