@@ -48,6 +48,8 @@ def kernel_source_hash(family="softmax"):
     for p in sorted(glob.glob(os.path.join(ROOT, "row_wise_online_amd",
                                            "csrc", "*"))):
         name = os.path.basename(p)
+        if os.path.splitext(name)[1] not in (".hip", ".hpp", ".h"):
+            continue  # sources only, not compiler temporaries
         is_attn = name.startswith("attention")
         if family == "softmax" and is_attn:
             continue
