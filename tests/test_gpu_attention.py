@@ -149,7 +149,8 @@ def test_causal_offsets(causal):
 
 
 @pytest.mark.parametrize("Sq,Sk", [(1, 1), (1, 64), (1, 65), (31, 7), (129, 1),
-                                   (128, 64), (257, 200), (64, 1000), (5, 4097)])
+                                   (128, 64), (70, 192), (257, 200), (64, 1000),
+                                   (5, 4097)])
 @pytest.mark.parametrize("D", [32, 64, 128])
 def test_ragged_shapes(Sq, Sk, D):
     q, k, v = wl.attention_inputs(1, 1, Sq, Sk, D, seed=Sq * 7 + Sk)
