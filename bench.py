@@ -401,7 +401,11 @@ def run_workload(name, steps, warmup, path="auto", want_cpu=True,
             "traffic": traffic_record(name) if (op == "softmax" and
                                             causal is None) else None,
             "algorithmic_bytes_per_launch": nbytes,
-            "kernel_launches_per_step": 1 if resolved != "split" else 3,
+            # split: partial states, then the normalise (or, for
+            # statistics and cross-entropy, the state merge); the
+            # cross-entropy adds its mean
+            "kernel_launches_per_step": (2 if resolved == "split" else 1) +
+                                        (1 if op == "cross_entropy" else 0),
         },
         "kernel_source": kernel_source_hash(),
     }

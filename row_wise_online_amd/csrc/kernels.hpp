@@ -428,12 +428,19 @@ __global__ __launch_bounds__(kWave *WAVES) void split_partial_kernel(
     }
 }
 
+// The normalise pass of the split path, with the second-level merge folded
+// in: every wavefront first merges the row's P partial states (lane k
+// folds states k, k + 64, ... with the pairwise merge, then the wavefront
+// merge), the same order state_merge_kernel uses, so every workgroup of the
+// row gets the same state bit for bit.  P is at most a few hundred, so the
+// merge is a few loads per lane; it saves the merge launch.  The row's first
+// workgroup writes the requested row statistics.
 template <class Tr, bool VEC, int WAVES, int U, Out OUT, class Pol = StreamingNT,
           bool MASKED = false>
 __global__ __launch_bounds__(kWave *WAVES) void split_normalize_kernel(
     const typename Tr::elem_t *x, int64_t ldx, typename Tr::elem_t *y,
-    int64_t ldy, int N, int P, int C, const float *row_m,
-    const float *row_d, Mask mk) {
+    int64_t ldy, int N, int P, int C, const float *part_m,
+    const float *part_d, StatsOut so, Mask mk) {
     using T = Tiles<Tr, VEC, WAVES, U, Pol::nt2, Pol::nts>;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
@@ -443,7 +450,11 @@ __global__ __launch_bounds__(kWave *WAVES) void split_normalize_kernel(
     const int c0 = p * C;
     const int n = min(C, N - c0);
     const int nl = min(n, valid_cols<MASKED>(mk, row, N) - c0);
-    const State st{row_m[row], row_d[row]};
+    float m = kNegInf, d = 0.0f;
+    for (int k = lane; k < P; k += kWave) merge_into(m, d, part_m[row * P + k], part_d[row * P + k]);
+    const State st = wave_merge(m, d);
+    if (p == 0 && threadIdx.x == 0)
+        write_row_stats<Tr, false>(so, row, st, Target<Tr>{-1, typename Tr::elem_t(0)}, N);
     T::template normalize<OUT, Pol::rev>(x + row * ldx + c0, y + row * ldy + c0,
                                          nl, n, wave * kWave + lane, st);
 }

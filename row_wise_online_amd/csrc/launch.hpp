@@ -53,8 +53,9 @@ struct SplitPlan {
 SplitPlan split_plan(int64_t M, int64_t N);
 size_t split_workspace_bytes(int64_t M, int64_t N);
 
-// Split path: partial states into ws, state merge (row statistics and
-// cross-entropy), then (unless Mode::Stats) the normalise kernel.
+// Split path: partial states into ws; then, for statistics alone (and the
+// cross-entropy), the state-merge kernel, and for softmax / log-softmax the
+// normalise kernel, which merges the row's partial states itself.
 void launch_split(const FwdArgs &a, void *ws);
 
 // Second-level state merge of K fp32 states per row (no cross-entropy):

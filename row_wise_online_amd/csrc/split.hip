@@ -1,5 +1,6 @@
-// Split-row path (partial states -> state merge -> normalise), the public
-// state-merge launcher and the cross-entropy mean.
+// Split-row path (partial states -> state merge, alone for statistics or
+// folded into the normalise kernel), the public state-merge launcher and the
+// cross-entropy mean.
 #include "kernels.hpp"
 #include "launch.hpp"
 
@@ -55,34 +56,36 @@ void run(const FwdArgs &a, void *ws) {
     split_partial_kernel<Tr, VEC, kSplitWaves, U, Pol, MK><<<grid, block, 0, a.stream>>>(
         x, a.ldx, a.N, plan.P, plan.C, l.part_m, l.part_d, mk);
 
-    // Row states go to the workspace (read by the normalise kernel) and to
-    // whichever of the caller's m / d / lse / cross-entropy are asked for,
-    // in one merge launch.
     const StatsOut so{a.m_out, a.d_out, a.lse_out, a.inc_out, a.labels, a.loss,
                       a.accumulate};
-    const dim3 mgrid(static_cast<unsigned>((a.M + kMergeRows - 1) / kMergeRows));
-    const dim3 mblock(kWave * kMergeRows);
-    if (a.labels) {
-        state_merge_kernel<kMergeRows, Tr, true><<<mgrid, mblock, 0, a.stream>>>(
-            l.part_m, l.part_d, plan.P, a.M, plan.P, l.row_m, l.row_d, 1, so,
-            x, a.ldx, a.N);
-    } else {
-        state_merge_kernel<kMergeRows, Tr, false><<<mgrid, mblock, 0, a.stream>>>(
-            l.part_m, l.part_d, plan.P, a.M, plan.P, l.row_m, l.row_d, 1, so,
-            x, a.ldx, a.N);
+    if (a.mode == Mode::Stats) {
+        // statistics alone: the row states go to whichever of the caller's
+        // m / d / lse / cross-entropy are asked for, in one merge launch
+        const dim3 mgrid(static_cast<unsigned>((a.M + kMergeRows - 1) / kMergeRows));
+        const dim3 mblock(kWave * kMergeRows);
+        if (a.labels) {
+            state_merge_kernel<kMergeRows, Tr, true><<<mgrid, mblock, 0, a.stream>>>(
+                l.part_m, l.part_d, plan.P, a.M, plan.P, l.row_m, l.row_d, 1, so,
+                x, a.ldx, a.N);
+        } else {
+            state_merge_kernel<kMergeRows, Tr, false><<<mgrid, mblock, 0, a.stream>>>(
+                l.part_m, l.part_d, plan.P, a.M, plan.P, l.row_m, l.row_d, 1, so,
+                x, a.ldx, a.N);
+        }
+        return;
     }
 
-    if (a.mode != Mode::Stats) {
-        E *y = static_cast<E *>(a.y);
-        if (a.mode == Mode::Prob) {
-            split_normalize_kernel<Tr, VEC, kSplitWaves, U, Out::Prob, Pol, MK>
-                <<<grid, block, 0, a.stream>>>(x, a.ldx, y, a.ldy, a.N, plan.P,
-                                               plan.C, l.row_m, l.row_d, mk);
-        } else {
-            split_normalize_kernel<Tr, VEC, kSplitWaves, U, Out::LogProb, Pol, MK>
-                <<<grid, block, 0, a.stream>>>(x, a.ldx, y, a.ldy, a.N, plan.P,
-                                               plan.C, l.row_m, l.row_d, mk);
-        }
+    // softmax / log-softmax: the normalise kernel merges the partial states
+    // itself and writes the requested statistics
+    E *y = static_cast<E *>(a.y);
+    if (a.mode == Mode::Prob) {
+        split_normalize_kernel<Tr, VEC, kSplitWaves, U, Out::Prob, Pol, MK>
+            <<<grid, block, 0, a.stream>>>(x, a.ldx, y, a.ldy, a.N, plan.P, plan.C,
+                                           l.part_m, l.part_d, so, mk);
+    } else {
+        split_normalize_kernel<Tr, VEC, kSplitWaves, U, Out::LogProb, Pol, MK>
+            <<<grid, block, 0, a.stream>>>(x, a.ldx, y, a.ldy, a.N, plan.P, plan.C,
+                                           l.part_m, l.part_d, so, mk);
     }
 }
 
