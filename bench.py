@@ -343,7 +343,7 @@ def run_workload(name, steps, warmup, path="auto", want_cpu=True,
     import row_wise_online_amd as rw
     from row_wise_online_amd import workloads as wl
     w = wl.WORKLOADS[name]
-    resolved = rw.select_path(w.M, w.N, w.dtype) if path == "auto" else path
+    resolved = rw.select_path(w.M, w.N, w.dtype, op=op) if path == "auto" else path
     n_stats = len(set(w.outputs) & {"m", "d", "lse"})
     if op == "cross_entropy":
         n_stats = 0

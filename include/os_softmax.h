@@ -85,10 +85,14 @@ typedef enum { OS_F32 = 0, OS_BF16 = 1 } os_dtype;
  *  STREAM:   one workgroup per row; pass 1 streams the row folding (m, d),
  *            pass 2 re-reads it and writes y (two reads + one write).  Any N.
  *            For statistics and cross-entropy: pass 1 only (one read).
- *  SPLIT:    several workgroups per row: a partial-state kernel, the
- *            state-merge kernel, and a normalise kernel (§7.1 of the same
- *            page names this two-stage scheme for few, very long rows).
- *  AUTO:     choose by shape (os_softmax_select_path). */
+ *  SPLIT:    several workgroups per row: a partial-state kernel, then a
+ *            normalise kernel whose workgroups first merge their row's
+ *            partial states (for statistics and cross-entropy, the
+ *            state-merge kernel instead); §7.1 of the same page names this
+ *            two-stage scheme for few, very long rows.
+ *  AUTO:     choose by shape: os_softmax_select_path for the softmax and
+ *            log-softmax entry points, os_softmax_stats_select_path for
+ *            the statistics and cross-entropy ones. */
 typedef enum {
     OS_PATH_AUTO = 0,
     OS_PATH_RESIDENT = 1,
@@ -234,9 +238,18 @@ os_status os_state_merge(const float *m_in, const float *d_in, int64_t ld_in,
 size_t os_softmax_workspace_bytes(int64_t M, int64_t N, os_dtype dt,
                                   os_path path);
 
-/* The path AUTO resolves to at this shape, for every row-wise entry point
- * (host only). */
+/* The path AUTO resolves to at this shape for the softmax and log-softmax
+ * entry points, masked or not (host only).  OS_PATH_AUTO for an invalid
+ * shape or dtype. */
 os_path os_softmax_select_path(int64_t M, int64_t N, os_dtype dt);
+
+/* The path AUTO resolves to for the read-only entry points
+ * (os_softmax_stats*, os_softmax_stats_update, os_cross_entropy_fwd*):
+ * that of os_softmax_select_path, except that with 512 rows or more, rows
+ * longer than 16384 elements take STREAM rather than RESIDENT (nothing is
+ * kept for a pass 2).  The workspace size is the same either way (host
+ * only; OS_PATH_AUTO for an invalid shape or dtype). */
+os_path os_softmax_stats_select_path(int64_t M, int64_t N, os_dtype dt);
 
 /* Static description of a status code (never NULL). */
 const char *os_status_string(os_status s);

@@ -16,7 +16,7 @@ Same names as the C ABI, without the ``os_`` prefix:
 * ``softmax_stats(x, m, d, lse=None, inc=1, ws=None, path="auto")``
 * ``softmax_stats_update(x, m, d, lse=None, inc=1, ws=None, path="auto")``
 * ``state_merge(m_in, d_in, m_out, d_out, lse_out=None)``
-* ``workspace_bytes(M, N, dtype, path="auto")``, ``select_path(M, N, dtype)``
+* ``workspace_bytes(M, N, dtype, path="auto")``, ``select_path(M, N, dtype, op)``
 * ``attention_fwd(q, k, v, o=None, lse=None, scale=None, causal_offset=-1)``
   (``include/os_attention.h``), and ``prepare_attention`` for launch loops
 """
@@ -102,9 +102,13 @@ def workspace_bytes(M, N, dtype, path="auto"):
         M, N, _dtype_code_any(dtype), _path_code(path))
 
 
-def select_path(M, N, dtype):
-    return _lib.PATH_NAMES[_lib.load().os_softmax_select_path(
-        M, N, _dtype_code_any(dtype))]
+def select_path(M, N, dtype, op="softmax"):
+    """The path AUTO takes at this shape: for softmax / log-softmax, or,
+    with op "stats" or "cross_entropy", for the read-only entry points."""
+    fn = ("os_softmax_stats_select_path" if op in ("stats", "cross_entropy")
+          else "os_softmax_select_path")
+    return _lib.PATH_NAMES[getattr(_lib.load(), fn)(
+        int(M), int(N), _dtype_code_any(dtype))]
 
 
 def _workspace(ws, need, device):

@@ -60,6 +60,7 @@ SIGNATURES = {
                               _vp]),
     "os_softmax_workspace_bytes": (_sz, [_i64, _i64, _i32, _i32]),
     "os_softmax_select_path": (_i32, [_i64, _i64, _i32]),
+    "os_softmax_stats_select_path": (_i32, [_i64, _i64, _i32]),
     "os_status_string": (ctypes.c_char_p, [_i32]),
     "os_attention_fwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64,
                                 _i64, _i64, _vp, _vp, _vp, _vp, _i32,

@@ -125,6 +125,29 @@ def test_select_path_for_the_workloads(lib):
     assert sel(-1, 5, 0) == "auto"          # invalid shape
 
 
+def test_read_only_select_path(lib):
+    # statistics and cross-entropy: long rows stream when rows are many;
+    # otherwise the forward rule
+    sel = lambda M, N, dt: _lib.PATH_NAMES[lib.os_softmax_stats_select_path(M, N, dt)]
+    fwd = lambda M, N, dt: _lib.PATH_NAMES[lib.os_softmax_select_path(M, N, dt)]
+    assert sel(1024, 32768, 0) == "stream"
+    assert sel(1024, 32768, 1) == "stream"
+    assert sel(512, 16385, 0) == "stream"
+    assert sel(512, 16384, 0) == "resident"
+    assert sel(511, 16385, 0) == fwd(511, 16385, 0) == "split"
+    for M, N, dt in [(64, 1000, 0), (4096, 4096, 0), (32768, 1024, 1),
+                     (16, 4194304, 0), (4096, 65536, 0), (16, 32768, 0)]:
+        assert sel(M, N, dt) == fwd(M, N, dt), (M, N, dt)
+    assert sel(-1, 5, 0) == "auto"
+    assert sel(5, 5, 7) == "auto"          # unknown dtype
+    # the workspace of AUTO does not depend on which of the two rules applies
+    for M, N in [(1024, 32768), (512, 16385), (16, 4194304)]:
+        auto = lib.os_softmax_workspace_bytes(M, N, 0, 0)
+        forced = lib.os_softmax_workspace_bytes(
+            M, N, 0, lib.os_softmax_stats_select_path(M, N, 0))
+        assert auto == forced
+
+
 def test_workspace_bytes(lib):
     ws = lib.os_softmax_workspace_bytes
     assert ws(4096, 4096, 0, 0) == 0

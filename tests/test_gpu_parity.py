@@ -186,6 +186,30 @@ def test_stats(path, dtype):
             assert np.all(np.isnan(buf.cpu().numpy()[:, 1::inc]))
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_read_only_auto_streams_long_rows(dtype):
+    # with many rows longer than 16384, AUTO streams the statistics (the
+    # forward stays resident); the result equals the forced stream path
+    M, N = 600, 20000
+    assert rw.select_path(M, N, dtype, op="stats") == "stream"
+    assert rw.select_path(M, N, dtype, op="cross_entropy") == "stream"
+    assert rw.select_path(M, N, dtype) == "resident"
+    x_h = wl.normal(M, N, scale=4.0, seed=21, dtype=dtype)
+    x = to_device(x_h)
+    auto = torch.empty((3, M), device="cuda")
+    forced = torch.empty((3, M), device="cuda")
+    rw.softmax_stats(x, auto[0], auto[1], auto[2])
+    rw.softmax_stats(x, forced[0], forced[1], forced[2], path="stream")
+    torch.cuda.synchronize()
+    assert torch.equal(auto, forced)
+    _, m_ref, d_ref, l_ref = oracle.softmax(x_h, want_y=False)
+    h = auto.cpu().numpy()
+    what = f"stats auto {dtype} {M}x{N}"
+    check_m(h[0], m_ref, what)
+    check_d(h[1], d_ref, what)
+    check_lse(h[2], l_ref, what)
+
+
 def test_column_windows_merge_to_row_state():
     # the state of each column window, merged, is the state of the row
     M, N, Wn = 7, 50000, 6
@@ -505,7 +529,7 @@ def test_cross_entropy_worked_example():
     assert abs(mean.item() - 0.4170) <= 5e-5
 
 
-@pytest.mark.parametrize("name", ["c2", "c3", "c5"])
+@pytest.mark.parametrize("name", ["c2", "c3", "c4", "c5"])
 def test_cross_entropy_workloads(name):
     w = wl.WORKLOADS[name]
     x_h = wl.generate(name)
