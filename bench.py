@@ -518,6 +518,42 @@ def cpu_baseline_attention(w, budget_s):
                       f"{el:.1f} s"}
 
 
+def cpu_baseline_attention_parallel(w, budget_s):
+    """The same fp64 attention oracle on T host threads at once (the C call
+    releases the interpreter lock), each taking its own random query rows,
+    until about budget_s seconds have passed."""
+    from concurrent.futures import ThreadPoolExecutor
+    import numpy as np
+    import oracle
+    from row_wise_online_amd import workloads as wl
+    q, k, v = wl.attention_workload(w.name)
+    T = host_threads()
+    t0 = time.perf_counter()
+
+    def worker(t):
+        rows = np.random.default_rng(w.seed + 1 + t).integers(0, w.Sq, size=4096)
+        flops, n = 0.0, 0
+        while True:
+            i = int(rows[n % len(rows)])
+            oracle.attention(q[0, 0], k[0, 0], v[0, 0], causal=w.causal, rows=[i])
+            keys = w.Sk if w.causal < 0 else min(w.Sk, i + w.causal + 1)
+            flops += 4.0 * keys * w.D
+            n += 1
+            if time.perf_counter() - t0 >= budget_s:
+                return flops, n
+
+    with ThreadPoolExecutor(T) as ex:
+        res = list(ex.map(worker, range(T)))
+    el = time.perf_counter() - t0
+    flops = sum(r[0] for r in res)
+    n = sum(r[1] for r in res)
+    return {"value": round(flops / el / 1e12, 8), "unit": "TFLOP/s",
+            "cores": T, "kind": "oracle",
+            "sample": f"{n} random query rows of {w.Sq}x{w.Sk} d={w.D} "
+                      f"(head 0), fp64 definition oracle, {T} threads, "
+                      f"{el:.1f} s"}
+
+
 def run_attention(name, steps, warmup, want_cpu=True, cpu_budget=10.0,
                   extras=True):
     from row_wise_online_amd import workloads as wl
@@ -563,6 +599,9 @@ def run_attention(name, steps, warmup, want_cpu=True, cpu_budget=10.0,
     rec["copy_ceiling_GBps"] = round(copy_ceiling(w.B * w.H * w.Sq * w.D * 2), 1)
     if want_cpu:
         rec["cpu_baseline"] = cpu_baseline_attention(w, cpu_budget)
+        if host_threads() > 1:
+            rec["cpu_baseline_parallel"] = cpu_baseline_attention_parallel(
+                w, cpu_budget / 2)
     return rec
 
 
