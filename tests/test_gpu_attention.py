@@ -294,6 +294,22 @@ def _sample_rows(Sq, seed):
     return sorted(set(fixed) | set(rng.integers(0, Sq, 14).tolist()))
 
 
+@pytest.mark.parametrize("D", [32, 64, 128])
+@pytest.mark.parametrize("causal", [-1, 0, 700])
+def test_many_heads_medium_sampled(D, causal):
+    # a grid of many workgroups over several (batch, head) pairs, a ragged
+    # query count, more keys than queries, BSHD input and output layouts;
+    # sampled rows of every (batch, head) against the oracle
+    B, H, Sq, Sk = 2, 3, 2049, 3001
+    q, k, v = wl.attention_inputs(B, H, Sq, Sk, D, seed=900 + D + causal,
+                                  layout="bshd")
+    print(f"many heads D={D} causal={causal}", flush=True)
+    o, lse = run(q, k, v, causal=causal, out=torch.float32, o_layout="bshd")
+    rows = [r for r in _sample_rows(Sq, D) if r < Sq]
+    check(q, k, v, o, lse, causal=causal, bf16_out=False, rows=rows,
+          what=f"many heads D{D} c{causal}")
+
+
 @pytest.mark.parametrize("name", ["a2", "a3", "a4", "a5"])
 def test_full_size_sampled_rows(name):
     w = wl.ATTN_WORKLOADS[name]
