@@ -310,6 +310,59 @@ def test_many_heads_medium_sampled(D, causal):
           what=f"many heads D{D} c{causal}")
 
 
+def _all_rows_check(q, k, v, o, lse, causal, what, chunk=4096):
+    """Every query row of head (0, 0) against the definition computed again
+    in fp32 with torch on the GPU, in row chunks (scores, logsumexp,
+    probabilities, P V).  The reference carries roundings of the same kinds
+    as the kernel, so the tolerance is twice the bound of the module
+    docstring, with Delta from the row's largest sum_c |q_c k_jc| and w
+    from the largest |v| over the keys it admits.  This is a check of
+    every row for gross errors (a wrong block, tile or head, an unwritten
+    row); the fp64 oracle checks the sampled rows to the bound itself."""
+    f32 = lambda a: torch.from_numpy(_w(a).astype(np.float32)).cuda()
+    Q, K, V = f32(q[0, 0]), f32(k[0, 0]), f32(v[0, 0])
+    O = torch.from_numpy(o[0, 0].astype(np.float32)).cuda()
+    L = torch.from_numpy(lse[0, 0].astype(np.float32)).cuda()
+    Sq, D = Q.shape
+    Sk = K.shape[0]
+    scale = 1.0 / math.sqrt(D)
+    c = scale * LOG2E
+    Kt, Kat = K.t().contiguous(), K.abs().t().contiguous()
+    vabs = V.abs()
+    wpre = torch.cummax(vabs, dim=0).values if causal >= 0 else None
+    wall = vabs.max(dim=0).values
+    cols = torch.arange(Sk, device="cuda")[None, :]
+    n_acc = Sk / 16 + 2 * Sk / 64 + 64
+    for r0 in range(0, Sq, chunk):
+        r1 = min(Sq, r0 + chunk)
+        S = (Q[r0:r1] @ Kt) * scale
+        A = Q[r0:r1].abs() @ Kat
+        if causal >= 0:
+            rows = torch.arange(r0, r1, device="cuda")[:, None]
+            masked = cols > rows + causal
+            S.masked_fill_(masked, float("-inf"))
+            A.masked_fill_(masked, 0.0)
+            w = wpre[torch.clamp(torch.arange(r0, r1, device="cuda") + causal, max=Sk - 1)]
+        else:
+            w = wall[None, :].expand(r1 - r0, D)
+        lref = torch.logsumexp(S, dim=1)
+        oref = torch.exp(S - lref[:, None]) @ V
+        del S
+        amax = A.max(dim=1).values.double()
+        del A
+        dt = c * D * U * amax + 2 * torch.clamp(c * amax, min=1.0) * 2.0 ** -23
+        delta = 2 * math.log(2) * dt
+        tol_l = 2 * (delta + n_acc * U + 2 * lref.double().abs().clamp(min=1.0) * 2.0 ** -23)
+        tol_o = 2 * ((2.0 ** -8 + 2 * delta[:, None] + n_acc * U) * w.double()
+                     + 2.0 ** -8 * oref.double().abs())
+        err_l = (L[r0:r1].double() - lref.double()).abs()
+        err_o = (O[r0:r1].double() - oref.double()).abs()
+        assert bool((err_l <= tol_l).all()), (
+            f"{what}: lse off in rows {r0}..{r1}: worst {float(err_l.max()):.3g}")
+        assert bool((err_o <= tol_o).all()), (
+            f"{what}: o off in rows {r0}..{r1}: worst {float((err_o - tol_o).max()):.3g} past")
+
+
 @pytest.mark.parametrize("name", ["a2", "a3", "a4", "a5"])
 def test_full_size_sampled_rows(name):
     w = wl.ATTN_WORKLOADS[name]
@@ -321,3 +374,14 @@ def test_full_size_sampled_rows(name):
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
     if w.causal == 0:                        # row 0 sees key 0 alone
         assert np.array_equal(o[0, 0, 0], _w(v[0, 0, 0]))
+    _all_rows_check(q, k, v, o, lse, w.causal, name)
+    if name == "a2":
+        # the all-rows check has teeth: one wrong row of o, or of lse, fails it
+        bad = o.copy()
+        bad[0, 0, w.Sq // 3, 5] += 0.25
+        with pytest.raises(AssertionError):
+            _all_rows_check(q, k, v, bad, lse, w.causal, "planted o error")
+        bad = lse.copy()
+        bad[0, 0, 2 * w.Sq // 3] += 0.01
+        with pytest.raises(AssertionError):
+            _all_rows_check(q, k, v, o, bad, w.causal, "planted lse error")
