@@ -115,6 +115,8 @@ struct Geo {
     static constexpr int CPR = D / 8;                   // 16-byte chunks per row
     static constexpr int RPB = 1024 / RB;               // rows per 1 KB wave load
     static constexpr int NDMA = TILE / 1024 / kWaves;   // wave loads per tile
+    static_assert(NDMA >= 1 && NDMA * kWaves * 1024 == TILE,
+                  "the waves' 1 KiB loads must cover a tile exactly");
     static constexpr int NSLOT = D == 128 ? 3 : 2;      // tiles per ring
     static constexpr int kLdsBytes = 2 * NSLOT * TILE;  // V ring, then K ring
     static constexpr int VRING = 0, KRING = NSLOT * TILE;
