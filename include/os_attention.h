@@ -59,8 +59,10 @@ extern "C" {
  *             each >= 0, the row stride >= D; read during the call only.
  *  scale      multiplies q.k; finite and > 0 (the pages use 1/sqrt(D)).
  *  stream     HIP stream the kernel is enqueued on (0: the null stream).
- * Returns OS_OK after enqueueing one kernel (nothing when B, H or Sq is 0),
- * or, before any HIP call:
+ * Returns OS_OK after enqueueing one kernel (nothing when B, H or Sq is 0;
+ * beyond 2^22 workgroups, one launch per run of whole batches or of heads
+ * of one batch, since a launch counts its threads in 32 bits), or, before
+ * any HIP call:
  *  OS_ERR_NULL        a pointer the call needs is NULL;
  *  OS_ERR_SHAPE       B, H or Sq < 0, Sk < 1, Sq or Sk > 2^30, or more
  *                     than 2^31 - 1 workgroups (query blocks of 256 rows,

@@ -31,7 +31,10 @@
  *    even).  y always has the dtype of x.
  *  - Asynchrony: every call enqueues work on `stream` and returns; outputs
  *    are valid once the stream reaches that point.  Multi-kernel paths are
- *    ordered by the stream alone (no host sync, no atomics).
+ *    ordered by the stream alone (no host sync, no atomics).  Calls of more
+ *    than 2^22 rows are enqueued as launches over consecutive runs of at
+ *    most 2^22 rows (a launch counts its threads in 32 bits), with the same
+ *    results per row as one launch would give.
  *  - Validation happens on the host, before any HIP call; an invalid call
  *    enqueues nothing.  M == 0 is a valid no-op.
  *  - HIP errors: a failed launch returns OS_ERR_HIP (from hipGetLastError,

@@ -3,6 +3,7 @@
 #include <stdint.h>
 
 #include "../../include/os_softmax.h"
+#include "chunks.hpp"
 #include "launch.hpp"
 
 namespace {
@@ -67,13 +68,41 @@ os_status resolve(int64_t M, int64_t N, os_path path, void *ws,
     return OS_OK;
 }
 
+// Rows [r0, r0 + n) of a call as a call of its own: every per-row pointer
+// moves to row r0, and a causal offset is taken relative to the new row 0.
+os::FwdArgs rows_of(const os::FwdArgs &a, int64_t r0, int64_t n) {
+    const int64_t es = a.dt == os::Dt::F32 ? 4 : 2;
+    os::FwdArgs c = a;
+    c.M = n;
+    c.x = static_cast<const char *>(a.x) + r0 * a.ldx * es;
+    if (a.y) c.y = static_cast<char *>(a.y) + r0 * a.ldy * es;
+    if (a.m_out) c.m_out = a.m_out + r0 * a.inc_out;
+    if (a.d_out) c.d_out = a.d_out + r0 * a.inc_out;
+    if (a.lse_out) c.lse_out = a.lse_out + r0 * a.inc_out;
+    if (a.labels) c.labels = a.labels + r0;
+    if (a.loss) c.loss = a.loss + r0;
+    if (a.row_len) c.row_len = a.row_len + r0;
+    if (a.causal >= 0) c.causal = a.causal + r0;
+    return c;
+}
+
+// One launch per part of at most 2^22 rows (the grid of a launch counts
+// work-items in 32 bits); the parts run in stream order and share the
+// workspace, which each part's plan fits in.
 os_status launch(const os::FwdArgs &a, os_path p, void *ws) {
-    switch (p) {
-        case OS_PATH_RESIDENT: os::launch_resident(a); break;
-        case OS_PATH_STREAM: os::launch_stream(a); break;
-        default: os::launch_split(a, ws); break;
+    const os::RowChunks rc = os::row_chunks(a.M);
+    for (int64_t c = 0; c < rc.count; ++c) {
+        const int64_t r0 = c * rc.rows;
+        const int64_t n = a.M - r0 < rc.rows ? a.M - r0 : rc.rows;
+        const os::FwdArgs part = rc.count == 1 ? a : rows_of(a, r0, n);
+        switch (p) {
+            case OS_PATH_RESIDENT: os::launch_resident(part); break;
+            case OS_PATH_STREAM: os::launch_stream(part); break;
+            default: os::launch_split(part, ws); break;
+        }
+        if (hipGetLastError() != hipSuccess) return OS_ERR_HIP;
     }
-    return hipGetLastError() == hipSuccess ? OS_OK : OS_ERR_HIP;
+    return OS_OK;
 }
 
 os::FwdArgs make_args(const void *x, int64_t ld_x, void *y, int64_t ld_y,
@@ -114,7 +143,9 @@ os_status fwd(os::Mode mode, const void *x, int64_t ld_x, void *y,
     a.d_out = d_out;
     a.lse_out = lse_out;
     a.row_len = row_len;
-    a.causal = causal < 0 ? -1 : causal;
+    // an offset of N - 1 or more admits every column of every row; larger
+    // ones are clamped to N so that row + offset stays far inside int64
+    a.causal = causal < 0 ? -1 : (causal > N ? N : causal);
     return launch(a, p, ws);
 }
 
@@ -298,9 +329,16 @@ os_status os_state_merge(const float *m_in, const float *d_in, int64_t ld_in,
     if (m_in == nullptr || d_in == nullptr || m_out == nullptr ||
         d_out == nullptr)
         return OS_ERR_NULL;
-    os::launch_state_merge(m_in, d_in, ld_in, M, static_cast<int>(K), m_out,
-                           d_out, lse_out, 1, stream);
-    return hipGetLastError() == hipSuccess ? OS_OK : OS_ERR_HIP;
+    const os::RowChunks rc = os::row_chunks(M);
+    for (int64_t c = 0; c < rc.count; ++c) {
+        const int64_t r0 = c * rc.rows;
+        const int64_t n = M - r0 < rc.rows ? M - r0 : rc.rows;
+        os::launch_state_merge(m_in + r0 * ld_in, d_in + r0 * ld_in, ld_in, n,
+                               static_cast<int>(K), m_out + r0, d_out + r0,
+                               lse_out ? lse_out + r0 : nullptr, 1, stream);
+        if (hipGetLastError() != hipSuccess) return OS_ERR_HIP;
+    }
+    return OS_OK;
 }
 
 const char *os_status_string(os_status s) {

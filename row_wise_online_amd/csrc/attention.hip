@@ -75,6 +75,7 @@
 #include <stdint.h>
 
 #include "../../include/os_attention.h"
+#include "chunks.hpp"
 #include "common.hpp"
 
 namespace os {
@@ -637,7 +638,7 @@ extern "C" os_status os_attention_fwd(
     if (!(scale > 0.0f) || !(scale <= 3.4028234663852886e38f)) return OS_ERR_UNSUPPORTED;
     if (!q_strides || !k_strides || !v_strides || !o_strides) return OS_ERR_NULL;
     const int64_t nqb = (Sq + kBlockM - 1) / kBlockM;
-    if (B > 0 && H > 0 && (B * H > kMax || nqb * B * H > kMax)) return OS_ERR_SHAPE;
+    if (B > 0 && H > 0 && (B > kMax / H || nqb * B * H > kMax)) return OS_ERR_SHAPE;
     const int64_t *st[4] = {q_strides, k_strides, v_strides, o_strides};
     const int es[4] = {2, 2, 2, o_dtype == OS_BF16 ? 2 : 4};
     for (int t = 0; t < 4; ++t) {
@@ -675,9 +676,27 @@ extern "C" os_status os_attention_fwd(
     p.causal = causal ? int(causal_offset) : 0;
     p.c = float(double(scale) * 1.4426950408889634);
     // causal: one workgroup per pair of query blocks {nqb - 1 - i, i}
-    const int64_t blocks = (causal ? (nqb + 1) / 2 : nqb) * B * H;
-    if (D == 32) launch<32>(p, causal, o_dtype == OS_BF16, blocks, stream);
-    else if (D == 64) launch<64>(p, causal, o_dtype == OS_BF16, blocks, stream);
-    else launch<128>(p, causal, o_dtype == OS_BF16, blocks, stream);
-    return hipGetLastError() == hipSuccess ? OS_OK : OS_ERR_HIP;
+    const int64_t per_head = causal ? (nqb + 1) / 2 : nqb;
+    // A launch's grid counts work-items in 32 bits: beyond 2^22 workgroups
+    // the heads are launched in parts (whole batches, or runs of heads of
+    // one batch), each a call of its own on the heads it covers.
+    const int oes = o_dtype == OS_BF16 ? 2 : 4;
+    bool ok = true;
+    os::for_each_head_chunk(B, H, per_head, [&](const os::HeadChunk &c) {
+        if (!ok) return;
+        Params pc = p;
+        pc.q = p.q + c.b0 * p.qs[0] + c.h0 * p.qs[1];
+        pc.k = p.k + c.b0 * p.ks[0] + c.h0 * p.ks[1];
+        pc.v = p.v + c.b0 * p.vs[0] + c.h0 * p.vs[1];
+        pc.o = static_cast<char *>(o) + (c.b0 * p.os[0] + c.h0 * p.os[1]) * oes;
+        if (lse) pc.lse = lse + (c.b0 * H + c.h0) * Sq;
+        pc.H = int(c.nh);
+        pc.BH = int(c.nb * c.nh);
+        const int64_t blocks = per_head * c.nb * c.nh;
+        if (D == 32) launch<32>(pc, causal, o_dtype == OS_BF16, blocks, stream);
+        else if (D == 64) launch<64>(pc, causal, o_dtype == OS_BF16, blocks, stream);
+        else launch<128>(pc, causal, o_dtype == OS_BF16, blocks, stream);
+        ok = ok && hipGetLastError() == hipSuccess;
+    });
+    return ok ? OS_OK : OS_ERR_HIP;
 }

@@ -1,0 +1,147 @@
+"""Problems larger than one launch: a dispatch counts its grid in 32-bit
+work-items, so row calls of more than 2^22 rows and attention calls of more
+than 2^22 workgroups are issued in parts.  These cases put part boundaries
+inside the problem and compare every row (or sampled heads, including those
+on each side of a boundary) with the fp64 oracle.  A per-row pointer left
+unmoved, or a causal offset not taken relative to the part, shows up in the
+rows after a boundary."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import row_wise_online_amd as rw
+from row_wise_online_amd import workloads as wl
+from gpu_util import check_d, check_log, check_lse, check_m, check_y, to_device, to_host
+import test_gpu_attention as ta
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.filterwarnings("ignore::RuntimeWarning")]
+
+LIMIT = 1 << 22           # rows / attention workgroups per launch
+M_BIG = LIMIT + 3         # two parts of 2097154 and 2097153 rows
+EDGE = (M_BIG + 1) // 2   # first row of the second part
+N = 8
+
+
+def _x(seed, dtype="f32"):
+    return wl.normal(M_BIG, N, scale=3.0, seed=seed, dtype=dtype)
+
+
+@pytest.mark.parametrize("path", ["resident", "stream", "split"])
+def test_softmax_rows_beyond_one_launch(path):
+    x_h = _x(900)
+    x = to_device(x_h)
+    m, d, lse = (torch.empty(M_BIG, device="cuda") for _ in range(3))
+    print(f"softmax {M_BIG}x{N} path={path}", flush=True)
+    y = rw.softmax_fwd(x, m=m, d=d, lse=lse, path=path)
+    torch.cuda.synchronize()
+    y_ref, m_ref, d_ref, l_ref = oracle.softmax(x_h)
+    what = f"softmax {path}"
+    check_y(to_host(y), y_ref, what)
+    check_m(m.cpu().numpy(), m_ref, what)
+    check_d(d.cpu().numpy(), d_ref, what)
+    check_lse(lse.cpu().numpy(), l_ref, what)
+
+
+@pytest.mark.parametrize("path", ["resident", "stream", "split"])
+def test_masked_rows_beyond_one_launch(path):
+    # lengths per row and causal offset 0: row i keeps min(len_i, i + 1)
+    # columns, so the first rows of the problem are masked by the offset and
+    # the rows after the part boundary are not
+    x_h = _x(901, "bf16")
+    rl = np.random.default_rng(5).integers(-1, N + 2, size=M_BIG).astype(np.int32)
+    rl[EDGE:EDGE + 8] = N
+    x = to_device(x_h)
+    print(f"masked log-softmax {M_BIG}x{N} path={path}", flush=True)
+    ly = rw.log_softmax_fwd(x, path=path, row_len=torch.from_numpy(rl).cuda(),
+                            causal=0)
+    torch.cuda.synchronize()
+    _, ly_ref, _, _, _ = oracle.softmax_masked(x_h, rl, 0)
+    check_log(to_host(ly), ly_ref, f"masked {path}")
+
+
+def test_cross_entropy_rows_beyond_one_launch():
+    x_h = _x(902)
+    lab = np.random.default_rng(6).integers(-1, N, size=M_BIG).astype(np.int64)
+    x = to_device(x_h)
+    mean = torch.empty(1, device="cuda")
+    print(f"cross-entropy {M_BIG}x{N}", flush=True)
+    loss = rw.cross_entropy_fwd(x, torch.from_numpy(lab).cuda(), mean=mean,
+                                path="resident")
+    torch.cuda.synchronize()
+    l_ref, _ = oracle.cross_entropy(x_h, lab)
+    check_log(loss.cpu().numpy(), l_ref, "cross-entropy")
+    keep = lab >= 0
+    assert abs(mean.item() - l_ref[keep].mean()) <= 1e-5 * abs(l_ref[keep].mean())
+
+
+def test_stats_update_strided_beyond_one_launch():
+    # statistics at index row * 2, merged into a running state in place
+    x_h = _x(903)
+    x = to_device(x_h)
+    m = torch.full((2 * M_BIG,), float("-inf"), device="cuda")
+    d = torch.zeros(2 * M_BIG, device="cuda")
+    print(f"stats update {M_BIG}x{N} inc=2", flush=True)
+    rw.softmax_stats_update(x[:, :3], m, d, inc=2, path="stream")
+    rw.softmax_stats_update(x[:, 3:], m, d, inc=2, path="stream")
+    torch.cuda.synchronize()
+    _, m_ref, d_ref, _ = oracle.softmax(x_h, want_y=False)
+    mh, dh = m.cpu().numpy(), d.cpu().numpy()
+    check_m(mh[0::2], m_ref, "stats update m")
+    check_d(dh[0::2], d_ref, "stats update d")
+    assert np.all(mh[1::2] == -np.inf) and np.all(dh[1::2] == 0)
+
+
+def test_state_merge_rows_beyond_one_launch():
+    K = 3
+    rng = np.random.default_rng(7)
+    m_in = rng.uniform(-50.0, 50.0, (M_BIG, K)).astype(np.float32)
+    d_in = rng.uniform(0.5, 100.0, (M_BIG, K)).astype(np.float32)
+    ident = rng.random((M_BIG, K)) < 0.2
+    m_in[ident] = -np.inf
+    d_in[ident] = 0.0
+    mo, do, lo = (torch.empty(M_BIG, device="cuda") for _ in range(3))
+    print(f"state merge {M_BIG}x{K}", flush=True)
+    rw.state_merge(torch.from_numpy(m_in).cuda(), torch.from_numpy(d_in).cuda(),
+                   mo, do, lo)
+    torch.cuda.synchronize()
+    m_ref, d_ref, l_ref = oracle.merge(m_in, d_in)
+    mh, dh, lh = mo.cpu().numpy(), do.cpu().numpy(), lo.cpu().numpy()
+    assert np.array_equal(mh.astype(np.float64), m_ref)
+    fin = np.isfinite(m_ref)
+    assert np.all(np.abs(dh[fin] - d_ref[fin]) <= 1e-5 * d_ref[fin])
+    assert np.all(dh[~fin] == 0) and np.all(lh[~fin] == -np.inf)
+    assert np.all(np.abs(lh[fin] - l_ref[fin]) <= 1e-5 + oracle.f32_ulp(l_ref[fin]))
+
+
+@pytest.mark.parametrize("B,H,D,causal,out", [
+    (1, LIMIT + 5, 32, -1, torch.float32),    # runs of heads of one batch
+    (3, 1398102, 64, 0, torch.bfloat16),      # whole batches, 2 + 1
+])
+def test_attention_heads_beyond_one_launch(B, H, D, causal, out):
+    # one query row per head (one workgroup each), keys and values shared
+    # by every head through zero strides
+    Sk = 17
+    G = B * H
+    q, k, v = wl.attention_inputs(1, 1, G, Sk, D, seed=903 + D)
+    qd = ta._dev(q).view(B, H, 1, D)
+    kd = ta._dev(k).expand(B, H, Sk, D)
+    vd = ta._dev(v).expand(B, H, Sk, D)
+    o = torch.empty((B, H, 1, D), dtype=out, device="cuda")
+    lse = torch.empty((B, H, 1), dtype=torch.float32, device="cuda")
+    print(f"attention B{B} H{H} Sq1 Sk{Sk} D{D} causal={causal}", flush=True)
+    rw.attention_fwd(qd, kd, vd, o, lse=lse, causal_offset=causal)
+    torch.cuda.synchronize()
+    edges = [0, 1, LIMIT - 1, LIMIT, LIMIT + 1, 2 * H - 1, 2 * H, G - 1]
+    rng = np.random.default_rng(11)
+    heads = sorted({g for g in edges if 0 <= g < G} |
+                   set(rng.integers(0, G, size=40).tolist()))
+    n = len(heads)
+    qs = np.ascontiguousarray(q[0, 0][heads].reshape(1, n, 1, D))
+    ks = np.ascontiguousarray(np.broadcast_to(k, (1, n, Sk, D)))
+    vs = np.ascontiguousarray(np.broadcast_to(v, (1, n, Sk, D)))
+    oh = ta._host(o.view(G, D)[heads]).reshape(1, n, 1, D)
+    lh = lse.view(G)[heads].cpu().numpy().astype(np.float64).reshape(1, n, 1)
+    ta.check(qs, ks, vs, oh, lh, causal=causal, bf16_out=out == torch.bfloat16,
+             what=f"attention B{B} H{H}")

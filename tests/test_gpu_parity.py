@@ -627,6 +627,22 @@ def test_masked_in_place_and_reads(path):
     assert np.all(np.isnan(yh[5]))
 
 
+@pytest.mark.parametrize("path", ["resident", "stream", "split"])
+def test_causal_offset_beyond_the_row_is_no_mask(path):
+    # an offset of N - 1 or more admits every column of every row, up to the
+    # largest int64 (where row + offset would not fit without the clamp)
+    M, N = 40, 3000
+    x_h = wl.normal(M, N, scale=2.0, seed=77)
+    x = to_device(x_h)
+    y_ref, *_ = oracle.softmax(x_h)
+    for off in (N - 1, N, 2 ** 40, 2 ** 63 - 1):
+        y = rw.softmax_fwd(x, path=path, causal=off)
+        ly = rw.log_softmax_fwd(x, path=path, causal=off)
+        torch.cuda.synchronize()
+        check_y(to_host(y), y_ref, f"causal {off} {path}")
+        check_log(to_host(ly), oracle.log_softmax(x_h), f"log causal {off} {path}")
+
+
 # ---------------------------------------------------------------------------
 # Streaming statistics: windows folded into a running state
 # ---------------------------------------------------------------------------
