@@ -46,8 +46,8 @@ ROTATE_BYTES = 1 << 30      # rotating working set, 4x the Infinity Cache
 def kernel_source_hash(family="softmax"):
     """Hash of the sources one kernel family is built from: "softmax" (every
     csrc file but the attention kernel) or "attention" (the attention kernel
-    and the shared header).  A committed counter record applies only while
-    this hash is unchanged."""
+    and the headers it includes).  A committed counter record applies only
+    while this hash is unchanged."""
     h = hashlib.sha256()
     for p in sorted(glob.glob(os.path.join(ROOT, "row_wise_online_amd",
                                            "csrc", "*"))):
@@ -57,7 +57,8 @@ def kernel_source_hash(family="softmax"):
         is_attn = name.startswith("attention")
         if family == "softmax" and is_attn:
             continue
-        if family == "attention" and not (is_attn or name == "common.hpp"):
+        if family == "attention" and not (is_attn or name in ("common.hpp",
+                                                              "chunks.hpp")):
             continue
         with open(p, "rb") as f:
             h.update(name.encode())
