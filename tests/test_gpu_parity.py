@@ -685,3 +685,74 @@ def test_stats_update_from_identity_equals_stats():
     torch.cuda.synchronize()
     # merging into the identity leaves the window state unchanged
     assert torch.equal(m, m2) and torch.equal(d, d2)
+
+
+# ---------------------------------------------------------------------------
+# HIP graph replay: the row ops captured once, replayed on new inputs
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("path", ["resident", "stream", "split"])
+def test_graph_replay_rows(path):
+    # softmax with its statistics, log-softmax, statistics alone and the
+    # cross-entropy with its mean (two launches), captured in one graph;
+    # each replay runs on inputs written eagerly just before it and must
+    # give the bits of the same calls made eagerly
+    M, N = 300, 5000
+    x = torch.empty(M, N, device="cuda")
+    labels = torch.empty(M, dtype=torch.int64, device="cuda")
+    outs = dict(y=torch.empty(M, N, device="cuda"),
+                ly=torch.empty(M, N, device="cuda"),
+                m=torch.empty(M, device="cuda"), d=torch.empty(M, device="cuda"),
+                lse=torch.empty(M, device="cuda"),
+                sm=torch.empty(M, device="cuda"), sd=torch.empty(M, device="cuda"),
+                loss=torch.empty(M, device="cuda"),
+                mean=torch.empty(1, device="cuda"))
+    need = max(rw.workspace_bytes(M, N, torch.float32, path), 1)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+
+    def calls(stream):
+        o = outs
+        return [rw.prepare_fwd(x, o["y"], m=o["m"], d=o["d"], lse=o["lse"],
+                               ws=ws, path=path, stream=stream),
+                rw.prepare_fwd(x, o["ly"], ws=ws, path=path, stream=stream,
+                               log=True),
+                rw.prepare_stats(x, o["sm"], o["sd"], ws=ws, path=path,
+                                 stream=stream),
+                rw.prepare_cross_entropy(x, labels, o["loss"], mean=o["mean"],
+                                         ws=ws, path=path, stream=stream)]
+
+    def inputs(seed):
+        x.copy_(torch.from_numpy(wl.normal(M, N, scale=3.0, seed=seed)))
+        labels.copy_(torch.from_numpy(_labels(M, N, seed)))
+
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    inputs(70)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=s):
+        for c in calls(torch.cuda.current_stream()):
+            c()
+    eager = calls(None)
+    for i, seed in enumerate((71, 72, 73)):
+        inputs(seed)
+        for c in eager:
+            c()
+        torch.cuda.synchronize()
+        want = {k: v.clone() for k, v in outs.items()}
+        for v in outs.values():
+            v.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k, v in outs.items():
+            assert torch.equal(v, want[k]) or (
+                torch.isnan(v).equal(torch.isnan(want[k]))
+                and torch.equal(v.nan_to_num(), want[k].nan_to_num())), \
+                f"replay {i} ({path}): {k} differs from the eager call"
+        # and the eager result is the oracle's
+        if i == 0:
+            x_h = wl.normal(M, N, scale=3.0, seed=seed)
+            y_ref, m_ref, d_ref, l_ref = oracle.softmax(x_h)
+            check_y(want["y"].cpu().numpy(), y_ref, f"graph {path}")
+            check_m(want["m"].cpu().numpy(), m_ref, f"graph {path}")
+            check_lse(want["lse"].cpu().numpy(), l_ref, f"graph {path}")
