@@ -145,3 +145,42 @@ def test_attention_heads_beyond_one_launch(B, H, D, causal, out):
     lh = lse.view(G)[heads].cpu().numpy().astype(np.float64).reshape(1, n, 1)
     ta.check(qs, ks, vs, oh, lh, causal=causal, bf16_out=out == torch.bfloat16,
              what=f"attention B{B} H{H}")
+
+
+@pytest.mark.parametrize("dtype,path", [("f32", "auto"), ("bf16", "stream")])
+def test_longest_row(dtype, path):
+    # one row of N = 2^30 elements, the largest the entry points take (4 GiB
+    # in fp32), with a planted maximum in the middle; the oracle evaluates
+    # the whole row and sampled columns are compared, including the planted
+    # one, the ends and the split path's chunk edges
+    N = 1 << 30
+    planted = 123_456_789
+    g = torch.Generator(device="cuda").manual_seed(904)
+    x = torch.randn(1, N, device="cuda", generator=g)
+    x.mul_(2.0)
+    if dtype == "bf16":
+        x = x.to(torch.bfloat16)
+    x[0, planted] = 30.0
+    m, d, lse = (torch.empty(1, device="cuda") for _ in range(3))
+    print(f"softmax 1x{N} {dtype} path={path}", flush=True)
+    y = rw.softmax_fwd(x, m=m, d=d, lse=lse, path=path)
+    torch.cuda.synchronize()
+    x_h = to_host(x)
+    y_ref, m_ref, d_ref, l_ref = oracle.softmax(x_h)
+    rng = np.random.default_rng(12)
+    chunk = 1 << 19                                 # the split path's chunk length here
+    edges = [k * chunk + e for k in (1, 2, 1000, 2047) for e in (-1, 0)]
+    cols = sorted(set(rng.integers(0, N, size=4000).tolist())
+                  | {0, 1, planted - 1, planted, planted + 1, N - 2, N - 1}
+                  | set(edges))
+    ct = torch.tensor(cols, device="cuda")
+    what = f"longest row {dtype} {path}"
+    check_y(to_host(y[:, ct]), y_ref[:, cols], what)
+    check_m(m.cpu().numpy(), m_ref, what)
+    check_d(d.cpu().numpy(), d_ref, what)
+    check_lse(lse.cpu().numpy(), l_ref, what)
+    # every element: non-negative, and the row sums to 1 within the
+    # per-element relative bar (fp32 1e-5, bf16 one step of 2^-8)
+    total = float(y.double().sum())
+    assert float(y.min()) >= 0.0
+    assert abs(total - 1.0) <= (1e-5 if dtype == "f32" else 2.0 ** -8), total
