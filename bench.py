@@ -78,7 +78,8 @@ def algorithmic_bytes(w, path, n_stats, op="softmax", causal=None):
     """Bytes the path must move for one step of workload w: x read once per
     read pass (only the unmasked part of each row), y written once (all of
     it), row statistics written; the cross-entropy reads x once and moves
-    8 B of label + 4 B of loss per row (+ 4 B mean)."""
+    8 B of label + 4 B of loss per row (+ 4 B mean); pass 2 alone
+    (normalize) reads x and the 8 B row state and writes y."""
     import row_wise_online_amd as rw
     xy = w.M * w.N * w.esize
     xr = valid_elements(w, causal) * w.esize
@@ -86,6 +87,8 @@ def algorithmic_bytes(w, path, n_stats, op="softmax", causal=None):
         b = xy + 12 * w.M + 4
     elif op == "stats":
         b = xy + 12 * w.M
+    elif op == "normalize":
+        return 2 * xy + 8 * w.M
     else:
         reads = 1 if path == "resident" else 2
         b = reads * xr + xy + 4 * w.M * n_stats
@@ -137,6 +140,13 @@ def measure(w, steps, warmup, path="auto", rotate=True, graph=False,
         m = torch.empty(w.M, device="cuda")
         d = torch.empty(w.M, device="cuda")
         lse = torch.empty(w.M, device="cuda")
+    if op == "normalize":
+        # the row state every buffer set shares (they hold the same values),
+        # taken once before the timed steps
+        m_st = torch.empty(w.M, device="cuda")
+        d_st = torch.empty(w.M, device="cuda")
+        rw.softmax_stats(x0, m_st, d_st)
+        m = d = lse = None
 
     extra_streams = []
     if streams == 2:
@@ -152,6 +162,9 @@ def measure(w, steps, warmup, path="auto", rotate=True, graph=False,
         strm = [torch.cuda.current_stream()] + extra_streams
         if op == "stats":
             return [rw.prepare_stats(xs[i], m, d, lse, ws=ws, path=path)
+                    for i in range(R)]
+        if op == "normalize":
+            return [rw.prepare_normalize(xs[i], ys[i], m_st, d_st)
                     for i in range(R)]
         if ce:
             return [rw.prepare_cross_entropy(xs[i], labels, loss, mean=mean,
@@ -302,6 +315,11 @@ def cpu_baseline(w, n_stats, budget_s, op="softmax", causal=None):
         fn = lambda: oracle.softmax(x, want_y=False)
         what = "row statistics (m, d, lse)"
         b = w.M * w.N * w.esize + 12 * w.M
+    elif op == "normalize":
+        # the oracle has no pass 2 of its own: its softmax forms the same y
+        fn = lambda: oracle.softmax(x)
+        what = "three-pass softmax (y, for pass 2 alone)"
+        b = 2 * w.M * w.N * w.esize + 8 * w.M
     elif causal is not None:
         fn = lambda: oracle.softmax_masked(x, None, causal)
         what = f"causal (offset {causal}) softmax and log-softmax"
@@ -348,12 +366,19 @@ def run_workload(name, steps, warmup, path="auto", want_cpu=True,
     import row_wise_online_amd as rw
     from row_wise_online_amd import workloads as wl
     w = wl.WORKLOADS[name]
-    resolved = rw.select_path(w.M, w.N, w.dtype, op=op) if path == "auto" else path
+    if op == "normalize":
+        resolved = "normalize"   # one kernel of its own, whatever the path
+    else:
+        resolved = rw.select_path(w.M, w.N, w.dtype, op=op) if path == "auto" else path
     n_stats = len(set(w.outputs) & {"m", "d", "lse"})
     if op == "cross_entropy":
         n_stats = 0
     if op == "stats":
         n_stats = 3
+    if op == "normalize":
+        n_stats = 0
+        if causal is not None:
+            raise ValueError("pass 2 alone takes no mask")
     if causal is not None and op == "cross_entropy":
         raise ValueError("the causal mask applies to softmax / log-softmax")
     ms, R, host_us, dist = measure(w, steps, warmup, path, op=op,
@@ -368,7 +393,8 @@ def run_workload(name, steps, warmup, path="auto", want_cpu=True,
     eff = (2 * w.M * w.N * w.esize + 4 * w.M * n_stats) / (ms * 1e-3) / 1e9
     opname = {"softmax": "softmax", "log_softmax": "log-softmax",
               "cross_entropy": "cross-entropy",
-              "stats": "row statistics (m, d, lse)"}[op]
+              "stats": "row statistics (m, d, lse)",
+              "normalize": "softmax pass 2 with a held row state"}[op]
     if causal is not None:
         opname = f"causal (offset {causal}) {opname}"
     rec = {
@@ -397,6 +423,7 @@ def run_workload(name, steps, warmup, path="auto", want_cpu=True,
                    "causal_offset": causal,
                    "outputs": (["loss", "mean"] if op == "cross_entropy"
                                else ["m", "d", "lse"] if op == "stats"
+                               else ["y"] if op == "normalize"
                                else list(w.outputs)), "path": resolved},
         "pct_of_peak": round(100.0 * gbs / PEAK_GBS, 2),
         "rows_per_s": round(w.M / (ms * 1e-3), 1),
@@ -631,7 +658,7 @@ def main():
                     choices=["auto", "resident", "stream", "split"])
     ap.add_argument("--op", default="softmax",
                     choices=["softmax", "log_softmax", "cross_entropy",
-                             "stats", "attention"])
+                             "stats", "normalize", "attention"])
     ap.add_argument("--causal", type=int, default=None,
                     help="causal mask offset (softmax / log-softmax)")
     ap.add_argument("--all", action="store_true",
@@ -671,7 +698,8 @@ def main():
     rw.load()
 
     if args.all:
-        for op in ["softmax", "log_softmax", "cross_entropy", "stats"]:
+        for op in ["softmax", "log_softmax", "cross_entropy", "stats",
+                   "normalize"]:
             for name in ["c1", "c2", "c3", "c4", "c5"]:
                 print(f"[bench] {op} workload {name}", file=sys.stderr,
                       flush=True)

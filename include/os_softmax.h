@@ -226,6 +226,41 @@ os_status os_softmax_stats_update(const void *x, int64_t ld_x, int64_t M,
                                   void *ws, size_t ws_bytes, os_path path,
                                   hipStream_t stream);
 
+/* Pass 2 alone, for a row state the caller already holds: for i < M,
+ * j < N,
+ *   os_softmax_normalize:      y[i*ld_y + j] = e^(x[i*ld_x + j] - m_i) / d_i
+ *   os_log_softmax_normalize:  y[i*ld_y + j] = (x[i*ld_x + j] - m_i) - log d_i
+ * with m_i = m_in[i*inc], d_i = d_in[i*inc] (fp32, device, read only).  The
+ * outputs of a column window need only its row's final state, however that
+ * state was reached: os_softmax_stats over the whole row, the statistics of
+ * several windows merged by os_softmax_stats_update or os_state_merge, or
+ * states gathered from other devices ("5.2 CUDA Online Softmax 实现优化"
+ * §7.1, the second stage of a split row; "Softmax 数值稳定性与 IO-Aware
+ * Attention：从在线归一化到FlashAttention" §4.1, the merged state).  So x
+ * may be a window of a longer row: the call then writes that window of the
+ * row's softmax.
+ *  x, y     device, M rows of N elements, row pitches ld_x, ld_y >= N; y
+ *           has x's dtype; y == x with ld_y == ld_x (in place) is allowed.
+ *  m_in, d_in  the row states; the state must cover the elements of x
+ *           (m_i at least their max, d_i their sum of e^(x - m_i) together
+ *           with any other columns of the row), as the functions above
+ *           produce.  The identity (-inf, 0) gives a NaN row, like a row of
+ *           only -inf.
+ *  inc      stride between the states of consecutive rows, >= 1.
+ * One read of x and one write of y, on `stream`; no workspace.  Errors:
+ * OS_ERR_SHAPE, OS_ERR_DTYPE, OS_ERR_STRIDE (a pitch < N or inc < 1),
+ * OS_ERR_NULL (x, y, m_in or d_in NULL with M > 0), OS_ERR_HIP. */
+os_status os_softmax_normalize(const void *x, int64_t ld_x, void *y,
+                               int64_t ld_y, int64_t M, int64_t N,
+                               os_dtype dt, const float *m_in,
+                               const float *d_in, int64_t inc,
+                               hipStream_t stream);
+os_status os_log_softmax_normalize(const void *x, int64_t ld_x, void *y,
+                                   int64_t ld_y, int64_t M, int64_t N,
+                                   os_dtype dt, const float *m_in,
+                                   const float *d_in, int64_t inc,
+                                   hipStream_t stream);
+
 /* Merge K partial states per row ("5.2 CUDA Online Softmax 实现优化" §4.1):
  * row i's states are (m_in[i*ld_in + k], d_in[i*ld_in + k]), k < K, fp32.
  * (-inf, 0) is an exact identity.  Writes m_out[i], d_out[i] (required) and

@@ -29,7 +29,7 @@ from ._lib import OsError, PATHS, PATH_NAMES  # noqa: F401
 __all__ = ["softmax_fwd", "log_softmax_fwd", "cross_entropy_fwd",
            "prepare_fwd", "prepare_cross_entropy", "prepare_stats",
            "softmax_stats",
-           "softmax_stats_update",
+           "softmax_stats_update", "softmax_normalize", "prepare_normalize",
            "state_merge", "workspace_bytes", "select_path", "OsError", "load",
            "attention_fwd", "prepare_attention"]
 
@@ -328,6 +328,52 @@ def softmax_stats_update(x, m, d, lse=None, *, inc=1, ws=None, path="auto",
                                      _vec(lse, "lse", M, inc), wp, wb, pc,
                                      _stream(stream))
     _lib.check("os_softmax_stats_update", st)
+
+
+def softmax_normalize(x, m, d, y=None, *, inc=1, log=False, stream=None):
+    """Pass 2 alone with a row state the caller holds: y = e^(x - m) / d
+    (log=True: (x - m) - log d) per row, m and d fp32 at index row * inc.
+    x may be a column window of longer rows whose state (m, d) covers the
+    whole row.  Returns y (allocated like x when not given)."""
+    torch = _torch()
+    lib = _lib.load()
+    dt = _dtype_code(x.dtype)
+    if y is None:
+        y = torch.empty_like(x)
+    if y.dtype != x.dtype or y.shape != x.shape:
+        raise ValueError("y must have the dtype and shape of x")
+    xp, ldx = _matrix(x, "x")
+    yp, ldy = _matrix(y, "y")
+    M, N = x.shape
+    name = "os_log_softmax_normalize" if log else "os_softmax_normalize"
+    st = getattr(lib, name)(xp, ldx, yp, ldy, M, N, dt, _vec(m, "m", M, inc),
+                            _vec(d, "d", M, inc), inc, _stream(stream))
+    _lib.check(name, st)
+    return y
+
+
+def prepare_normalize(x, y, m, d, *, inc=1, log=False, stream=None):
+    """softmax_normalize's counterpart of prepare_fwd: marshal once, return
+    a function that repeats the call."""
+    lib = _lib.load()
+    dt = _dtype_code(x.dtype)
+    if y.dtype != x.dtype or y.shape != x.shape:
+        raise ValueError("y must have the dtype and shape of x")
+    xp, ldx = _matrix(x, "x")
+    yp, ldy = _matrix(y, "y")
+    M, N = x.shape
+    name = "os_log_softmax_normalize" if log else "os_softmax_normalize"
+    args = (xp, ldx, yp, ldy, M, N, dt, _vec(m, "m", M, inc),
+            _vec(d, "d", M, inc), inc, _stream(stream))
+    fn = getattr(lib, name)
+    keep = (x, y, m, d)
+
+    def call():
+        st = fn(*args)
+        if st:
+            _lib.check(name, st)
+    call.tensors = keep
+    return call
 
 
 def state_merge(m_in, d_in, m_out, d_out, lse_out=None, *, stream=None):

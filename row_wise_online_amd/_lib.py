@@ -58,6 +58,10 @@ SIGNATURES = {
                                        _i64, _vp, _vp, _sz, _i32, _vp]),
     "os_state_merge": (_i32, [_vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp,
                               _vp]),
+    "os_softmax_normalize": (_i32, [_vp, _i64, _vp, _i64, _i64, _i64, _i32,
+                                    _vp, _vp, _i64, _vp]),
+    "os_log_softmax_normalize": (_i32, [_vp, _i64, _vp, _i64, _i64, _i64,
+                                        _i32, _vp, _vp, _i64, _vp]),
     "os_softmax_workspace_bytes": (_sz, [_i64, _i64, _i32, _i32]),
     "os_softmax_select_path": (_i32, [_i64, _i64, _i32]),
     "os_softmax_stats_select_path": (_i32, [_i64, _i64, _i32]),

@@ -227,6 +227,52 @@ os_status os_log_softmax_fwd_masked(const void *x, int64_t ld_x, void *y,
 
 namespace {
 
+// softmax / log-softmax of rows (or column windows of rows) for a row state
+// the caller holds: pass 2 alone
+os_status normalize(os::Mode mode, const void *x, int64_t ld_x, void *y,
+                    int64_t ld_y, int64_t M, int64_t N, os_dtype dt,
+                    const float *m_in, const float *d_in, int64_t inc,
+                    hipStream_t stream) {
+    os_status s = check_shape(M, N, dt);
+    if (s != OS_OK) return s;
+    if (ld_x < N || ld_y < N || inc < 1) return OS_ERR_STRIDE;
+    if (M == 0) return OS_OK;
+    if (x == nullptr || y == nullptr || m_in == nullptr || d_in == nullptr)
+        return OS_ERR_NULL;
+    const os::FwdArgs a = make_args(x, ld_x, y, ld_y, M, N, dt, mode, stream);
+    const os::RowChunks rc = os::row_chunks(M);
+    for (int64_t c = 0; c < rc.count; ++c) {
+        const int64_t r0 = c * rc.rows;
+        const int64_t n = M - r0 < rc.rows ? M - r0 : rc.rows;
+        os::launch_state_normalize(rc.count == 1 ? a : rows_of(a, r0, n),
+                                   m_in + r0 * inc, d_in + r0 * inc, inc);
+        if (hipGetLastError() != hipSuccess) return OS_ERR_HIP;
+    }
+    return OS_OK;
+}
+
+}  // namespace
+
+os_status os_softmax_normalize(const void *x, int64_t ld_x, void *y,
+                               int64_t ld_y, int64_t M, int64_t N,
+                               os_dtype dt, const float *m_in,
+                               const float *d_in, int64_t inc,
+                               hipStream_t stream) {
+    return normalize(os::Mode::Prob, x, ld_x, y, ld_y, M, N, dt, m_in, d_in,
+                     inc, stream);
+}
+
+os_status os_log_softmax_normalize(const void *x, int64_t ld_x, void *y,
+                                   int64_t ld_y, int64_t M, int64_t N,
+                                   os_dtype dt, const float *m_in,
+                                   const float *d_in, int64_t inc,
+                                   hipStream_t stream) {
+    return normalize(os::Mode::LogProb, x, ld_x, y, ld_y, M, N, dt, m_in, d_in,
+                     inc, stream);
+}
+
+namespace {
+
 os_status stats(const void *x, int64_t ld_x, int64_t M, int64_t N,
                 os_dtype dt, float *m_out, float *d_out, int64_t inc_out,
                 float *lse_out, void *ws, size_t ws_bytes, os_path path,

@@ -460,6 +460,33 @@ __global__ __launch_bounds__(kWave *WAVES) void split_normalize_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Pass 2 alone, with a row state the caller holds: the outputs of a column
+// window need only the final (m, d) of its row, however that state was
+// reached (the statistics of several windows merged, as the split path's
+// second stage does for its chunks, "5.2 CUDA Online Softmax 实现优化" §7.1).
+// Rows are cut into P chunks of C columns as on the split path; workgroup b
+// normalises chunk b % P of row b / P with (m[row * inc], d[row * inc]).
+// One read and one write per element, both non-temporal.
+// ---------------------------------------------------------------------------
+template <class Tr, bool VEC, int WAVES, int U, Out OUT>
+__global__ __launch_bounds__(kWave *WAVES) void state_normalize_kernel(
+    const typename Tr::elem_t *x, int64_t ldx, typename Tr::elem_t *y,
+    int64_t ldy, int N, int P, int C, const float *sm, const float *sd,
+    int64_t inc) {
+    using T = Tiles<Tr, VEC, WAVES, U, true, true>;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int64_t b = blockIdx.x;
+    const int64_t row = b / P;
+    const int p = static_cast<int>(b - row * P);
+    const int c0 = p * C;
+    const int n = min(C, N - c0);
+    const State st{sm[row * inc], sd[row * inc]};
+    T::template normalize<OUT, false>(x + row * ldx + c0, y + row * ldy + c0, n,
+                                      n, wave * kWave + lane, st);
+}
+
+// ---------------------------------------------------------------------------
 // Second-level state merge ("5.2 CUDA Online Softmax 实现优化" §4.1): one
 // wavefront per row, ROWS rows per workgroup.  Each lane folds states
 // k = lane, lane + 64, ... with the pairwise merge; the wavefront merge

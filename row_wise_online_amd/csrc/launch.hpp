@@ -58,6 +58,11 @@ size_t split_workspace_bytes(int64_t M, int64_t N);
 // normalise kernel, which merges the row's partial states itself.
 void launch_split(const FwdArgs &a, void *ws);
 
+// Pass 2 alone (Mode::Prob or Mode::LogProb) with the caller's row state
+// (m, d) at row * inc; rows are cut into chunks as on the split path.
+void launch_state_normalize(const FwdArgs &a, const float *sm, const float *sd,
+                            int64_t inc);
+
 // Second-level state merge of K fp32 states per row (no cross-entropy):
 // m, d and lse (nullable) at row * inc.
 void launch_state_merge(const float *m_in, const float *d_in, int64_t ld,

@@ -1,6 +1,6 @@
 // Split-row path (partial states -> state merge, alone for statistics or
-// folded into the normalise kernel), the public state-merge launcher and the
-// cross-entropy mean.
+// folded into the normalise kernel), the normalise pass for a given row
+// state, the public state-merge launcher and the cross-entropy mean.
 #include "kernels.hpp"
 #include "launch.hpp"
 
@@ -118,6 +118,59 @@ void launch_split(const FwdArgs &a, void *ws) {
         if (a.vec) by_mode<F32, true>(a, ws); else by_mode<F32, false>(a, ws);
     } else {
         if (a.vec) by_mode<BF16, true>(a, ws); else by_mode<BF16, false>(a, ws);
+    }
+}
+
+namespace {
+
+template <class Tr, bool VEC, int WAVES, int U>
+void state_normalize(const FwdArgs &a, const SplitPlan &plan, const float *sm,
+                     const float *sd, int64_t inc) {
+    using E = typename Tr::elem_t;
+    const dim3 grid(static_cast<unsigned>(a.M * plan.P));
+    const dim3 block(kWave * WAVES);
+    const E *x = static_cast<const E *>(a.x);
+    E *y = static_cast<E *>(a.y);
+    if (a.mode == Mode::Prob) {
+        state_normalize_kernel<Tr, VEC, WAVES, U, Out::Prob>
+            <<<grid, block, 0, a.stream>>>(x, a.ldx, y, a.ldy, a.N, plan.P,
+                                           plan.C, sm, sd, inc);
+    } else {
+        state_normalize_kernel<Tr, VEC, WAVES, U, Out::LogProb>
+            <<<grid, block, 0, a.stream>>>(x, a.ldx, y, a.ldy, a.N, plan.P,
+                                           plan.C, sm, sd, inc);
+    }
+}
+
+// Workgroup shape by the bytes one workgroup covers (a row, or a chunk of
+// one): with 16-byte slots the tile is the whole row up to 32 KiB, as on
+// the resident path (one wavefront up to 4 KiB, then 4 or 8), and longer
+// rows loop over tiles of 8 slots per lane.
+template <class Tr, bool VEC>
+void run_state_normalize(const FwdArgs &a, const float *sm, const float *sd,
+                         int64_t inc) {
+    const SplitPlan plan = split_plan(a.M, a.N);
+    const int64_t len = plan.C < a.N ? plan.C : a.N;
+    const int64_t bytes = len * static_cast<int64_t>(sizeof(typename Tr::elem_t));
+    if (bytes <= 1024) state_normalize<Tr, VEC, 1, 1>(a, plan, sm, sd, inc);
+    else if (bytes <= 2048) state_normalize<Tr, VEC, 1, 2>(a, plan, sm, sd, inc);
+    else if (bytes <= 4096) state_normalize<Tr, VEC, 1, 4>(a, plan, sm, sd, inc);
+    else if (bytes <= 8192) state_normalize<Tr, VEC, 4, 2>(a, plan, sm, sd, inc);
+    else if (bytes <= 16384) state_normalize<Tr, VEC, 8, 2>(a, plan, sm, sd, inc);
+    else if (bytes <= 32768) state_normalize<Tr, VEC, 8, 4>(a, plan, sm, sd, inc);
+    else state_normalize<Tr, VEC, 8, 8>(a, plan, sm, sd, inc);
+}
+
+}  // namespace
+
+void launch_state_normalize(const FwdArgs &a, const float *sm, const float *sd,
+                            int64_t inc) {
+    if (a.dt == Dt::F32) {
+        if (a.vec) run_state_normalize<F32, true>(a, sm, sd, inc);
+        else run_state_normalize<F32, false>(a, sm, sd, inc);
+    } else {
+        if (a.vec) run_state_normalize<BF16, true>(a, sm, sd, inc);
+        else run_state_normalize<BF16, false>(a, sm, sd, inc);
     }
 }
 

@@ -113,6 +113,25 @@ def test_merge_validation(lib, args, status):
     assert lib.os_state_merge(*args, NUL) == status
 
 
+def _norm(lib, name, x=FAKE, ldx=8, y=FAKE, ldy=8, M=4, N=8, dt=0, m=FAKE,
+          d=FAKE, inc=1):
+    return getattr(lib, name)(x, ldx, y, ldy, M, N, dt, m, d, inc, NUL)
+
+
+@pytest.mark.parametrize("name", ["os_softmax_normalize",
+                                  "os_log_softmax_normalize"])
+@pytest.mark.parametrize("kw,status", [
+    (dict(M=-1), 2), (dict(N=0), 2), (dict(N=(1 << 30) + 1, ldx=1 << 31,
+                                           ldy=1 << 31), 2),
+    (dict(ldx=7), 3), (dict(ldy=7), 3), (dict(inc=0), 3), (dict(inc=-2), 3),
+    (dict(dt=2), 4), (dict(x=NUL), 1), (dict(y=NUL), 1), (dict(m=NUL), 1),
+    (dict(d=NUL), 1),
+    (dict(M=0, x=NUL, y=NUL, m=NUL, d=NUL), 0),      # M == 0: no-op
+])
+def test_normalize_validation(lib, name, kw, status):
+    assert _norm(lib, name, **kw) == status
+
+
 def test_select_path_for_the_workloads(lib):
     sel = lambda M, N, dt: _lib.PATH_NAMES[lib.os_softmax_select_path(M, N, dt)]
     assert sel(64, 1000, 0) == "resident"

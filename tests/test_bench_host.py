@@ -48,6 +48,15 @@ def test_cross_entropy_and_stats_read_once():
     assert bench.algorithmic_bytes(w, "resident", 3, "stats") == xy + 12 * w.M
 
 
+def test_normalize_reads_x_and_the_state_once():
+    # pass 2 alone: x read, y written, 8 B of row state read, on any path
+    for name in ("c2", "c5"):
+        w = wl.WORKLOADS[name]
+        xy = w.M * w.N * w.esize
+        for path in ("resident", "split", "normalize"):
+            assert bench.algorithmic_bytes(w, path, 0, "normalize") == 2 * xy + 8 * w.M
+
+
 def test_causal_elements_closed_form():
     # square rows with offset 0 keep the lower triangle: M (M + 1) / 2
     w = wl.WORKLOADS["c2"]

@@ -93,6 +93,23 @@ def test_stats_update_strided_beyond_one_launch():
     assert np.all(mh[1::2] == -np.inf) and np.all(dh[1::2] == 0)
 
 
+def test_normalize_rows_beyond_one_launch():
+    # the state of each row at index row * 2, from the statistics entry
+    # point, then pass 2 alone over all rows
+    x_h = _x(905, "bf16")
+    x = to_device(x_h)
+    m = torch.empty(2 * M_BIG, device="cuda")
+    d = torch.empty(2 * M_BIG, device="cuda")
+    print(f"normalize {M_BIG}x{N} inc=2", flush=True)
+    rw.softmax_stats(x, m, d, inc=2)
+    y = rw.softmax_normalize(x, m, d, inc=2)
+    ly = rw.softmax_normalize(x, m, d, inc=2, log=True)
+    torch.cuda.synchronize()
+    y_ref, *_ = oracle.softmax(x_h)
+    check_y(to_host(y), y_ref, "normalize")
+    check_log(to_host(ly), oracle.log_softmax(x_h), "log normalize")
+
+
 def test_state_merge_rows_beyond_one_launch():
     K = 3
     rng = np.random.default_rng(7)

@@ -688,6 +688,65 @@ def test_stats_update_from_identity_equals_stats():
 
 
 # ---------------------------------------------------------------------------
+# Pass 2 alone with a held row state: column windows normalised with the
+# state merged from their statistics
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("M,N", [(9, 40000), (3000, 700), (5, 300001), (1, 1)])
+def test_windows_normalized_with_the_row_state(M, N, dtype):
+    # the statistics of random column windows (some starting off the 16-byte
+    # grid) merged into one state per row, then each window normalised with
+    # it: together they are the row's softmax and log-softmax
+    x_h = wl.normal(M, N, scale=3.0, seed=24, dtype=dtype)
+    x = to_device(x_h)
+    rng = np.random.default_rng(24)
+    cuts = sorted(rng.choice(np.arange(1, N), size=min(6, N - 1),
+                             replace=False).tolist()) if N > 1 else []
+    edges = [0, *cuts, N]
+    inc = 2
+    m = torch.full((M * inc,), float("-inf"), device="cuda")
+    d = torch.zeros(M * inc, device="cuda")
+    for a, b in zip(edges[:-1], edges[1:]):
+        rw.softmax_stats_update(x[:, a:b], m, d, inc=inc)
+    y = torch.full_like(x, float("nan"))
+    ly = torch.full_like(x, float("nan"))
+    for a, b in zip(edges[:-1], edges[1:]):
+        rw.softmax_normalize(x[:, a:b], m, d, y[:, a:b], inc=inc)
+        rw.softmax_normalize(x[:, a:b], m, d, ly[:, a:b], inc=inc, log=True)
+    torch.cuda.synchronize()
+    what = f"normalize {M}x{N} {dtype} windows {edges}"
+    y_ref, m_ref, d_ref, _ = oracle.softmax(x_h)
+    check_m(m[0::inc].cpu().numpy(), m_ref, what)
+    check_d(d[0::inc].cpu().numpy(), d_ref, what)
+    check_y(to_host(y), y_ref, what)
+    check_log(to_host(ly), oracle.log_softmax(x_h), what)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_normalize_in_place_and_special_rows(dtype):
+    # in place, with the state from os_softmax_stats; a row of only -inf
+    # (state (-inf, 0)) comes out NaN, as from the full softmax
+    M, N = 6, 5000
+    v = np.random.default_rng(25).standard_normal((M, N)) * 2.0
+    v[2, :] = -np.inf
+    v[4, 100:] = -np.inf
+    x_h = wl.from_values(v, dtype=dtype)
+    x = to_device(x_h)
+    m = torch.empty(M, device="cuda")
+    d = torch.empty(M, device="cuda")
+    rw.softmax_stats(x, m, d)
+    rw.softmax_normalize(x, m, d, x)
+    torch.cuda.synchronize()
+    y_ref, *_ = oracle.softmax(x_h)
+    yh = to_host(x)
+    keep = [0, 1, 3, 4, 5]
+    check_y(yh[keep], y_ref[keep], f"normalize in place {dtype}")
+    yf = yh.astype(np.float64) if dtype == "f32" else oracle.bf16_bits_to_f64(yh)
+    assert np.all(np.isnan(yf[2]))
+
+
+# ---------------------------------------------------------------------------
 # HIP graph replay: the row ops captured once, replayed on new inputs
 # ---------------------------------------------------------------------------
 
