@@ -518,6 +518,32 @@ def test_cross_entropy_label_edge_cases():
             assert np.isnan(mean.item()) and np.isnan(mean_ref), note
 
 
+@pytest.mark.parametrize("M", [1, 3, 4, 5, 4095, 4097, 32771, 70001])
+@pytest.mark.parametrize("offset", [0, 1])
+def test_cross_entropy_mean_shapes(M, offset):
+    # the mean over row counts around the 4-row groups and the kernel's
+    # batch of 1024 x 4 x 8 rows, with loss and labels 16-byte aligned
+    # (offset 0) or one element off (offset 1: one row at a time); the
+    # oracle's mean over its own losses
+    N = 40
+    x_h = wl.normal(M, N, scale=2.0, seed=26 + M)
+    lab = np.random.default_rng(M).integers(-2, N, size=M).astype(np.int64)
+    x = to_device(x_h)
+    lab_d = torch.empty(M + offset, dtype=torch.int64, device="cuda")
+    lab_d[offset:] = torch.from_numpy(lab).cuda()
+    loss = torch.empty(M + offset, device="cuda")
+    mean = torch.empty(1, device="cuda")
+    rw.cross_entropy_fwd(x, lab_d[offset:], loss[offset:], mean=mean)
+    torch.cuda.synchronize()
+    l_ref, mean_ref = oracle.cross_entropy(x_h, lab)
+    check_log(loss[offset:].cpu().numpy(), l_ref, f"loss M={M}")
+    if np.isnan(mean_ref):
+        assert np.isnan(mean.item())
+    else:
+        # fp32 sums of up to 70001 losses of about 4: relative 1e-5
+        assert abs(mean.item() - mean_ref) <= 1e-5 * abs(mean_ref), (mean.item(), mean_ref)
+
+
 def test_cross_entropy_worked_example():
     # "从原始Softmax到在线Softmax": logits [2, 1, 0.1], class 0 -> loss 0.4170
     x = torch.tensor([[2.0, 1.0, 0.1]], device="cuda")
