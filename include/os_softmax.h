@@ -190,8 +190,10 @@ os_status os_log_softmax_fwd_masked(const void *x, int64_t ld_x, void *y,
 /* Cross-entropy forward from logits ("从原始Softmax到在线Softmax",
  * cross-entropy section): one read of x.
  *  labels    int64 [M] device array, required.  A negative label marks a row
- *            to ignore: its loss is 0 and it is left out of the mean.  A label
- *            >= N gives a NaN loss (and so a NaN mean).
+ *            to ignore: its loss is -0.0 (equal to 0 in any comparison; the
+ *            sign marks the row as left out of the mean, and no computed
+ *            loss is -0.0) and it is left out of the mean.  A label >= N
+ *            gives a NaN loss (and so a NaN mean).
  *  loss_out  fp32 [M], required: lse_i - x_{i,label_i}.
  *  lse_out   fp32 [M], nullable.
  *  mean_out  fp32 scalar, nullable: the mean loss over rows whose label is

@@ -336,7 +336,7 @@ os_status os_cross_entropy_fwd_path(const void *x, int64_t ld_x, int64_t M,
     if (M == 0) {
         // no rows: the mean of nothing is NaN, and it is still an output
         if (mean_out == nullptr) return OS_OK;
-        os::launch_ce_mean(nullptr, nullptr, 0, mean_out, stream);
+        os::launch_ce_mean(nullptr, 0, mean_out, stream);
         return hipGetLastError() == hipSuccess ? OS_OK : OS_ERR_HIP;
     }
     if (x == nullptr || labels == nullptr || loss_out == nullptr)
@@ -350,7 +350,7 @@ os_status os_cross_entropy_fwd_path(const void *x, int64_t ld_x, int64_t M,
     a.loss = loss_out;
     if ((s = launch(a, p, ws)) != OS_OK) return s;
     if (mean_out != nullptr) {
-        os::launch_ce_mean(loss_out, labels, M, mean_out, stream);
+        os::launch_ce_mean(loss_out, M, mean_out, stream);
         if (hipGetLastError() != hipSuccess) return OS_ERR_HIP;
     }
     return OS_OK;

@@ -24,8 +24,10 @@ enum class Out { Prob, LogProb, None };
 // Per-row outputs of pass 1.  m, d and lse are nullable and written at
 // row * inc.  In the cross-entropy kernels (CE = true) labels and loss are
 // required and loss[row] is the cross-entropy of the row against
-// labels[row]: 0 for a negative (ignored) label, NaN for a label >= N, else
-// LSE - x_label.
+// labels[row]: -0.0 for a negative (ignored) label, NaN for a label >= N,
+// else LSE - x_label.  A computed loss, (m - x_c) + log d with both terms
+// >= +0, is never -0.0, so the sign of zero tells the batch mean which rows
+// to leave out without reading the labels again.
 struct StatsOut {
     float *m;
     float *d;
@@ -108,7 +110,7 @@ __device__ __forceinline__ void write_row_stats(const StatsOut &o, int64_t row,
     if constexpr (CE) {
         float l;
         if (t.c < 0) {
-            l = 0.0f;
+            l = -0.0f;
         } else if (t.c >= N) {
             l = __builtin_nanf("");
         } else {
@@ -517,73 +519,69 @@ __global__ __launch_bounds__(kWave *ROWS) void state_merge_kernel(
 
 // ---------------------------------------------------------------------------
 // Batch mean of the cross-entropy ("从原始Softmax到在线Softmax", cross-entropy
-// section: the mean over the batch), over rows whose label is not negative.
-// One workgroup of THREADS lanes, so the result needs no atomics and is
-// deterministic.  When loss and labels are 16-byte aligned, a lane takes
-// groups of 4 consecutive rows (one 16-byte load of losses, two of labels)
-// and keeps up to 8 groups in flight, so a batch of up to THREADS * 32 rows
-// costs one memory round trip; the last M mod 4 rows (and every row when
-// unaligned) go one per lane.  Each lane sums in a fixed order, then a
-// fixed butterfly / LDS order combines the lanes.  NaN when no row counts.
+// section: the mean over the batch), over the rows whose label is not
+// negative: those whose loss is not -0.0, the mark the row kernels leave on
+// ignored rows.  One workgroup of THREADS lanes, so the result needs no
+// atomics and is deterministic.  Only the losses are read (4 B per row).
+// With a 16-byte aligned loss vector a lane takes groups of 4 consecutive
+// rows and keeps as many groups in flight as the rows need, up to 8, so a
+// batch of up to THREADS * 32 rows costs one memory round trip; the last
+// M mod 4 rows (and every row when unaligned) go one per lane.  Each lane
+// sums in a fixed order, then a fixed butterfly / LDS order combines the
+// lanes.  NaN when no row counts.
 // ---------------------------------------------------------------------------
-// Rows [0, 4 M4) of the mean in groups of 4, G groups per lane in flight.
+__device__ __forceinline__ void ce_count(float l, float &s, float &c) {
+    if (__float_as_uint(l) != 0x80000000u) {
+        s += l;
+        c += 1.0f;
+    }
+}
+
+// Rows [0, 4 M4) in groups of 4, G groups per lane in flight.
 template <int THREADS, int G>
-__device__ __forceinline__ void ce_sum_groups(const float4 *l4,
-                                              const longlong2 *b2, int64_t M4,
+__device__ __forceinline__ void ce_sum_groups(const float4 *l4, int64_t M4,
                                               float &s, float &c) {
     for (int64_t g0 = threadIdx.x; g0 < M4; g0 += int64_t(THREADS) * G) {
         // groups past the end load the last group again (no branch, so all
-        // 3 G loads issue back to back) and are not counted
+        // G loads issue back to back) and are not counted
         float4 lv[G];
-        longlong2 la[G], lb[G];
 #pragma unroll
         for (int k = 0; k < G; ++k) {
             const int64_t g = g0 + int64_t(k) * THREADS;
-            const int64_t gc = g < M4 ? g : M4 - 1;
-            lv[k] = l4[gc];
-            la[k] = b2[2 * gc];
-            lb[k] = b2[2 * gc + 1];
+            lv[k] = l4[g < M4 ? g : M4 - 1];
         }
 #pragma unroll
         for (int k = 0; k < G; ++k) {
             if (g0 + int64_t(k) * THREADS < M4) {
-                if (la[k].x >= 0) { s += lv[k].x; c += 1.0f; }
-                if (la[k].y >= 0) { s += lv[k].y; c += 1.0f; }
-                if (lb[k].x >= 0) { s += lv[k].z; c += 1.0f; }
-                if (lb[k].y >= 0) { s += lv[k].w; c += 1.0f; }
+                ce_count(lv[k].x, s, c);
+                ce_count(lv[k].y, s, c);
+                ce_count(lv[k].z, s, c);
+                ce_count(lv[k].w, s, c);
             }
         }
     }
 }
 
 template <int THREADS>
-__global__ __launch_bounds__(THREADS) void ce_mean_kernel(
-    const float *loss, const int64_t *labels, int64_t M, float *mean) {
+__global__ __launch_bounds__(THREADS) void ce_mean_kernel(const float *loss,
+                                                          int64_t M,
+                                                          float *mean) {
     constexpr int WAVES = THREADS / kWave;
     __shared__ float2 lds[WAVES];
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
     float s = 0.0f, c = 0.0f;
     int64_t done = 0;
-    const bool vec = (reinterpret_cast<uintptr_t>(loss) % 16 == 0) &&
-                     (reinterpret_cast<uintptr_t>(labels) % 16 == 0);
-    if (vec) {
+    if (reinterpret_cast<uintptr_t>(loss) % 16 == 0) {
         const int64_t M4 = M / 4;
         const float4 *l4 = reinterpret_cast<const float4 *>(loss);
-        const longlong2 *b2 = reinterpret_cast<const longlong2 *>(labels);
-        // as many groups per lane in flight as the rows need, up to 8
-        if (M4 <= THREADS) ce_sum_groups<THREADS, 1>(l4, b2, M4, s, c);
-        else if (M4 <= 2 * THREADS) ce_sum_groups<THREADS, 2>(l4, b2, M4, s, c);
-        else if (M4 <= 4 * THREADS) ce_sum_groups<THREADS, 4>(l4, b2, M4, s, c);
-        else ce_sum_groups<THREADS, 8>(l4, b2, M4, s, c);
+        if (M4 <= THREADS) ce_sum_groups<THREADS, 1>(l4, M4, s, c);
+        else if (M4 <= 2 * THREADS) ce_sum_groups<THREADS, 2>(l4, M4, s, c);
+        else if (M4 <= 4 * THREADS) ce_sum_groups<THREADS, 4>(l4, M4, s, c);
+        else ce_sum_groups<THREADS, 8>(l4, M4, s, c);
         done = M4 * 4;
     }
-    for (int64_t i = done + threadIdx.x; i < M; i += THREADS) {
-        if (labels[i] >= 0) {
-            s += loss[i];
-            c += 1.0f;
-        }
-    }
+    for (int64_t i = done + threadIdx.x; i < M; i += THREADS) ce_count(loss[i], s, c);
     s = wave_allreduce(s, OpAdd{});
     c = wave_allreduce(c, OpAdd{});
     if (lane == 0) lds[wave] = make_float2(s, c);

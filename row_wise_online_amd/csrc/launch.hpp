@@ -69,8 +69,9 @@ void launch_state_merge(const float *m_in, const float *d_in, int64_t ld,
                         int64_t M, int K, float *m_out, float *d_out,
                         float *lse_out, int64_t inc, hipStream_t stream);
 
-// Mean of loss[i] over rows with labels[i] >= 0 (one workgroup).
-void launch_ce_mean(const float *loss, const int64_t *labels, int64_t M,
-                    float *mean, hipStream_t stream);
+// Mean of loss[i] over the rows not marked ignored (loss -0.0; one
+// workgroup).
+void launch_ce_mean(const float *loss, int64_t M, float *mean,
+                    hipStream_t stream);
 
 }  // namespace os

@@ -184,10 +184,9 @@ void launch_state_merge(const float *m_in, const float *d_in, int64_t ld,
                                                   d_out, inc, so, nullptr, 0, 0);
 }
 
-void launch_ce_mean(const float *loss, const int64_t *labels, int64_t M,
-                    float *mean, hipStream_t stream) {
-    ce_mean_kernel<1024><<<dim3(1), dim3(1024), 0, stream>>>(loss, labels, M,
-                                                             mean);
+void launch_ce_mean(const float *loss, int64_t M, float *mean,
+                    hipStream_t stream) {
+    ce_mean_kernel<1024><<<dim3(1), dim3(1024), 0, stream>>>(loss, M, mean);
 }
 
 }  // namespace os

@@ -544,6 +544,30 @@ def test_cross_entropy_mean_shapes(M, offset):
         assert abs(mean.item() - mean_ref) <= 1e-5 * abs(mean_ref), (mean.item(), mean_ref)
 
 
+@pytest.mark.parametrize("path", ["resident", "stream", "split"])
+def test_cross_entropy_ignored_rows_marked_by_negative_zero(path):
+    # ignored rows carry -0.0 (equal to 0); a row whose loss is exactly +0
+    # (label on the max, every other term below 2^-24 of it) still counts
+    # in the mean, which is taken over the losses alone
+    M, N = 7, 300
+    v = np.random.default_rng(27).standard_normal((M, N))
+    v[3, :] = -200.0
+    v[3, 5] = 0.0
+    x_h = wl.from_values(v)
+    lab = np.array([4, -1, 10, 5, -7, 0, -1], np.int64)
+    x = to_device(x_h)
+    mean = torch.empty(1, device="cuda")
+    loss = rw.cross_entropy_fwd(x, torch.from_numpy(lab).cuda(), mean=mean,
+                                path=path)
+    torch.cuda.synchronize()
+    bits = loss.cpu().numpy().view(np.uint32)
+    assert np.all(bits[lab < 0] == 0x80000000)
+    assert bits[3] == 0 and np.all(bits[lab >= 0] != 0x80000000)
+    l_ref, mean_ref = oracle.cross_entropy(x_h, lab)
+    check_log(loss.cpu().numpy(), l_ref, f"ignored rows {path}")
+    assert abs(mean.item() - mean_ref) <= 1e-6 * abs(mean_ref)
+
+
 def test_cross_entropy_worked_example():
     # "从原始Softmax到在线Softmax": logits [2, 1, 0.1], class 0 -> loss 0.4170
     x = torch.tensor([[2.0, 1.0, 0.1]], device="cuda")
