@@ -797,6 +797,53 @@ def test_normalize_in_place_and_special_rows(dtype):
 
 
 # ---------------------------------------------------------------------------
+# Host threads and streams: the library keeps no host state, so concurrent
+# calls from several threads, each on its own stream, give the bits of the
+# same calls made one after another
+# ---------------------------------------------------------------------------
+
+def test_concurrent_threads_and_streams():
+    import threading
+    shapes = [(300, 5000, "f32", "split"), (700, 1000, "bf16", "resident"),
+              (64, 40000, "f32", "stream"), (2000, 4096, "f32", "auto")]
+    xs = [to_device(wl.normal(M, N, scale=2.0, seed=30 + i, dtype=dt))
+          for i, (M, N, dt, _) in enumerate(shapes)]
+
+    def work(i, stream, reps):
+        M, N, dt, path = shapes[i]
+        x = xs[i]
+        with torch.cuda.stream(stream):
+            m = torch.empty(M, device="cuda")
+            d = torch.empty(M, device="cuda")
+            ws = torch.empty(max(rw.workspace_bytes(M, N, x.dtype, path), 1),
+                             dtype=torch.uint8, device="cuda")
+            y = torch.empty_like(x)
+            for _ in range(reps):
+                rw.softmax_fwd(x, y, m=m, d=d, ws=ws, path=path, stream=stream)
+                z = rw.softmax_normalize(x, m, d, stream=stream)
+        return y, m, d, z
+
+    # one after another on the default stream
+    want = [work(i, torch.cuda.current_stream(), 1) for i in range(len(shapes))]
+    torch.cuda.synchronize()
+    got = [None] * len(shapes)
+    streams = [torch.cuda.Stream() for _ in shapes]
+
+    def run(i):
+        got[i] = work(i, streams[i], 20)
+
+    threads = [threading.Thread(target=run, args=(i,)) for i in range(len(shapes))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    for i in range(len(shapes)):
+        for a, b in zip(got[i], want[i]):
+            assert torch.equal(a, b), f"thread {i} ({shapes[i]}) differs"
+
+
+# ---------------------------------------------------------------------------
 # HIP graph replay: the row ops captured once, replayed on new inputs
 # ---------------------------------------------------------------------------
 
