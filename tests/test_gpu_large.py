@@ -201,3 +201,20 @@ def test_longest_row(dtype, path):
     total = float(y.double().sum())
     assert float(y.min()) >= 0.0
     assert abs(total - 1.0) <= (1e-5 if dtype == "f32" else 2.0 ** -8), total
+
+
+def test_attention_long_key_sequence():
+    # 2^24 keys (262144 tiles of 64, 1 GiB each for K and V at D = 32) for
+    # 300 queries in two blocks: tile indices far past the bench shapes and
+    # a running max that moves over the whole sequence; sampled rows
+    # against the oracle at the derived bound
+    Sq, Sk, D = 300, 1 << 24, 32
+    g = torch.Generator(device="cuda").manual_seed(906)
+    bits = lambda t: t.to(torch.bfloat16).view(torch.int16).cpu().numpy().view(np.uint16)
+    q = bits(2.0 * torch.randn(1, 1, Sq, D, device="cuda", generator=g))
+    k = bits(torch.randn(1, 1, Sk, D, device="cuda", generator=g))
+    v = bits(torch.randn(1, 1, Sk, D, device="cuda", generator=g))
+    print(f"attention Sq{Sq} Sk{Sk} D{D}", flush=True)
+    o, lse = ta.run(q, k, v, out=torch.float32)
+    ta.check(q, k, v, o, lse, bf16_out=False, rows=[0, 255, 256, 299],
+             what="long key sequence")
