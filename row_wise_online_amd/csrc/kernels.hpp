@@ -466,8 +466,8 @@ __global__ __launch_bounds__(kWave *WAVES) void split_normalize_kernel(
 // window need only the final (m, d) of its row, however that state was
 // reached (the statistics of several windows merged, as the split path's
 // second stage does for its chunks, "5.2 CUDA Online Softmax 实现优化" §7.1).
-// Rows are cut into P chunks of C columns as on the split path; workgroup b
-// normalises chunk b % P of row b / P with (m[row * inc], d[row * inc]).
+// Rows are cut into P chunks of C columns; workgroup b normalises chunk
+// b % P of row b / P with (m[row * inc], d[row * inc]).
 // One read and one write per element, both non-temporal.
 // ---------------------------------------------------------------------------
 template <class Tr, bool VEC, int WAVES, int U, Out OUT>

@@ -59,7 +59,8 @@ size_t split_workspace_bytes(int64_t M, int64_t N);
 void launch_split(const FwdArgs &a, void *ws);
 
 // Pass 2 alone (Mode::Prob or Mode::LogProb) with the caller's row state
-// (m, d) at row * inc; rows are cut into chunks as on the split path.
+// (m, d) at row * inc; long rows are cut into chunks of whole multiples of
+// 4096 elements.
 void launch_state_normalize(const FwdArgs &a, const float *sm, const float *sd,
                             int64_t inc);
 
