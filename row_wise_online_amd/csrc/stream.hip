@@ -6,7 +6,11 @@
 namespace os {
 namespace {
 
+// Waves per workgroup: 4 for the two-read passes; 8 for the one-read
+// statistics and cross-entropy pass, which keeps twice the loads in flight
+// per row (fp32 1024 x 32768 statistics 22.1 us against 23.1 us with 4).
 constexpr int kStreamWaves = 4;
+constexpr int kStatsWaves = 8;
 
 // Pass 1 loads are temporal so that the row stays in the Infinity Cache;
 // pass 2 walks the row last tile first (the most recently read lines
@@ -28,10 +32,11 @@ template <class Tr, bool VEC, Out OUT, class Pol, bool CE = false,
 void run(const FwdArgs &a) {
     using E = typename Tr::elem_t;
     constexpr int U = tile_slots<Tr, VEC>();
+    constexpr int WAVES = OUT == Out::None ? kStatsWaves : kStreamWaves;
     const StatsOut so{a.m_out, a.d_out, a.lse_out, a.inc_out, a.labels, a.loss,
                       a.accumulate};
-    stream_kernel<Tr, VEC, kStreamWaves, U, OUT, Pol, CE, MK>
-        <<<dim3(static_cast<unsigned>(a.M)), dim3(kWave * kStreamWaves), 0, a.stream>>>(
+    stream_kernel<Tr, VEC, WAVES, U, OUT, Pol, CE, MK>
+        <<<dim3(static_cast<unsigned>(a.M)), dim3(kWave * WAVES), 0, a.stream>>>(
             static_cast<const E *>(a.x), a.ldx, static_cast<E *>(a.y), a.ldy,
             a.N, so, Mask{a.row_len, a.causal});
 }
