@@ -527,12 +527,18 @@ __global__ __launch_bounds__(kWave *ROWS) void state_merge_kernel(
 // rows and keeps as many groups in flight as the rows need, up to 8, so a
 // batch of up to THREADS * 32 rows costs one memory round trip; the last
 // M mod 4 rows (and every row when unaligned) go one per lane.  Each lane
-// sums in a fixed order, then a fixed butterfly / LDS order combines the
-// lanes.  NaN when no row counts.
+// sums in a fixed order with compensation, then a fixed butterfly / LDS
+// order combines the lanes.  NaN when no row counts.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void ce_count(float l, float &s, float &c) {
+// Adds a row's loss to the lane's compensated sum (s, e: Kahan's running
+// error term, so a lane's many rows keep an fp32 sum within a few units of
+// rounding however long the batch) unless the row is marked ignored.
+__device__ __forceinline__ void ce_count(float l, float &s, float &e, float &c) {
     if (__float_as_uint(l) != 0x80000000u) {
-        s += l;
+        const float y = l - e;
+        const float t = s + y;
+        e = (t - s) - y;
+        s = t;
         c += 1.0f;
     }
 }
@@ -540,7 +546,7 @@ __device__ __forceinline__ void ce_count(float l, float &s, float &c) {
 // Rows [0, 4 M4) in groups of 4, G groups per lane in flight.
 template <int THREADS, int G>
 __device__ __forceinline__ void ce_sum_groups(const float4 *l4, int64_t M4,
-                                              float &s, float &c) {
+                                              float &s, float &e, float &c) {
     for (int64_t g0 = threadIdx.x; g0 < M4; g0 += int64_t(THREADS) * G) {
         // groups past the end load the last group again (no branch, so all
         // G loads issue back to back) and are not counted
@@ -553,10 +559,10 @@ __device__ __forceinline__ void ce_sum_groups(const float4 *l4, int64_t M4,
 #pragma unroll
         for (int k = 0; k < G; ++k) {
             if (g0 + int64_t(k) * THREADS < M4) {
-                ce_count(lv[k].x, s, c);
-                ce_count(lv[k].y, s, c);
-                ce_count(lv[k].z, s, c);
-                ce_count(lv[k].w, s, c);
+                ce_count(lv[k].x, s, e, c);
+                ce_count(lv[k].y, s, e, c);
+                ce_count(lv[k].z, s, e, c);
+                ce_count(lv[k].w, s, e, c);
             }
         }
     }
@@ -570,18 +576,19 @@ __global__ __launch_bounds__(THREADS) void ce_mean_kernel(const float *loss,
     __shared__ float2 lds[WAVES];
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
-    float s = 0.0f, c = 0.0f;
+    float s = 0.0f, e = 0.0f, c = 0.0f;
     int64_t done = 0;
     if (reinterpret_cast<uintptr_t>(loss) % 16 == 0) {
         const int64_t M4 = M / 4;
         const float4 *l4 = reinterpret_cast<const float4 *>(loss);
-        if (M4 <= THREADS) ce_sum_groups<THREADS, 1>(l4, M4, s, c);
-        else if (M4 <= 2 * THREADS) ce_sum_groups<THREADS, 2>(l4, M4, s, c);
-        else if (M4 <= 4 * THREADS) ce_sum_groups<THREADS, 4>(l4, M4, s, c);
-        else ce_sum_groups<THREADS, 8>(l4, M4, s, c);
+        if (M4 <= THREADS) ce_sum_groups<THREADS, 1>(l4, M4, s, e, c);
+        else if (M4 <= 2 * THREADS) ce_sum_groups<THREADS, 2>(l4, M4, s, e, c);
+        else if (M4 <= 4 * THREADS) ce_sum_groups<THREADS, 4>(l4, M4, s, e, c);
+        else ce_sum_groups<THREADS, 8>(l4, M4, s, e, c);
         done = M4 * 4;
     }
-    for (int64_t i = done + threadIdx.x; i < M; i += THREADS) ce_count(loss[i], s, c);
+    for (int64_t i = done + threadIdx.x; i < M; i += THREADS) ce_count(loss[i], s, e, c);
+    s -= e;
     s = wave_allreduce(s, OpAdd{});
     c = wave_allreduce(c, OpAdd{});
     if (lane == 0) lds[wave] = make_float2(s, c);
