@@ -179,8 +179,9 @@ def log_softmax_fwd(x, y=None, *, m=None, d=None, lse=None, ws=None,
 def cross_entropy_fwd(x, labels, loss=None, *, lse=None, mean=None, ws=None,
                       path="auto", stream=None):
     """Per-row cross-entropy of the logits x against int64 labels (negative
-    label: ignored row).  Returns the fp32 loss vector; ``mean`` (a 1-element
-    fp32 tensor) receives the mean over non-ignored rows."""
+    label: ignored row, loss -0.0, which equals 0).  Returns the fp32 loss
+    vector; ``mean`` (a 1-element fp32 tensor) receives the mean over
+    non-ignored rows."""
     torch = _torch()
     lib = _lib.load()
     dt = _dtype_code(x.dtype)
