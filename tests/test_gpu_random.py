@@ -1,6 +1,7 @@
 """Randomised parity cases: each case draws its own shape, dtype, row
 stride, path, value scale and offset, operation (softmax, log-softmax,
-masked rows, statistics) or attention configuration (batch, heads, query
+masked rows, statistics, pass 2 alone over column windows, cross-entropy
+with its mean) or attention configuration (batch, heads, query
 and key lengths, head dimension, causal offset, layout, output dtype) from
 a generator seeded by the case number, and checks the HIP path against the
 fp64 oracle at the same accuracy bars as the fixed cases.  The draws cover
@@ -33,7 +34,8 @@ def _row_case(rng, k):
         path = "auto"
     scale = float(rng.choice([1.0, 4.0, 30.0]))
     offset = float(rng.choice([0.0, 50.0, -1e3]))
-    op = str(rng.choice(["softmax", "log_softmax", "masked", "stats"]))
+    op = str(rng.choice(["softmax", "log_softmax", "masked", "stats",
+                         "normalize", "cross_entropy"]))
     what = (f"case {k}: {op} {dtype} {M}x{N} ld={ld} path={path} "
             f"scale={scale} offset={offset}")
     print(what, flush=True)
@@ -45,6 +47,46 @@ def _row_case(rng, k):
         rw.softmax_stats(x, m, d, lse, path=path)
         torch.cuda.synchronize()
         _, m_ref, d_ref, l_ref = oracle.softmax(x_h, want_y=False)
+    elif op == "normalize":
+        # statistics of random column windows merged at a stride, then each
+        # window normalised with the merged state
+        cuts = sorted(rng.choice(np.arange(1, N), size=min(3, N - 1),
+                                 replace=False).tolist()) if N > 1 else []
+        edges = [0, *cuts, N]
+        inc = int(rng.integers(1, 3))
+        mm = torch.full((M * inc,), float("-inf"), device="cuda")
+        dd = torch.zeros(M * inc, device="cuda")
+        for a, b in zip(edges[:-1], edges[1:]):
+            rw.softmax_stats_update(x[:, a:b], mm, dd, inc=inc)
+        y = torch.full_like(x, float("nan"))
+        ly = torch.full_like(x, float("nan"))
+        for a, b in zip(edges[:-1], edges[1:]):
+            rw.softmax_normalize(x[:, a:b], mm, dd, y[:, a:b], inc=inc)
+            rw.softmax_normalize(x[:, a:b], mm, dd, ly[:, a:b], inc=inc, log=True)
+        torch.cuda.synchronize()
+        what += f" windows {edges} inc={inc}"
+        y_ref, m_ref, d_ref, _ = oracle.softmax(x_h)
+        check_y(to_host(y), y_ref, what)
+        check_log(to_host(ly), oracle.log_softmax(x_h), what)
+        check_m(mm[0::inc].cpu().numpy(), m_ref, what)
+        check_d(dd[0::inc].cpu().numpy(), d_ref, what)
+        return
+    elif op == "cross_entropy":
+        lab = rng.integers(-2, N, size=M).astype(np.int64)
+        mean = torch.empty(1, device="cuda")
+        loss = rw.cross_entropy_fwd(x, torch.from_numpy(lab).cuda(), lse=lse,
+                                    mean=mean, path=path)
+        torch.cuda.synchronize()
+        l_ref, mean_ref = oracle.cross_entropy(x_h, lab)
+        check_log(loss.cpu().numpy(), l_ref, what)
+        if np.isnan(mean_ref):
+            assert np.isnan(mean.item()), what
+        else:
+            assert abs(mean.item() - mean_ref) <= 1e-5 * abs(mean_ref) + 1e-6, \
+                (what, mean.item(), mean_ref)
+        _, _, _, l2 = oracle.softmax(x_h, want_y=False)
+        check_lse(lse.cpu().numpy(), l2, what)
+        return
     elif op == "masked":
         causal = int(rng.integers(0, N + 5)) if rng.random() < 0.5 else None
         rl = (rng.integers(-2, N + 3, size=M).astype(np.int32)
