@@ -218,3 +218,23 @@ def test_attention_long_key_sequence():
     o, lse = ta.run(q, k, v, out=torch.float32)
     ta.check(q, k, v, o, lse, bf16_out=False, rows=[0, 255, 256, 299],
              what="long key sequence")
+
+
+def test_most_rows():
+    # M = 2^31 - 1, the largest row count the entry points take, with one
+    # element per row (8 GiB of x): 512 launches of about 2^22 rows.  A
+    # one-element row has the closed form y = 1, m = x, d = 1, lse = x and
+    # log-softmax 0, checked on every row on the device
+    M = (1 << 31) - 1
+    g = torch.Generator(device="cuda").manual_seed(907)
+    x = torch.randn(M, 1, device="cuda", generator=g)
+    m, d, lse = (torch.empty(M, device="cuda") for _ in range(3))
+    print(f"softmax {M}x1", flush=True)
+    y = rw.softmax_fwd(x, m=m, d=d, lse=lse)
+    torch.cuda.synchronize()
+    assert bool((y == 1.0).all())
+    assert torch.equal(m, x[:, 0]) and bool((d == 1.0).all()) and torch.equal(lse, x[:, 0])
+    del y
+    ly = rw.log_softmax_fwd(x)
+    torch.cuda.synchronize()
+    assert bool((ly == 0.0).all())
