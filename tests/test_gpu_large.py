@@ -238,3 +238,17 @@ def test_most_rows():
     ly = rw.log_softmax_fwd(x)
     torch.cuda.synchronize()
     assert bool((ly == 0.0).all())
+    del ly
+    # statistics, pass 2 alone and the merge of one state per row
+    m.fill_(0.0)
+    d.fill_(0.0)
+    rw.softmax_stats(x, m, d)
+    z = rw.softmax_normalize(x, m, d)
+    torch.cuda.synchronize()
+    assert torch.equal(m, x[:, 0]) and bool((d == 1.0).all())
+    assert bool((z == 1.0).all())
+    del z
+    mo, do = torch.empty_like(m), torch.empty_like(d)
+    rw.state_merge(m.view(M, 1), d.view(M, 1), mo, do, lse)
+    torch.cuda.synchronize()
+    assert torch.equal(mo, m) and torch.equal(do, d) and torch.equal(lse, m)
