@@ -252,3 +252,15 @@ def test_most_rows():
     rw.state_merge(m.view(M, 1), d.view(M, 1), mo, do, lse)
     torch.cuda.synchronize()
     assert torch.equal(mo, m) and torch.equal(do, d) and torch.equal(lse, m)
+    del mo, do
+    # cross-entropy: label 0 is the row's only element, loss (x - x) + log 1
+    # = +0; every third row ignored (-0.0); the mean of the rest is 0
+    labels = torch.zeros(M, dtype=torch.int64, device="cuda")
+    labels[::3] = -1
+    mean = torch.empty(1, device="cuda")
+    loss = rw.cross_entropy_fwd(x, labels, mean=mean)
+    torch.cuda.synchronize()
+    bits = loss.view(torch.int32)
+    assert bool((bits[::3] == -(1 << 31)).all())        # -0.0
+    assert bool((bits[1::3] == 0).all()) and bool((bits[2::3] == 0).all())
+    assert mean.item() == 0.0
