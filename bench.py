@@ -74,7 +74,16 @@ def valid_elements(w, causal):
     return int(__import__("numpy").minimum(w.N, i + causal + 1).sum())
 
 
-def algorithmic_bytes(w, path, n_stats, op="softmax", causal=None):
+def device_cus():
+    """Compute units of the current GPU (256 on MI355X), from torch."""
+    import torch
+    if torch.cuda.is_available():
+        return torch.cuda.get_device_properties(
+            torch.cuda.current_device()).multi_processor_count
+    return 256
+
+
+def algorithmic_bytes(w, path, n_stats, op="softmax", causal=None, cus=None):
     """Bytes the path must move for one step of workload w: x read once per
     read pass (only the unmasked part of each row), y written once (all of
     it), row statistics written; the cross-entropy reads x once and moves
@@ -93,12 +102,14 @@ def algorithmic_bytes(w, path, n_stats, op="softmax", causal=None):
         reads = 1 if path == "resident" else 2
         b = reads * xr + xy + 4 * w.M * n_stats
     if path == "split":
-        b += 2 * rw.workspace_bytes(w.M, w.N, w.dtype, "split")  # states w+r
+        cus = device_cus() if cus is None else cus
+        b += 2 * rw.softmax_plan(w.M, w.N, w.dtype, cus, "split")[
+            "workspace_bytes"]  # partial and row states, written and read
     return b
 
 
 def measure(w, steps, warmup, path="auto", rotate=True, graph=False,
-            op="softmax", causal=None, streams=1, trials=0):
+            op="softmax", causal=None, streams=1, trials=0, keep=False):
     """Average device time per step (ms), the rotation depth, the host time
     per launch (us), and the spread of the launch time (or None).  Steps
     cycle over R buffer sets; with graph=True the launches are captured
@@ -107,7 +118,9 @@ def measure(w, steps, warmup, path="auto", rotate=True, graph=False,
     can start while the previous one drains.  With trials > 0 (plain
     launches on one stream) that many further runs of up to 50 launches,
     each between its own pair of events, follow the timed steps; their
-    per-launch times give the p10 / p50 / p90 spread."""
+    per-launch times give the p10 / p50 / p90 spread.  With keep=True the
+    outputs of the last step on buffer set 0 (every set holds the same x)
+    are copied to the host and returned last, else None."""
     import numpy as np
     import torch
     import row_wise_online_amd as rw
@@ -238,29 +251,169 @@ def measure(w, steps, warmup, path="auto", rotate=True, graph=False,
         torch.cuda.synchronize()
         ms = start.elapsed_time(end) / (reps * per_graph)
         del g
+    outs = None
+    if keep:
+        def host(t):
+            if t is None:
+                return None
+            if t.dtype == torch.bfloat16:
+                return t.view(torch.int16).cpu().numpy().view(np.uint16)
+            return t.cpu().numpy()
+        if op in ("softmax", "log_softmax", "normalize"):
+            outs = {"y": host(ys[0]), "m": host(m), "d": host(d),
+                    "lse": host(lse)}
+        elif op == "stats":
+            outs = {"m": host(m), "d": host(d), "lse": host(lse)}
+        else:
+            outs = {"loss": host(loss), "mean": float(mean.item())}
     del xs, ys
-    return ms, R, host_us, dist
+    return ms, R, host_us, dist, outs
 
 
-def copy_ceiling(nbytes, steps=50):
-    """GB/s of a plain device copy of nbytes (read + write), rotating."""
+def resident_shape(w):
+    """(waves, 16-byte vectors per lane) of the resident kernel the library
+    launches for this row length and dtype (one workgroup per row), if the
+    row is a whole number of its tiles; else None."""
+    E = 4 if w.dtype == "f32" else 8          # elements per 16-byte vector
+    ladder = [(256, 1, 4), (512, 1, 8), (1024, 1, 16), (2048, 4, 8),
+              (4096, 8, 8), (8192, 8, 16), (16384, 8, 32), (32768, 8, 64)]
+    for n_max, waves, epl in ladder:
+        if w.N <= n_max:
+            if epl % E or w.N * w.esize != 16 * 64 * waves * (epl // E):
+                return None
+            return waves, epl // E
+    return None
+
+
+def ceiling_shape(w):
+    """Rows, row bytes, waves and vectors per lane of the ceiling kernels for
+    workload w: the resident kernel's launch shape when it tiles the row
+    exactly, else x cut into 128 KiB rows (512 lanes x 16 vectors)."""
+    rs = resident_shape(w)
+    nbytes = w.M * w.N * w.esize
+    if rs is not None:
+        waves, spl = rs
+        return w.M, w.N * w.esize, waves, spl
+    rb = 16 * 512 * 16
+    if nbytes % rb == 0:
+        return nbytes // rb, rb, 8, 16
+    return None
+
+
+def _time_launches(launch, R, steps, warmup, trials):
+    """Mean device time per launch (us) over `steps` launches cycling over R
+    buffer sets, bracketed by synchronisation and events on the current
+    stream, and the p10 / p50 / p90 of `trials` further runs of up to 50."""
     import torch
-    n = nbytes // 4
-    R = max(2, -(-ROTATE_BYTES // (2 * nbytes)))
-    src = [torch.ones(n, device="cuda") for _ in range(R)]
-    dst = [torch.empty(n, device="cuda") for _ in range(R)]
-    for i in range(5):
-        dst[i % R].copy_(src[i % R])
+    for i in range(warmup):
+        launch(i % R)
     torch.cuda.synchronize()
-    s = torch.cuda.Event(enable_timing=True)
-    e = torch.cuda.Event(enable_timing=True)
-    s.record()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
     for i in range(steps):
-        dst[i % R].copy_(src[i % R])
-    e.record()
-    e.synchronize()
-    ms = s.elapsed_time(e) / steps
-    return 2 * nbytes / (ms * 1e-3) / 1e9
+        launch(i % R)
+    b.record()
+    b.synchronize()
+    mean = a.elapsed_time(b) / steps * 1e3
+    per = max(1, min(steps, 50))
+    evs = [(torch.cuda.Event(enable_timing=True),
+            torch.cuda.Event(enable_timing=True)) for _ in range(trials)]
+    k = 0
+    for e0, e1 in evs:
+        e0.record()
+        for _ in range(per):
+            launch(k % R)
+            k += 1
+        e1.record()
+    torch.cuda.synchronize()
+    us = sorted(e0.elapsed_time(e1) / per * 1e3 for e0, e1 in evs)
+    q = lambda f: round(us[int(f * (len(us) - 1) + 0.5)], 3) if us else None
+    return mean, {"us_p10": q(0.1), "us_p50": q(0.5), "us_p90": q(0.9)}
+
+
+def copy_gbps(nbytes, steps=50):
+    """GB/s (read + write) of the in-tree copy kernel over nbytes, cut into
+    128 KiB rows (512 lanes x 16 vectors), rotating over >= 1 GiB."""
+    import torch
+    import ceiling
+    lib = ceiling.load()
+    rb = 16 * 512 * 16
+    rows = nbytes // rb
+    if rows < 1:
+        return None
+    R = max(2, -(-ROTATE_BYTES // (2 * rows * rb)))
+    src = [torch.ones(rows * rb // 4, device="cuda") for _ in range(R)]
+    dst = [torch.empty(rows * rb // 4, device="cuda") for _ in range(R)]
+    strm = torch.cuda.current_stream().cuda_stream
+    mean, _ = _time_launches(lambda i: ceiling.check(lib.ceil_copy(
+        src[i].data_ptr(), dst[i].data_ptr(), rows, rb, rb, 8, 16, strm),
+        "ceil_copy"), R, steps, 10, 0)
+    return round(2 * rows * rb / (mean * 1e-6) / 1e9, 1)
+
+
+def ceilings(w, steps=200, warmup=400, trials=20):
+    """What this device reaches on the bytes of one softmax launch of
+    workload w, cold (buffer sets rotating over >= 1 GiB), with no
+    arithmetic: the in-tree copy, read-only and write-only kernels in the
+    resident kernel's launch shape (ceiling/ceiling.hip), the runtime's
+    device-to-device copy, torch's copy, and the launch floor (an empty
+    kernel back to back, one workgroup and the workload's grid)."""
+    import torch
+    import ceiling
+    lib = ceiling.load()
+    shape = ceiling_shape(w)
+    nbytes = w.M * w.N * w.esize
+    R = max(2, -(-ROTATE_BYTES // (2 * nbytes)))
+    src = [torch.full((nbytes // 4,), 1.0, device="cuda") for _ in range(R)]
+    dst = [torch.empty(nbytes // 4, device="cuda") for _ in range(R)]
+    sink = torch.zeros(max(shape[0] if shape else 1, 1), device="cuda")
+    strm = torch.cuda.current_stream().cuda_stream
+    out = {"rotating_sets": R}
+
+    def rate(nb, us):
+        return round(nb / (us * 1e-6) / 1e9, 1)
+
+    if shape is not None:
+        rows, rb, waves, spl = shape
+        out["shape"] = {"grid": rows, "threads": 64 * waves,
+                        "vectors_per_lane": spl, "row_bytes": rb}
+        kern = {
+            "copy": (lambda i: ceiling.check(lib.ceil_copy(
+                src[i].data_ptr(), dst[i].data_ptr(), rows, rb, rb, waves,
+                spl, strm), "ceil_copy"), 2 * nbytes),
+            "read": (lambda i: ceiling.check(lib.ceil_read(
+                src[i].data_ptr(), sink.data_ptr(), rows, rb, rb, waves, spl,
+                strm), "ceil_read"), nbytes),
+            "write": (lambda i: ceiling.check(lib.ceil_write(
+                dst[i].data_ptr(), rows, rb, rb, waves, spl, strm),
+                "ceil_write"), nbytes),
+        }
+        for k, (fn, nb) in kern.items():
+            mean, dist = _time_launches(fn, R, steps, warmup, trials)
+            out[k] = {"GBps": rate(nb, mean), "us": round(mean, 3),
+                      "bytes": nb, **dist}
+    mean, dist = _time_launches(lambda i: ceiling.check(lib.ceil_memcpy(
+        dst[i].data_ptr(), src[i].data_ptr(), nbytes, strm), "ceil_memcpy"),
+        R, min(steps, 50), 10, trials)
+    out["hip_memcpy_dtod"] = {"GBps": rate(2 * nbytes, mean),
+                              "us": round(mean, 3), **dist}
+    mean, dist = _time_launches(lambda i: dst[i].copy_(src[i]), R,
+                                min(steps, 50), 10, trials)
+    out["torch_copy"] = {"GBps": rate(2 * nbytes, mean), "us": round(mean, 3),
+                         **dist}
+    floor = {}
+    grids = [(1, 64)]
+    if shape is not None:
+        grids.append((shape[0], 64 * shape[2]))
+    for g, t in grids:
+        mean, dist = _time_launches(lambda i: ceiling.check(
+            lib.ceil_empty(g, t, strm), "ceil_empty"), 1, 1000, 1000, trials)
+        floor[f"{g}x{t}"] = {"us": round(mean, 3), **dist}
+    out["launch_floor"] = floor
+    del src, dst, sink
+    torch.cuda.empty_cache()
+    return out
 
 
 def host_threads():
@@ -301,7 +454,8 @@ def cpu_baseline_parallel(w, n_stats, budget_s):
 
 def cpu_baseline(w, n_stats, budget_s, op="softmax", causal=None):
     """The fp64 oracle, as it is, on this host: whole input matrices of the
-    workload, repeated until about budget_s seconds have passed."""
+    workload, repeated until about budget_s seconds have passed.  Returns
+    the record and the oracle's result (the same every repetition)."""
     import numpy as np
     import oracle
     from row_wise_online_amd import workloads as wl
@@ -334,7 +488,7 @@ def cpu_baseline(w, n_stats, budget_s, op="softmax", causal=None):
         b = 2 * w.M * w.N * w.esize + 4 * w.M * n_stats
     reps, t0 = 0, time.perf_counter()
     while True:
-        fn()
+        ref = fn()
         reps += 1
         el = time.perf_counter() - t0
         if el >= budget_s or reps >= 64:
@@ -344,7 +498,81 @@ def cpu_baseline(w, n_stats, budget_s, op="softmax", causal=None):
             "kind": "oracle",
             "rows_per_s": round(w.M / per, 1),
             "sample": f"{reps} x full {w.M}x{w.N} {w.dtype} matrix, fp64 "
-                      f"{what} oracle, 1 thread, {el:.1f} s"}
+                      f"{what} oracle, 1 thread, {el:.1f} s"}, ref
+
+
+def cpu_leg_accuracy(w, op, ref, outs):
+    """How far the benched step's outputs (every row) are from the oracle's
+    result that the CPU baseline just computed on the same input: max abs
+    and max rel error of y (fp32) or its largest distance in bf16 steps
+    from the correctly rounded value, the largest |lse - lse_ref|, whether
+    m is bit-exact, the largest relative error of d, and of the loss."""
+    import numpy as np
+    import oracle
+    acc = {"rows_checked": w.M, "reference": "fp64 oracle (cpu_baseline leg)"}
+
+    def y_err(y, y_ref, log=False):
+        fin = np.isfinite(y_ref)
+        if y.dtype == np.uint16:
+            want = oracle.round_f64_to_bf16_bits(y_ref[fin])
+            acc["y_max_bf16_ulp"] = int(oracle.bf16_ulp_distance(
+                y[fin], want).max(initial=0))
+            yf = oracle.bf16_bits_to_f64(y[fin])
+        else:
+            yf = y[fin].astype(np.float64)
+        err = np.abs(yf - y_ref[fin])
+        acc["y_max_abs_err"] = float(err.max(initial=0.0))
+        big = np.abs(y_ref[fin]) > (0.0 if log else 1e-30)
+        acc["y_max_rel_err"] = float((err[big] / np.abs(y_ref[fin][big])).max(
+            initial=0.0))
+
+    if op == "softmax":
+        if isinstance(ref, tuple) and len(ref) == 5:      # masked
+            y_ref, _, m_ref, d_ref, l_ref = ref
+        else:
+            y_ref, m_ref, d_ref, l_ref = ref
+        y_err(outs["y"], y_ref)
+    elif op == "log_softmax":
+        if isinstance(ref, tuple):
+            _, y_ref, m_ref, d_ref, l_ref = ref
+        else:
+            y_ref, m_ref, d_ref, l_ref = ref, None, None, None
+        y_err(outs["y"], y_ref, log=True)
+    elif op == "normalize":
+        y_ref, m_ref, d_ref, l_ref = ref
+        y_err(outs["y"], y_ref)
+        m_ref = d_ref = l_ref = None
+    elif op == "stats":
+        _, m_ref, d_ref, l_ref = ref
+    else:
+        l_ref, mean_ref = ref
+        err = np.abs(outs["loss"].astype(np.float64) - l_ref)
+        acc["loss_max_abs_err"] = float(err.max(initial=0.0))
+        acc["mean_rel_err"] = float(abs(outs["mean"] - mean_ref) /
+                                    abs(mean_ref))
+        return acc
+    if outs.get("m") is not None and m_ref is not None:
+        acc["m_bit_exact"] = bool(np.array_equal(
+            outs["m"].astype(np.float64), m_ref))
+    if outs.get("d") is not None and d_ref is not None:
+        acc["d_max_rel_err"] = float(np.max(np.abs(
+            outs["d"].astype(np.float64) - d_ref) / d_ref))
+    if outs.get("lse") is not None and l_ref is not None:
+        acc["lse_max_abs_err"] = float(np.max(np.abs(
+            outs["lse"].astype(np.float64) - l_ref)))
+    return acc
+
+
+def git_sha():
+    """The commit the tree was built from, where git and the repository's
+    history are at hand (a copy of the tree without .git gives None)."""
+    import subprocess
+    try:
+        r = subprocess.run(["git", "-C", ROOT, "rev-parse", "HEAD"],
+                           capture_output=True, text=True, timeout=10)
+    except (OSError, subprocess.SubprocessError):
+        return None
+    return r.stdout.strip() or None if r.returncode == 0 else None
 
 
 def traffic_record(workload):
@@ -381,13 +609,18 @@ def run_workload(name, steps, warmup, path="auto", want_cpu=True,
             raise ValueError("pass 2 alone takes no mask")
     if causal is not None and op == "cross_entropy":
         raise ValueError("the causal mask applies to softmax / log-softmax")
-    ms, R, host_us, dist = measure(w, steps, warmup, path, op=op,
-                                   causal=causal, trials=20 if extras else 0)
+    # the ceilings first: they also bring the clocks up from idle before
+    # the timed steps
+    ceil = ceilings(w) if extras else None
+    ms, R, host_us, dist, outs = measure(w, steps, warmup, path, op=op,
+                                         causal=causal,
+                                         trials=20 if extras else 0,
+                                         keep=want_cpu)
     if extras:
-        graph_ms, _, _, _ = measure(w, steps, warmup, path, graph=True, op=op,
-                                    causal=causal)
-        warm_ms, _, _, _ = measure(w, max(10, steps // 4), 3, path,
-                                   rotate=False, op=op, causal=causal)
+        graph_ms = measure(w, steps, warmup, path, graph=True, op=op,
+                           causal=causal)[0]
+        warm_ms = measure(w, max(10, steps // 4), 3, path, rotate=False,
+                          op=op, causal=causal)[0]
     nbytes = algorithmic_bytes(w, resolved, n_stats, op, causal)
     gbs = nbytes / (ms * 1e-3) / 1e9
     eff = (2 * w.M * w.N * w.esize + 4 * w.M * n_stats) / (ms * 1e-3) / 1e9
@@ -459,7 +692,7 @@ def run_workload(name, steps, warmup, path="auto", want_cpu=True,
             w2 = wl.WORKLOADS[name]
             w2 = type(w2)(w2.name, w2.M, w2.N, w2.dtype, w2.seed, ("y",),
                           w2.desc)
-            ms2, _, _, _ = measure(w2, steps, warmup, path, op=op, streams=2)
+            ms2 = measure(w2, steps, warmup, path, op=op, streams=2)[0]
             b2 = algorithmic_bytes(w2, resolved, 0, op)
             rec["two_stream"] = {
                 "GBps": round(b2 / (ms2 * 1e-3) / 1e9, 1),
@@ -468,10 +701,22 @@ def run_workload(name, steps, warmup, path="auto", want_cpu=True,
                 "ms_per_step": round(ms2, 6),
                 "note": "independent steps alternate over two streams (y "
                         "only); not the headline"}
-    rec["copy_ceiling_GBps"] = round(
-        copy_ceiling(w.M * w.N * w.esize), 1)
+    if ceil is not None:
+        if "copy" in ceil:
+            # the in-tree copy kernel in this launch shape: x read, y written
+            rec["copy_ceiling_GBps"] = ceil["copy"]["GBps"]
+            rec["roofline"]["frac_of_copy_ceiling"] = round(
+                ceil["copy"]["us"] / (ms * 1e3) *
+                nbytes / ceil["copy"]["bytes"], 4)
+        rec["launch_floor_us"] = {k: v["us"] for k, v in
+                                  ceil["launch_floor"].items()}
+        rec["ceilings"] = ceil
+    rec["git_sha"] = git_sha()
     if want_cpu:
-        rec["cpu_baseline"] = cpu_baseline(w, n_stats, cpu_budget, op, causal)
+        base, ref = cpu_baseline(w, n_stats, cpu_budget, op, causal)
+        rec["cpu_baseline"] = base
+        if outs is not None:
+            rec["accuracy"] = cpu_leg_accuracy(w, op, ref, outs)
         if op == "softmax" and causal is None and host_threads() > 1:
             rec["cpu_baseline_parallel"] = cpu_baseline_parallel(
                 w, n_stats, cpu_budget / 2)
@@ -632,8 +877,9 @@ def run_attention(name, steps, warmup, want_cpu=True, cpu_budget=10.0,
     if extras:
         gms, _ = measure_attention(w, steps, 1, graph=True)
         rec["graph_replay_TFLOPs"] = round(flops / (gms * 1e-3) / 1e12, 2)
-    # a plain copy of Q's size: the calibration kernel for the HBM counters
-    rec["copy_ceiling_GBps"] = round(copy_ceiling(w.B * w.H * w.Sq * w.D * 2), 1)
+    # a plain copy of Q's size (the in-tree copy kernel): the calibration
+    # kernel for the HBM counters
+    rec["copy_ceiling_GBps"] = copy_gbps(w.B * w.H * w.Sq * w.D * 2)
     if want_cpu:
         rec["cpu_baseline"] = cpu_baseline_attention(w, cpu_budget)
         if host_threads() > 1:

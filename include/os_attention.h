@@ -72,6 +72,9 @@ extern "C" {
  *  OS_ERR_DTYPE       o_dtype is neither OS_F32 nor OS_BF16;
  *  OS_ERR_UNSUPPORTED D is not 32, 64 or 128, scale is not finite and > 0, or
  *                     a K or V row stride is 2^23 elements or more;
+ * then, once the arguments are valid,
+ *  OS_ERR_DEVICE      no device is current or it is not a gfx950 (read
+ *                     with hipGetDevice, cached per device);
  *  OS_ERR_HIP         the launch failed.
  * Deterministic: the work partition depends on the shape only and no
  * atomics are used. */

@@ -35,8 +35,16 @@
  *    than 2^22 rows are enqueued as launches over consecutive runs of at
  *    most 2^22 rows (a launch counts its threads in 32 bits), with the same
  *    results per row as one launch would give.
- *  - Validation happens on the host, before any HIP call; an invalid call
- *    enqueues nothing.  M == 0 is a valid no-op.
+ *  - Validation happens on the host; an invalid call enqueues nothing.
+ *    Arguments are checked first, before any HIP call (M == 0 is a valid
+ *    no-op).  Then the current device is read (hipGetDevice; its
+ *    compute-unit count and architecture are cached per device on first
+ *    use, thread-safely): OS_ERR_DEVICE unless it is a gfx950.  Last come
+ *    the checks that depend on the device's plan (the workspace size).
+ *    The stream must belong to the current device, as for any launch.
+ *  - Plans: the path AUTO takes, the grids and the workspace size are pure
+ *    functions of the shape and the device's CU count (os_softmax_plan);
+ *    MI355X has 256 CUs, a partitioned device fewer.
  *  - HIP errors: a failed launch returns OS_ERR_HIP (from hipGetLastError,
  *    which may also report an earlier, unrelated error left on the thread).
  *  - Alignment is never an error: 16-byte vector memory operations are used
@@ -45,7 +53,7 @@
  *  - Aliasing: y == x with ld_y == ld_x (in place) is allowed; any other
  *    overlap between inputs and outputs is undefined.
  *  - Determinism: the work partition is a pure function of (M, N, dtype,
- *    path, alignment class) and no atomics are used, so repeated calls give
+ *    path, alignment class, CU count) and no atomics are used, so repeated calls give
  *    bit-identical results.  Different paths round differently (within the
  *    documented accuracy).
  *  - Special values: an element -inf has weight 0; a row of only -inf gives
@@ -74,7 +82,10 @@ typedef enum {
     OS_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required */
     OS_ERR_PATH = 6,        /* unknown path value */
     OS_ERR_UNSUPPORTED = 7, /* forced path cannot take this shape */
-    OS_ERR_HIP = 8          /* a HIP launch reported an error */
+    OS_ERR_HIP = 8,         /* a HIP launch reported an error */
+    OS_ERR_DEVICE = 9       /* no current device, or it is not a gfx950 (the
+                               only architecture the kernels are built for);
+                               os_softmax_plan: cu_count < 1 */
 } os_status;
 
 typedef enum { OS_F32 = 0, OS_BF16 = 1 } os_dtype;
@@ -271,24 +282,56 @@ os_status os_state_merge(const float *m_in, const float *d_in, int64_t ld_in,
                          int64_t M, int64_t K, float *m_out, float *d_out,
                          float *lse_out, hipStream_t stream);
 
+/* The launch plan of a row-wise call, as os_softmax_plan describes it. */
+typedef struct {
+    os_path path;            /* the path taken (AUTO resolved) */
+    int32_t chunks_per_row;  /* SPLIT: workgroups per row (P); else 1 */
+    int64_t chunk_len;       /* SPLIT: elements per chunk (C, the last
+                                chunk of a row shorter); else N */
+    size_t workspace_bytes;  /* workspace the call needs (0 unless SPLIT) */
+} os_plan;
+
+/* The plan of a row-wise call of shape (M, N, dt) on `path` for a device
+ * with cu_count compute units.  read_only != 0: the statistics and
+ * cross-entropy entry points (their AUTO rule streams rows longer than
+ * 16384 elements when rows are many), else softmax / log-softmax.
+ * A pure host function (no HIP call), for sizing buffers ahead of time and
+ * for checking the plans on a machine without a GPU.  The rules, scaled by
+ * cu_count (MI355X: 256):
+ *   AUTO     RESIDENT when N <= 32768 and (M >= 2 cu_count or N <= 4096),
+ *            except read-only calls with N > 16384 and M >= 2 cu_count,
+ *            which STREAM; otherwise STREAM when M >= 2 cu_count, else
+ *            SPLIT.
+ *   SPLIT    rows cut into chunks of a multiple of 4096 elements, about
+ *            8 cu_count workgroups in all ("5.2 CUDA Online Softmax 实现
+ *            优化" §7.1, several blocks per long row and a second stage);
+ *            workspace: two tables of M P floats and two of M floats, each
+ *            rounded up to 256 bytes.
+ * Errors: OS_ERR_DTYPE, OS_ERR_SHAPE, OS_ERR_PATH, OS_ERR_NULL (out),
+ * OS_ERR_DEVICE (cu_count < 1), OS_ERR_UNSUPPORTED (RESIDENT with
+ * N > 32768). */
+os_status os_softmax_plan(int64_t M, int64_t N, os_dtype dt, os_path path,
+                          int read_only, int cu_count, os_plan *out);
+
 /* Workspace bytes that every row-wise entry point (softmax, log-softmax,
- * statistics, cross-entropy) needs for this shape and path (0 unless the
- * split path is taken).  A pure function of its arguments; returns 0 for
- * invalid arguments. */
+ * statistics, cross-entropy) needs for this shape and path on the current
+ * device (0 unless the split path is taken): os_softmax_plan for the
+ * device's CU count.  Returns 0 for invalid arguments, and when no gfx950
+ * device is current (a call would then fail with OS_ERR_DEVICE). */
 size_t os_softmax_workspace_bytes(int64_t M, int64_t N, os_dtype dt,
                                   os_path path);
 
-/* The path AUTO resolves to at this shape for the softmax and log-softmax
- * entry points, masked or not (host only).  OS_PATH_AUTO for an invalid
- * shape or dtype. */
+/* The path AUTO resolves to at this shape on the current device for the
+ * softmax and log-softmax entry points, masked or not.  OS_PATH_AUTO for
+ * an invalid shape or dtype, or when no gfx950 device is current. */
 os_path os_softmax_select_path(int64_t M, int64_t N, os_dtype dt);
 
 /* The path AUTO resolves to for the read-only entry points
  * (os_softmax_stats*, os_softmax_stats_update, os_cross_entropy_fwd*):
- * that of os_softmax_select_path, except that with 512 rows or more, rows
- * longer than 16384 elements take STREAM rather than RESIDENT (nothing is
- * kept for a pass 2).  The workspace size is the same either way (host
- * only; OS_PATH_AUTO for an invalid shape or dtype). */
+ * that of os_softmax_select_path, except that with 2 rows per CU or more,
+ * rows longer than 16384 elements take STREAM rather than RESIDENT (nothing
+ * is kept for a pass 2).  The workspace size is the same either way
+ * (OS_PATH_AUTO for an invalid shape or dtype, or no gfx950 device). */
 os_path os_softmax_stats_select_path(int64_t M, int64_t N, os_dtype dt);
 
 /* Static description of a status code (never NULL). */

@@ -30,7 +30,8 @@ __all__ = ["softmax_fwd", "log_softmax_fwd", "cross_entropy_fwd",
            "prepare_fwd", "prepare_cross_entropy", "prepare_stats",
            "softmax_stats",
            "softmax_stats_update", "softmax_normalize", "prepare_normalize",
-           "state_merge", "workspace_bytes", "select_path", "OsError", "load",
+           "state_merge", "workspace_bytes", "select_path", "softmax_plan",
+           "OsError", "load",
            "attention_fwd", "prepare_attention"]
 
 
@@ -91,6 +92,18 @@ def _stream(stream):
     return s.cuda_stream
 
 
+def _on(stream):
+    """Context in which tensors the binding allocates for a call belong to
+    the stream the call is launched on.  PyTorch's caching allocator reuses
+    a freed block only for allocations on the stream that owns it, in that
+    stream's order, so a workspace (or output) freed after the call cannot
+    be handed to other work while the call's kernels still use it."""
+    import contextlib
+    if stream is None:
+        return contextlib.nullcontext()
+    return _torch().cuda.stream(stream)
+
+
 def _path_code(path):
     if isinstance(path, str):
         return _lib.PATHS[path]
@@ -102,6 +115,23 @@ def workspace_bytes(M, N, dtype, path="auto"):
         M, N, _dtype_code_any(dtype), _path_code(path))
 
 
+def softmax_plan(M, N, dtype, cu_count, path="auto", op="softmax"):
+    """The launch plan (os_softmax_plan) of a call of shape (M, N) on a
+    device with cu_count compute units: a dict with the path, the split
+    path's chunks per row and chunk length, and the workspace bytes.  op
+    "stats" or "cross_entropy" takes the read-only entry points' rule."""
+    plan = _lib.Plan()
+    st = _lib.load().os_softmax_plan(
+        int(M), int(N), _dtype_code_any(dtype), _path_code(path),
+        1 if op in ("stats", "cross_entropy") else 0, int(cu_count),
+        ctypes.byref(plan))
+    _lib.check("os_softmax_plan", st)
+    return {"path": _lib.PATH_NAMES[plan.path],
+            "chunks_per_row": plan.chunks_per_row,
+            "chunk_len": plan.chunk_len,
+            "workspace_bytes": plan.workspace_bytes}
+
+
 def select_path(M, N, dtype, op="softmax"):
     """The path AUTO takes at this shape: for softmax / log-softmax, or,
     with op "stats" or "cross_entropy", for the read-only entry points."""
@@ -111,14 +141,18 @@ def select_path(M, N, dtype, op="softmax"):
         int(M), int(N), _dtype_code_any(dtype))]
 
 
-def _workspace(ws, need, device):
+def _workspace(ws, need, device, stream=None):
+    """(pointer, bytes, tensor) of the call's workspace: the caller's, or
+    one allocated here on the launch stream when the path needs one.  The
+    caller of this helper keeps the tensor referenced until the C call has
+    returned (its kernels are then ordered on that stream)."""
     torch = _torch()
-    if need == 0:
-        return (ws.data_ptr() if ws is not None else None), (
-            ws.numel() if ws is not None else 0)
     if ws is None:
-        ws = torch.empty(need, dtype=torch.uint8, device=device)
-    return ws.data_ptr(), ws.numel() * ws.element_size()
+        if need == 0:
+            return None, 0, None
+        with _on(stream):
+            ws = torch.empty(need, dtype=torch.uint8, device=device)
+    return ws.data_ptr(), ws.numel() * ws.element_size(), ws
 
 
 def _fwd(fn_name, x, y, m, d, lse, ws, path, stream, row_len=None,
@@ -127,7 +161,8 @@ def _fwd(fn_name, x, y, m, d, lse, ws, path, stream, row_len=None,
     lib = _lib.load()
     dt = _dtype_code(x.dtype)
     if y is None:
-        y = torch.empty_like(x)
+        with _on(stream):
+            y = torch.empty_like(x)
     if y.dtype != x.dtype or y.shape != x.shape:
         raise ValueError("y must have the dtype and shape of x")
     xp, ldx = _matrix(x, "x")
@@ -135,7 +170,7 @@ def _fwd(fn_name, x, y, m, d, lse, ws, path, stream, row_len=None,
     M, N = x.shape
     pc = _path_code(path)
     need = lib.os_softmax_workspace_bytes(M, N, dt, pc)
-    wp, wb = _workspace(ws, need, x.device)
+    wp, wb, ws = _workspace(ws, need, x.device, stream)
     if row_len is None and causal is None:
         st = getattr(lib, fn_name)(xp, ldx, yp, ldy, M, N, dt,
                                    _vec(m, "m", M), _vec(d, "d", M),
@@ -155,6 +190,7 @@ def _fwd(fn_name, x, y, m, d, lse, ws, path, stream, row_len=None,
             -1 if causal is None else int(causal), _vec(m, "m", M),
             _vec(d, "d", M), _vec(lse, "lse", M), wp, wb, pc,
             _stream(stream))
+    del ws  # released only now that the call's kernels are enqueued
     _lib.check(fn_name, st)
     return y
 
@@ -191,14 +227,16 @@ def cross_entropy_fwd(x, labels, loss=None, *, lse=None, mean=None, ws=None,
             or labels.numel() != M or labels.stride(0) != 1:
         raise ValueError("labels must be a contiguous int64 GPU vector of M")
     if loss is None:
-        loss = torch.empty(M, dtype=torch.float32, device=x.device)
+        with _on(stream):
+            loss = torch.empty(M, dtype=torch.float32, device=x.device)
     pc = _path_code(path)
     need = lib.os_softmax_workspace_bytes(M, N, dt, pc)
-    wp, wb = _workspace(ws, need, x.device)
+    wp, wb, ws = _workspace(ws, need, x.device, stream)
     st = lib.os_cross_entropy_fwd_path(
         xp, ldx, M, N, dt, labels.data_ptr(), _vec(loss, "loss", M),
         _vec(lse, "lse", M), _vec(mean, "mean", 1), wp, wb, pc,
         _stream(stream))
+    del ws
     _lib.check("os_cross_entropy_fwd_path", st)
     return loss
 
@@ -220,7 +258,7 @@ def prepare_fwd(x, y, *, m=None, d=None, lse=None, ws=None, path="auto",
     need = lib.os_softmax_workspace_bytes(M, N, dt, pc)
     if need and ws is None:
         raise ValueError(f"path needs a workspace of {need} bytes")
-    wp, wb = _workspace(ws, need, x.device)
+    wp, wb, ws = _workspace(ws, need, x.device)
     stats = (_vec(m, "m", M), _vec(d, "d", M), _vec(lse, "lse", M))
     name = "os_log_softmax_fwd_path" if log else "os_softmax_fwd_path"
     if causal is None:
@@ -257,7 +295,7 @@ def prepare_cross_entropy(x, labels, loss, *, lse=None, mean=None, ws=None,
     need = lib.os_softmax_workspace_bytes(M, N, dt, pc)
     if need and ws is None:
         raise ValueError(f"path needs a workspace of {need} bytes")
-    wp, wb = _workspace(ws, need, x.device)
+    wp, wb, ws = _workspace(ws, need, x.device)
     args = (xp, ldx, M, N, dt, labels.data_ptr(), _vec(loss, "loss", M),
             _vec(lse, "lse", M), _vec(mean, "mean", 1), wp, wb, pc,
             _stream(stream))
@@ -282,7 +320,7 @@ def prepare_stats(x, m, d, lse=None, *, ws=None, path="auto", stream=None):
     need = lib.os_softmax_workspace_bytes(M, N, dt, pc)
     if need and ws is None:
         raise ValueError(f"path needs a workspace of {need} bytes")
-    wp, wb = _workspace(ws, need, x.device)
+    wp, wb, ws = _workspace(ws, need, x.device)
     args = (xp, ldx, M, N, dt, _vec(m, "m", M), _vec(d, "d", M), 1,
             _vec(lse, "lse", M), wp, wb, pc, _stream(stream))
     fn = lib.os_softmax_stats_path
@@ -305,11 +343,12 @@ def softmax_stats(x, m, d, lse=None, *, inc=1, ws=None, path="auto",
     M, N = x.shape
     pc = _path_code(path)
     need = lib.os_softmax_workspace_bytes(M, N, dt, pc)
-    wp, wb = _workspace(ws, need, x.device)
+    wp, wb, ws = _workspace(ws, need, x.device, stream)
     st = lib.os_softmax_stats_path(xp, ldx, M, N, dt, _vec(m, "m", M, inc),
                                    _vec(d, "d", M, inc),
                                    inc, _vec(lse, "lse", M, inc), wp, wb, pc,
                                    _stream(stream))
+    del ws
     _lib.check("os_softmax_stats_path", st)
 
 
@@ -323,11 +362,12 @@ def softmax_stats_update(x, m, d, lse=None, *, inc=1, ws=None, path="auto",
     M, N = x.shape
     pc = _path_code(path)
     need = lib.os_softmax_workspace_bytes(M, N, dt, pc)
-    wp, wb = _workspace(ws, need, x.device)
+    wp, wb, ws = _workspace(ws, need, x.device, stream)
     st = lib.os_softmax_stats_update(xp, ldx, M, N, dt, _vec(m, "m", M, inc),
                                      _vec(d, "d", M, inc), inc,
                                      _vec(lse, "lse", M, inc), wp, wb, pc,
                                      _stream(stream))
+    del ws
     _lib.check("os_softmax_stats_update", st)
 
 
@@ -340,7 +380,8 @@ def softmax_normalize(x, m, d, y=None, *, inc=1, log=False, stream=None):
     lib = _lib.load()
     dt = _dtype_code(x.dtype)
     if y is None:
-        y = torch.empty_like(x)
+        with _on(stream):
+            y = torch.empty_like(x)
     if y.dtype != x.dtype or y.shape != x.shape:
         raise ValueError("y must have the dtype and shape of x")
     xp, ldx = _matrix(x, "x")
@@ -456,8 +497,9 @@ def attention_fwd(q, k, v, o=None, *, lse=None, scale=None, causal_offset=-1,
     bf16, when not given)."""
     torch = _torch()
     if o is None:
-        o = torch.empty(q.shape, dtype=out_dtype or torch.bfloat16,
-                        device=q.device)
+        with _on(stream):
+            o = torch.empty(q.shape, dtype=out_dtype or torch.bfloat16,
+                            device=q.device)
     prepare_attention(q, k, v, o, lse=lse, scale=scale,
                       causal_offset=causal_offset, stream=stream)()
     return o

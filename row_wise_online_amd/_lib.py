@@ -17,7 +17,7 @@ OS_OK = 0
 STATUS_NAMES = {
     0: "OS_OK", 1: "OS_ERR_NULL", 2: "OS_ERR_SHAPE", 3: "OS_ERR_STRIDE",
     4: "OS_ERR_DTYPE", 5: "OS_ERR_WORKSPACE", 6: "OS_ERR_PATH",
-    7: "OS_ERR_UNSUPPORTED", 8: "OS_ERR_HIP",
+    7: "OS_ERR_UNSUPPORTED", 8: "OS_ERR_HIP", 9: "OS_ERR_DEVICE",
 }
 # os_dtype
 OS_F32 = 0
@@ -25,6 +25,15 @@ OS_BF16 = 1
 # os_path
 PATHS = {"auto": 0, "resident": 1, "stream": 2, "split": 3}
 PATH_NAMES = {v: k for k, v in PATHS.items()}
+
+
+
+class Plan(ctypes.Structure):
+    """os_plan: the launch plan of a row-wise call."""
+    _fields_ = [("path", ctypes.c_int), ("chunks_per_row", ctypes.c_int32),
+                ("chunk_len", ctypes.c_int64),
+                ("workspace_bytes", ctypes.c_size_t)]
+
 
 # Every function the header declares, with its ctypes signature.
 _vp, _i64, _i32, _sz = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
@@ -63,6 +72,8 @@ SIGNATURES = {
     "os_log_softmax_normalize": (_i32, [_vp, _i64, _vp, _i64, _i64, _i64,
                                         _i32, _vp, _vp, _i64, _vp]),
     "os_softmax_workspace_bytes": (_sz, [_i64, _i64, _i32, _i32]),
+    "os_softmax_plan": (_i32, [_i64, _i64, _i32, _i32, _i32, _i32,
+                               ctypes.POINTER(Plan)]),
     "os_softmax_select_path": (_i32, [_i64, _i64, _i32]),
     "os_softmax_stats_select_path": (_i32, [_i64, _i64, _i32]),
     "os_status_string": (ctypes.c_char_p, [_i32]),

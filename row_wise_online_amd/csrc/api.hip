@@ -11,30 +11,6 @@ namespace {
 constexpr int64_t kMaxN = int64_t(1) << 30;  // keeps in-row int indexing exact
 constexpr int64_t kMaxM = (int64_t(1) << 31) - 1;
 
-// AUTO rule (pure function of the shape, tuned for 256 CUs):
-//  - rows that fit in registers go resident, unless they are long and so
-//    few that one workgroup per row would leave most CUs idle;
-//  - longer rows with many rows stream, one workgroup per row;
-//  - few long rows are split across workgroups.
-// The read-only passes (statistics, cross-entropy) follow the same rule,
-// except that with many rows they stream rows longer than 16384 elements:
-// they keep nothing for a pass 2, and the streaming fold has more loads in
-// flight than the resident kernel sized for one (MI355X, fp32 1024 x 32768
-// statistics: 23.1 us streamed against 26.9 us resident).
-constexpr int64_t kManyRows = 512;
-constexpr int64_t kShortRow = 4096;
-constexpr int64_t kReadOnlyResidentMax = 16384;
-
-os_path select_path(int64_t M, int64_t N, bool read_only = false) {
-    if (N <= os::kResidentMaxN && (M >= kManyRows || N <= kShortRow)) {
-        if (read_only && N > kReadOnlyResidentMax && M >= kManyRows)
-            return OS_PATH_STREAM;
-        return OS_PATH_RESIDENT;
-    }
-    if (M >= kManyRows) return OS_PATH_STREAM;
-    return OS_PATH_SPLIT;
-}
-
 int esize(os_dtype dt) { return dt == OS_BF16 ? 2 : 4; }
 
 bool aligned16(const void *p, int64_t ld, os_dtype dt) {
@@ -50,21 +26,32 @@ os_status check_shape(int64_t M, int64_t N, os_dtype dt) {
 
 bool valid_path(os_path p) { return p >= OS_PATH_AUTO && p <= OS_PATH_SPLIT; }
 
-size_t workspace_for(int64_t M, int64_t N, os_path resolved) {
-    return (resolved == OS_PATH_SPLIT && M > 0) ? os::split_workspace_bytes(M, N)
-                                                : 0;
+// The current device, if it is one the kernels run on.
+const os::Device *usable_device() {
+    const os::Device *dev = os::current_device();
+    return (dev != nullptr && dev->gfx950) ? dev : nullptr;
 }
 
 // Validation shared by every row-wise entry point once the pointers that
-// the mode requires are known to be present.  Resolves AUTO and checks the
-// forced path and the workspace.
+// the mode requires are known to be present.  What does not depend on the
+// device is checked first, before any HIP call: the forced path's shape
+// limit, and a split path forced without a workspace.  Then the current
+// device (OS_ERR_DEVICE unless it is a gfx950), AUTO resolved for its CU
+// count, and the workspace size of that plan.
 os_status resolve(int64_t M, int64_t N, os_path path, void *ws,
-                  size_t ws_bytes, os_path *out, bool read_only = false) {
-    const os_path p = (path == OS_PATH_AUTO) ? select_path(M, N, read_only) : path;
-    if (p == OS_PATH_RESIDENT && N > os::kResidentMaxN) return OS_ERR_UNSUPPORTED;
-    const size_t need = workspace_for(M, N, p);
+                  size_t ws_bytes, os_path *out, int *cus,
+                  bool read_only = false) {
+    if (path == OS_PATH_RESIDENT && N > os::kResidentMaxN) return OS_ERR_UNSUPPORTED;
+    if (path == OS_PATH_SPLIT && ws == nullptr) return OS_ERR_WORKSPACE;
+    const os::Device *dev = usable_device();
+    if (dev == nullptr) return OS_ERR_DEVICE;
+    const os_path p = (path == OS_PATH_AUTO)
+                          ? os::select_path(M, N, read_only, dev->cus)
+                          : path;
+    const size_t need = os::workspace_for(M, N, p, dev->cus);
     if (need > 0 && (ws == nullptr || ws_bytes < need)) return OS_ERR_WORKSPACE;
     *out = p;
+    *cus = dev->cus;
     return OS_OK;
 }
 
@@ -107,7 +94,7 @@ os_status launch(const os::FwdArgs &a, os_path p, void *ws) {
 
 os::FwdArgs make_args(const void *x, int64_t ld_x, void *y, int64_t ld_y,
                       int64_t M, int64_t N, os_dtype dt, os::Mode mode,
-                      hipStream_t stream) {
+                      int cus, hipStream_t stream) {
     os::FwdArgs a{};
     a.x = x;
     a.ldx = ld_x;
@@ -120,6 +107,7 @@ os::FwdArgs make_args(const void *x, int64_t ld_x, void *y, int64_t ld_y,
     a.causal = -1;
     a.dt = dt == OS_F32 ? os::Dt::F32 : os::Dt::BF16;
     a.vec = aligned16(x, ld_x, dt) && (y == nullptr || aligned16(y, ld_y, dt));
+    a.cus = cus;
     a.stream = stream;
     return a;
 }
@@ -137,8 +125,9 @@ os_status fwd(os::Mode mode, const void *x, int64_t ld_x, void *y,
     if (M == 0) return OS_OK;
     if (x == nullptr || y == nullptr) return OS_ERR_NULL;
     os_path p;
-    if ((s = resolve(M, N, path, ws, ws_bytes, &p)) != OS_OK) return s;
-    os::FwdArgs a = make_args(x, ld_x, y, ld_y, M, N, dt, mode, stream);
+    int cus;
+    if ((s = resolve(M, N, path, ws, ws_bytes, &p, &cus)) != OS_OK) return s;
+    os::FwdArgs a = make_args(x, ld_x, y, ld_y, M, N, dt, mode, cus, stream);
     a.m_out = m_out;
     a.d_out = d_out;
     a.lse_out = lse_out;
@@ -153,20 +142,53 @@ os_status fwd(os::Mode mode, const void *x, int64_t ld_x, void *y,
 
 extern "C" {
 
+os_status os_softmax_plan(int64_t M, int64_t N, os_dtype dt, os_path path,
+                          int read_only, int cu_count, os_plan *out) {
+    os_status s = check_shape(M, N, dt);
+    if (s != OS_OK) return s;
+    if (!valid_path(path)) return OS_ERR_PATH;
+    if (out == nullptr) return OS_ERR_NULL;
+    if (cu_count < 1) return OS_ERR_DEVICE;
+    if (path == OS_PATH_RESIDENT && N > os::kResidentMaxN) return OS_ERR_UNSUPPORTED;
+    const os_path p = (path == OS_PATH_AUTO)
+                          ? os::select_path(M, N, read_only != 0, cu_count)
+                          : path;
+    out->path = p;
+    out->chunks_per_row = 1;
+    out->chunk_len = N;
+    if (p == OS_PATH_SPLIT) {
+        const os::SplitPlan sp = os::split_plan(M, N, cu_count);
+        out->chunks_per_row = sp.P;
+        out->chunk_len = sp.C;
+    }
+    out->workspace_bytes = os::workspace_for(M, N, p, cu_count);
+    return OS_OK;
+}
+
 os_path os_softmax_select_path(int64_t M, int64_t N, os_dtype dt) {
     if (check_shape(M, N, dt) != OS_OK) return OS_PATH_AUTO;
-    return select_path(M, N);
+    const os::Device *dev = usable_device();
+    if (dev == nullptr) return OS_PATH_AUTO;
+    return os::select_path(M, N, false, dev->cus);
 }
 
 os_path os_softmax_stats_select_path(int64_t M, int64_t N, os_dtype dt) {
     if (check_shape(M, N, dt) != OS_OK) return OS_PATH_AUTO;
-    return select_path(M, N, true);
+    const os::Device *dev = usable_device();
+    if (dev == nullptr) return OS_PATH_AUTO;
+    return os::select_path(M, N, true, dev->cus);
 }
 
 size_t os_softmax_workspace_bytes(int64_t M, int64_t N, os_dtype dt,
                                   os_path path) {
     if (check_shape(M, N, dt) != OS_OK || !valid_path(path)) return 0;
-    return workspace_for(M, N, path == OS_PATH_AUTO ? select_path(M, N) : path);
+    if (path == OS_PATH_RESIDENT) return 0;
+    const os::Device *dev = usable_device();
+    if (dev == nullptr) return 0;
+    const os_path p = path == OS_PATH_AUTO
+                          ? os::select_path(M, N, false, dev->cus)
+                          : path;
+    return os::workspace_for(M, N, p, dev->cus);
 }
 
 os_status os_softmax_fwd_path(const void *x, int64_t ld_x, void *y,
@@ -239,7 +261,10 @@ os_status normalize(os::Mode mode, const void *x, int64_t ld_x, void *y,
     if (M == 0) return OS_OK;
     if (x == nullptr || y == nullptr || m_in == nullptr || d_in == nullptr)
         return OS_ERR_NULL;
-    const os::FwdArgs a = make_args(x, ld_x, y, ld_y, M, N, dt, mode, stream);
+    const os::Device *dev = usable_device();
+    if (dev == nullptr) return OS_ERR_DEVICE;
+    const os::FwdArgs a = make_args(x, ld_x, y, ld_y, M, N, dt, mode, dev->cus,
+                                    stream);
     const os::RowChunks rc = os::row_chunks(M);
     for (int64_t c = 0; c < rc.count; ++c) {
         const int64_t r0 = c * rc.rows;
@@ -284,9 +309,10 @@ os_status stats(const void *x, int64_t ld_x, int64_t M, int64_t N,
     if (M == 0) return OS_OK;
     if (x == nullptr || m_out == nullptr || d_out == nullptr) return OS_ERR_NULL;
     os_path p;
-    if ((s = resolve(M, N, path, ws, ws_bytes, &p, true)) != OS_OK) return s;
+    int cus;
+    if ((s = resolve(M, N, path, ws, ws_bytes, &p, &cus, true)) != OS_OK) return s;
     os::FwdArgs a = make_args(x, ld_x, nullptr, 0, M, N, dt, os::Mode::Stats,
-                              stream);
+                              cus, stream);
     a.m_out = m_out;
     a.d_out = d_out;
     a.lse_out = lse_out;
@@ -336,15 +362,17 @@ os_status os_cross_entropy_fwd_path(const void *x, int64_t ld_x, int64_t M,
     if (M == 0) {
         // no rows: the mean of nothing is NaN, and it is still an output
         if (mean_out == nullptr) return OS_OK;
+        if (usable_device() == nullptr) return OS_ERR_DEVICE;
         os::launch_ce_mean(nullptr, 0, mean_out, stream);
         return hipGetLastError() == hipSuccess ? OS_OK : OS_ERR_HIP;
     }
     if (x == nullptr || labels == nullptr || loss_out == nullptr)
         return OS_ERR_NULL;
     os_path p;
-    if ((s = resolve(M, N, path, ws, ws_bytes, &p, true)) != OS_OK) return s;
+    int cus;
+    if ((s = resolve(M, N, path, ws, ws_bytes, &p, &cus, true)) != OS_OK) return s;
     os::FwdArgs a = make_args(x, ld_x, nullptr, 0, M, N, dt, os::Mode::Stats,
-                              stream);
+                              cus, stream);
     a.lse_out = lse_out;
     a.labels = labels;
     a.loss = loss_out;
@@ -375,6 +403,7 @@ os_status os_state_merge(const float *m_in, const float *d_in, int64_t ld_in,
     if (m_in == nullptr || d_in == nullptr || m_out == nullptr ||
         d_out == nullptr)
         return OS_ERR_NULL;
+    if (usable_device() == nullptr) return OS_ERR_DEVICE;
     const os::RowChunks rc = os::row_chunks(M);
     for (int64_t c = 0; c < rc.count; ++c) {
         const int64_t r0 = c * rc.rows;
@@ -398,6 +427,7 @@ const char *os_status_string(os_status s) {
         case OS_ERR_PATH: return "OS_ERR_PATH: unknown path";
         case OS_ERR_UNSUPPORTED: return "OS_ERR_UNSUPPORTED: the forced path cannot take this shape";
         case OS_ERR_HIP: return "OS_ERR_HIP: a HIP launch failed";
+        case OS_ERR_DEVICE: return "OS_ERR_DEVICE: no current device, or it is not a gfx950 (or the cu_count given is < 1)";
     }
     return "unknown os_status";
 }

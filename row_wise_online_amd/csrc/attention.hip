@@ -77,6 +77,7 @@
 #include "../../include/os_attention.h"
 #include "chunks.hpp"
 #include "common.hpp"
+#include "launch.hpp"
 
 namespace os {
 namespace attn {
@@ -653,6 +654,8 @@ extern "C" os_status os_attention_fwd(
     if (!q || !k || !v || !o) return OS_ERR_NULL;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
         return OS_ERR_STRIDE;
+    const os::Device *dev = os::current_device();
+    if (dev == nullptr || !dev->gfx950) return OS_ERR_DEVICE;
 
     Params p{};
     p.q = static_cast<const uint16_t *>(q);

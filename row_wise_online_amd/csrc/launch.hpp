@@ -5,7 +5,20 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "plan.hpp"
+
 namespace os {
+
+// The properties of a device that the plans and the kernels depend on,
+// read once per device (thread-safe) and kept for the life of the process.
+struct Device {
+    int cus;      // compute units
+    bool gfx950;  // the architecture these kernels are built for
+};
+
+// The current device's properties, or nullptr when no device is current or
+// its properties cannot be read.
+const Device *current_device();
 
 enum class Dt { F32, BF16 };
 enum class Mode { Prob, LogProb, Stats };
@@ -33,25 +46,17 @@ struct FwdArgs {
     int64_t causal;
     Dt dt;
     bool vec;         // 16-byte vector access is legal for x (and y)
+    int cus;          // compute units of the device (sizes the grids)
     hipStream_t stream;
 
     bool masked() const { return row_len != nullptr || causal >= 0; }
 };
 
-// Resident single-read path: rows of up to kResidentMaxN elements.
-constexpr int kResidentMaxN = 32768;
+// Resident single-read path (rows of up to kResidentMaxN elements).
 void launch_resident(const FwdArgs &a);
 
 // Streaming path, one workgroup per row.
 void launch_stream(const FwdArgs &a);
-
-// Split-row plan: P chunks of C elements per row.
-struct SplitPlan {
-    int P;
-    int C;
-};
-SplitPlan split_plan(int64_t M, int64_t N);
-size_t split_workspace_bytes(int64_t M, int64_t N);
 
 // Split path: partial states into ws; then, for statistics alone (and the
 // cross-entropy), the state-merge kernel, and for softmax / log-softmax the

@@ -6,10 +6,9 @@
 namespace os {
 namespace {
 
-// Persistent form for the longest rows: a grid of at most kPersistentWgs
-// workgroups (two 512-thread workgroups per CU on 256 CUs) walks the rows,
-// prefetching each workgroup's next row while it finishes the current one.
-constexpr int64_t kPersistentWgs = 512;
+// Persistent form for the longest rows: a grid of at most two 512-thread
+// workgroups per CU (persistent_grid) walks the rows, prefetching each
+// workgroup's next row while it finishes the current one.
 
 StatsOut stats_of(const FwdArgs &a) {
     return StatsOut{a.m_out, a.d_out, a.lse_out, a.inc_out, a.labels, a.loss,
@@ -33,7 +32,7 @@ void run_persistent(const FwdArgs &a) {
     constexpr int W = VEC ? Tr::E : 1;
     static_assert(EPL % W == 0, "a lane holds whole slots");
     constexpr int SPL = EPL / W;
-    const int64_t g = a.M < kPersistentWgs ? a.M : kPersistentWgs;
+    const int64_t g = persistent_grid(a.M, a.cus);
     using E = typename Tr::elem_t;
     resident_persistent_kernel<Tr, VEC, WAVES, SPL, true, OUT, CE, MK>
         <<<dim3(static_cast<unsigned>(g)), dim3(kWave * WAVES), 0, a.stream>>>(

@@ -9,8 +9,6 @@ namespace {
 
 constexpr int kSplitWaves = 4;
 constexpr int kMergeRows = 4;          // rows (wavefronts) per merge workgroup
-constexpr int64_t kTargetWgs = 2048;   // 8 workgroups per CU on 256 CUs
-constexpr int64_t kChunkAlign = 4096;  // chunk length granularity (elements)
 
 // Temporal pass-1 loads leave x in the Infinity Cache for the normalise
 // pass (non-temporal); on fp32 16 x 4194304 this is 126 us against 142 us
@@ -23,8 +21,6 @@ template <class Tr, bool VEC>
 constexpr int tile_slots() {
     return VEC ? 32 / Tr::E : 16;
 }
-
-size_t align256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
 
 struct WsLayout {
     float *part_m, *part_d, *row_m, *row_d;
@@ -46,7 +42,7 @@ template <class Tr, bool VEC, class Pol, bool MK>
 void run(const FwdArgs &a, void *ws) {
     using E = typename Tr::elem_t;
     constexpr int U = tile_slots<Tr, VEC>();
-    const SplitPlan plan = split_plan(a.M, a.N);
+    const SplitPlan plan = split_plan(a.M, a.N, a.cus);
     const WsLayout l = layout(ws, a.M, plan.P);
     const dim3 grid(static_cast<unsigned>(a.M * plan.P));
     const dim3 block(kWave * kSplitWaves);
@@ -98,21 +94,6 @@ void by_mode(const FwdArgs &a, void *ws) {
 
 }  // namespace
 
-SplitPlan split_plan(int64_t M, int64_t N) {
-    int64_t P = (kTargetWgs + M - 1) / M;
-    if (P < 1) P = 1;
-    int64_t C = (N + P - 1) / P;
-    C = (C + kChunkAlign - 1) / kChunkAlign * kChunkAlign;
-    P = (N + C - 1) / C;
-    return SplitPlan{static_cast<int>(P), static_cast<int>(C)};
-}
-
-size_t split_workspace_bytes(int64_t M, int64_t N) {
-    const SplitPlan plan = split_plan(M, N);
-    return 2 * align256(sizeof(float) * static_cast<size_t>(M) * plan.P) +
-           2 * align256(sizeof(float) * static_cast<size_t>(M));
-}
-
 void launch_split(const FwdArgs &a, void *ws) {
     if (a.dt == Dt::F32) {
         if (a.vec) by_mode<F32, true>(a, ws); else by_mode<F32, false>(a, ws);
@@ -142,21 +123,11 @@ void state_normalize(const FwdArgs &a, const SplitPlan &plan, const float *sm,
     }
 }
 
-// Chunks for pass 2 alone: rows are cut (at multiples of kChunkAlign
-// elements) until there are about kNormalizeWgs workgroups.  With no pass 1
-// to share a chunk with, more and shorter chunks keep more loads in flight:
-// on fp32 16 x 4194304 83.7 us against 92.0 us with the split path's 2048
-// workgroups, on fp32 1024 x 32768 43.0 us against 46.2 us.
-constexpr int64_t kNormalizeWgs = 16384;
-
-SplitPlan normalize_plan(int64_t M, int64_t N) {
-    int64_t P = (kNormalizeWgs + M - 1) / M;
-    if (P < 1) P = 1;
-    int64_t C = (N + P - 1) / P;
-    C = (C + kChunkAlign - 1) / kChunkAlign * kChunkAlign;
-    P = (N + C - 1) / C;
-    return SplitPlan{static_cast<int>(P), static_cast<int>(C)};
-}
+// Chunks for pass 2 alone (normalize_plan): rows are cut at multiples of
+// kChunkAlign elements until there are about 64 workgroups per CU.  With no
+// pass 1 to share a chunk with, more and shorter chunks keep more loads in
+// flight: on fp32 16 x 4194304 83.7 us against 92.0 us with the split
+// path's 8 per CU, on fp32 1024 x 32768 43.0 us against 46.2 us (MI355X).
 
 // Workgroup shape by the bytes one workgroup covers (a row, or a chunk of
 // one): with 16-byte slots the tile is the whole row up to 32 KiB, as on
@@ -165,7 +136,7 @@ SplitPlan normalize_plan(int64_t M, int64_t N) {
 template <class Tr, bool VEC>
 void run_state_normalize(const FwdArgs &a, const float *sm, const float *sd,
                          int64_t inc) {
-    const SplitPlan plan = normalize_plan(a.M, a.N);
+    const SplitPlan plan = normalize_plan(a.M, a.N, a.cus);
     const int64_t len = plan.C < a.N ? plan.C : a.N;
     const int64_t bytes = len * static_cast<int64_t>(sizeof(typename Tr::elem_t));
     if (bytes <= 1024) state_normalize<Tr, VEC, 1, 1>(a, plan, sm, sd, inc);

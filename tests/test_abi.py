@@ -52,6 +52,18 @@ def test_status_strings(lib):
     assert lib.os_status_string(99).decode() == "unknown os_status"
 
 
+def _have_gfx950(lib):
+    # the planning queries answer only for a current gfx950 device
+    return lib.os_softmax_select_path(4, 4, 0) != 0
+
+
+# what a call that passes every argument check returns on this machine
+# when its workspace check depends on the device: without a gfx950 it stops
+# at OS_ERR_DEVICE
+def _device_or(lib, status):
+    return status if _have_gfx950(lib) else 9
+
+
 def _fwd(lib, x=FAKE, ldx=8, y=FAKE, ldy=8, M=4, N=8, dt=0, m=NUL, d=NUL,
          lse=NUL, ws=NUL, wsb=0, path=0):
     return lib.os_softmax_fwd_path(x, ldx, y, ldy, M, N, dt, m, d, lse, ws,
@@ -65,11 +77,33 @@ def _fwd(lib, x=FAKE, ldx=8, y=FAKE, ldy=8, M=4, N=8, dt=0, m=NUL, d=NUL,
     (dict(x=NUL), 1), (dict(y=NUL), 1), (dict(path=4), 6), (dict(path=-1), 6),
     (dict(N=40000, ldx=40000, ldy=40000, path=1), 7),
     (dict(M=16, N=1 << 22, ldx=1 << 22, ldy=1 << 22, path=3), 5),
+    (dict(M=16, N=1 << 22, ldx=1 << 22, ldy=1 << 22, path=3, ws=FAKE,
+          wsb=100), "dev5"),
     (dict(M=16, N=1 << 22, ldx=1 << 22, ldy=1 << 22, path=0, ws=FAKE,
-          wsb=100), 5),
+          wsb=100), "dev5"),
+    (dict(M=16, N=1 << 22, ldx=1 << 22, ldy=1 << 22, path=0), "dev5"),
 ])
 def test_fwd_validation(lib, kw, status):
+    if status == "dev5":
+        status = _device_or(lib, 5)
     assert _fwd(lib, **kw) == status
+
+
+def test_device_checked_after_the_arguments(lib):
+    # valid arguments: the call reads the current device next; without a
+    # gfx950 it fails with OS_ERR_DEVICE and enqueues nothing
+    if _have_gfx950(lib):
+        pytest.skip("a gfx950 device is current")
+    assert _fwd(lib) == 9
+    assert _stats(lib) == 9
+    assert _norm(lib, "os_softmax_normalize") == 9
+    assert lib.os_state_merge(FAKE, FAKE, 4, 3, 4, FAKE, FAKE, NUL, NUL) == 9
+    assert _ce(lib) == 9
+    assert _ce(lib, x=NUL, labels=NUL, loss=NUL, M=0, mean=FAKE) == 9
+    assert _attn(lib) == 9
+    assert lib.os_softmax_workspace_bytes(16, 1 << 22, 0, 3) == 0
+    assert lib.os_softmax_select_path(16, 1 << 22, 0) == 0
+    assert lib.os_softmax_stats_select_path(16, 1 << 22, 0) == 0
 
 
 def test_fwd_empty_is_noop(lib):
@@ -132,8 +166,19 @@ def test_normalize_validation(lib, name, kw, status):
     assert _norm(lib, name, **kw) == status
 
 
+def _plan(lib, M, N, dt=0, path=0, read_only=0, cus=256):
+    p = _lib.Plan()
+    st = lib.os_softmax_plan(M, N, dt, path, read_only, cus, ctypes.byref(p))
+    return st, p
+
+
+def _sel(lib, M, N, dt=0, read_only=0, cus=256):
+    st, p = _plan(lib, M, N, dt, 0, read_only, cus)
+    return _lib.PATH_NAMES[p.path] if st == 0 else st
+
+
 def test_select_path_for_the_workloads(lib):
-    sel = lambda M, N, dt: _lib.PATH_NAMES[lib.os_softmax_select_path(M, N, dt)]
+    sel = lambda M, N, dt: _sel(lib, M, N, dt)
     assert sel(64, 1000, 0) == "resident"
     assert sel(4096, 4096, 0) == "resident"
     assert sel(32768, 1024, 1) == "resident"
@@ -141,14 +186,15 @@ def test_select_path_for_the_workloads(lib):
     assert sel(16, 4194304, 0) == "split"
     assert sel(4096, 65536, 0) == "stream"
     assert sel(16, 32768, 0) == "split"
-    assert sel(-1, 5, 0) == "auto"          # invalid shape
+    assert sel(-1, 5, 0) == 2               # invalid shape
+    assert sel(5, 5, 3) == 4                # unknown dtype
 
 
 def test_read_only_select_path(lib):
     # statistics and cross-entropy: long rows stream when rows are many;
     # otherwise the forward rule
-    sel = lambda M, N, dt: _lib.PATH_NAMES[lib.os_softmax_stats_select_path(M, N, dt)]
-    fwd = lambda M, N, dt: _lib.PATH_NAMES[lib.os_softmax_select_path(M, N, dt)]
+    sel = lambda M, N, dt: _sel(lib, M, N, dt, read_only=1)
+    fwd = lambda M, N, dt: _sel(lib, M, N, dt)
     assert sel(1024, 32768, 0) == "stream"
     assert sel(1024, 32768, 1) == "stream"
     assert sel(512, 16385, 0) == "stream"
@@ -157,18 +203,14 @@ def test_read_only_select_path(lib):
     for M, N, dt in [(64, 1000, 0), (4096, 4096, 0), (32768, 1024, 1),
                      (16, 4194304, 0), (4096, 65536, 0), (16, 32768, 0)]:
         assert sel(M, N, dt) == fwd(M, N, dt), (M, N, dt)
-    assert sel(-1, 5, 0) == "auto"
-    assert sel(5, 5, 7) == "auto"          # unknown dtype
     # the workspace of AUTO does not depend on which of the two rules applies
     for M, N in [(1024, 32768), (512, 16385), (16, 4194304)]:
-        auto = lib.os_softmax_workspace_bytes(M, N, 0, 0)
-        forced = lib.os_softmax_workspace_bytes(
-            M, N, 0, lib.os_softmax_stats_select_path(M, N, 0))
-        assert auto == forced
+        assert _plan(lib, M, N)[1].workspace_bytes == \
+            _plan(lib, M, N, read_only=1)[1].workspace_bytes
 
 
 def test_workspace_bytes(lib):
-    ws = lib.os_softmax_workspace_bytes
+    ws = lambda M, N, dt, path: _plan(lib, M, N, dt, path)[1].workspace_bytes
     assert ws(4096, 4096, 0, 0) == 0
     assert ws(4096, 4096, 0, 1) == 0
     assert ws(4096, 4096, 0, 2) == 0
@@ -177,10 +219,61 @@ def test_workspace_bytes(lib):
     assert ws(16, 4194304, 0, 0) == 2 * 8192 + 2 * 256
     assert ws(16, 4194304, 0, 3) == 2 * 8192 + 2 * 256
     assert ws(16, 4194304, 1, 3) == 2 * 8192 + 2 * 256
-    assert ws(-1, 4, 0, 0) == 0 and ws(4, 4, 9, 0) == 0 and ws(4, 4, 0, 9) == 0
+    st, p = _plan(lib, 16, 4194304, 0, 3)
+    assert (st, p.chunks_per_row, p.chunk_len) == (0, 128, 32768)
     assert ws(0, 100, 0, 3) == 0
     # a single chunk per row when rows are many
     assert ws(4096, 4096, 0, 3) == 2 * 16384 + 2 * 16384
+    assert _plan(lib, 4096, 4096, 0, 3)[1].chunks_per_row == 1
+
+
+def test_plan_errors(lib):
+    p = _lib.Plan()
+    f = lambda *a: lib.os_softmax_plan(*a, ctypes.byref(p))
+    assert f(-1, 4, 0, 0, 0, 256) == 2
+    assert f(4, 0, 0, 0, 0, 256) == 2
+    assert f(4, 4, 9, 0, 0, 256) == 4
+    assert f(4, 4, 0, 9, 0, 256) == 6
+    assert f(4, 4, 0, 0, 0, 0) == 9          # no compute units
+    assert f(4, 4, 0, 0, 0, -3) == 9
+    assert f(4, 40000, 0, 1, 0, 256) == 7     # resident beyond 32768
+    assert lib.os_softmax_plan(4, 4, 0, 0, 0, 256, None) == 1
+
+
+@pytest.mark.parametrize("cus", [1, 8, 32, 80, 104, 228, 256, 304, 1024])
+def test_plan_scales_with_the_cu_count(lib, cus):
+    # the AUTO thresholds and the split grid follow the CU count: resident
+    # or stream from 2 rows per CU, split below; the split path aims at
+    # about 8 workgroups per CU with chunks of whole multiples of 4096
+    many = 2 * cus
+    assert _sel(lib, many, 8192, cus=cus) == "resident"
+    assert _sel(lib, many - 1, 8192, cus=cus) == ("split" if many > 1 else "resident")
+    assert _sel(lib, many, 40000, cus=cus) == "stream"
+    assert _sel(lib, many, 20000, read_only=1, cus=cus) == "stream"
+    assert _sel(lib, 1, 4096, cus=cus) == "resident"    # short rows always
+    for M, N in [(1, 1 << 22), (3, 1 << 22), (16, 4194304), (16, 5000),
+                 (100, 1 << 20), (many - 1, 100000), (4096, 4096)]:
+        st, p = _plan(lib, M, N, 0, 3, cus=cus)
+        assert st == 0
+        P, C = p.chunks_per_row, p.chunk_len
+        assert C % 4096 == 0 and P >= 1
+        assert (P - 1) * C < N <= P * C           # every column in one chunk
+        target = -(-8 * cus // M)
+        assert P <= max(1, target)                 # never more than asked
+        # fewer chunks only where a chunk of 4096 or the row itself runs out
+        assert P == target or C == 4096 or P == -(-N // C)
+        ws = 2 * (-(-4 * M * P // 256) * 256) + 2 * (-(-4 * M // 256) * 256)
+        assert p.workspace_bytes == ws
+
+
+def test_plan_at_256_cus_is_the_mi355x_plan(lib):
+    # the MI355X plans of the workloads, unchanged from the fixed tables
+    # the library used before it read the CU count
+    assert _sel(lib, 511, 16385) == "split" and _sel(lib, 512, 16385) == "resident"
+    st, p = _plan(lib, 16, 4194304, 0, 0)
+    assert (p.path, p.chunks_per_row, p.chunk_len) == (3, 128, 32768)
+    st, p = _plan(lib, 1, 1 << 22, 0, 3)
+    assert (p.chunks_per_row, p.chunk_len) == (1024, 4096)
 
 
 def _logfwd(lib, x=FAKE, ldx=8, y=FAKE, ldy=8, M=4, N=8, dt=0, path=0):

@@ -36,9 +36,10 @@ def test_split_bytes_include_the_state_tables():
     import row_wise_online_amd as rw
     w = wl.WORKLOADS["c5"]
     xy = w.M * w.N * 4
-    ws = rw.workspace_bytes(w.M, w.N, "f32", "split")
+    ws = rw.softmax_plan(w.M, w.N, "f32", 256, "split")["workspace_bytes"]
     assert ws > 0
-    assert bench.algorithmic_bytes(w, "split", 3) == 3 * xy + 4 * w.M * 3 + 2 * ws
+    assert bench.algorithmic_bytes(w, "split", 3, cus=256) == \
+        3 * xy + 4 * w.M * 3 + 2 * ws
 
 
 def test_cross_entropy_and_stats_read_once():
