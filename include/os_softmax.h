@@ -138,6 +138,33 @@ os_status os_softmax_fwd_path(const void *x, int64_t ld_x, void *y,
                               float *lse_out, void *ws, size_t ws_bytes,
                               os_path path, hipStream_t stream);
 
+/* os_softmax_fwd_path for callers that cannot allocate device memory (code
+ * under graph capture, tight serving loops, harnesses that forbid
+ * allocation): the split path's workspace (partial and row states) is a
+ * fixed 256 KiB array in device memory that the library holds, one copy
+ * per device, from the first call on that device until the process ends;
+ * there is no ws argument and nothing is allocated.
+ *  - A plan that needs more than 256 KiB returns OS_ERR_WORKSPACE and
+ *    enqueues nothing.  AUTO never does at 256 CUs (its largest split
+ *    workspace, fewer than 512 rows, is under 25 KiB); forcing SPLIT on
+ *    many rows can (about 16 bytes per row and chunk).
+ *  - The array keeps the last call's contents; nothing in it has to start
+ *    at any value (every partial state is written before it is read).
+ *  - Every call on one device shares that device's array: calls that
+ *    overlap on one device (other streams, other host threads) race and
+ *    give wrong results.  Order them on one stream or with events.
+ *  - The device address of the array is read once per device, on the first
+ *    call with that device current (hipGetSymbolAddress); OS_ERR_HIP if it
+ *    cannot be read.
+ * Everything else (arguments, paths, results, errors) as
+ * os_softmax_fwd_path; results are bit-identical to os_softmax_fwd_path
+ * with a caller workspace. */
+os_status os_softmax_fwd_noalloc(const void *x, int64_t ld_x, void *y,
+                                 int64_t ld_y, int64_t M, int64_t N,
+                                 os_dtype dt, float *m_out, float *d_out,
+                                 float *lse_out, os_path path,
+                                 hipStream_t stream);
+
 /* Pass 1 only: the (m, d) state of each row, written to m_out[i*inc_out]
  * and d_out[i*inc_out] (both required, fp32), and optionally
  * lse_out[i*inc_out].  Called on a column window (x advanced by a column

@@ -26,7 +26,7 @@ import math
 from . import _lib
 from ._lib import OsError, PATHS, PATH_NAMES  # noqa: F401
 
-__all__ = ["softmax_fwd", "log_softmax_fwd", "cross_entropy_fwd",
+__all__ = ["softmax_fwd", "softmax_fwd_noalloc", "log_softmax_fwd", "cross_entropy_fwd",
            "prepare_fwd", "prepare_cross_entropy", "prepare_stats",
            "softmax_stats",
            "softmax_stats_update", "softmax_normalize", "prepare_normalize",
@@ -202,6 +202,27 @@ def softmax_fwd(x, y=None, *, m=None, d=None, lse=None, ws=None,
     row to its first columns (os_softmax_fwd_masked)."""
     return _fwd("os_softmax_fwd_path", x, y, m, d, lse, ws, path, stream,
                 row_len, causal)
+
+
+def softmax_fwd_noalloc(x, y, *, m=None, d=None, lse=None, path="auto",
+                        stream=None):
+    """softmax_fwd without allocation (os_softmax_fwd_noalloc): y is
+    required and the split path's workspace is the library's fixed device
+    array (256 KiB per device, shared by every call on the device: calls
+    that overlap on one device race)."""
+    lib = _lib.load()
+    dt = _dtype_code(x.dtype)
+    if y.dtype != x.dtype or y.shape != x.shape:
+        raise ValueError("y must have the dtype and shape of x")
+    xp, ldx = _matrix(x, "x")
+    yp, ldy = _matrix(y, "y")
+    M, N = x.shape
+    st = lib.os_softmax_fwd_noalloc(xp, ldx, yp, ldy, M, N, dt,
+                                    _vec(m, "m", M), _vec(d, "d", M),
+                                    _vec(lse, "lse", M), _path_code(path),
+                                    _stream(stream))
+    _lib.check("os_softmax_fwd_noalloc", st)
+    return y
 
 
 def log_softmax_fwd(x, y=None, *, m=None, d=None, lse=None, ws=None,

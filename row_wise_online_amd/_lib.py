@@ -43,6 +43,8 @@ SIGNATURES = {
                               _vp, _vp, _vp, _vp, _sz, _vp]),
     "os_softmax_fwd_path": (_i32, [_vp, _i64, _vp, _i64, _i64, _i64, _i32,
                                    _vp, _vp, _vp, _vp, _sz, _i32, _vp]),
+    "os_softmax_fwd_noalloc": (_i32, [_vp, _i64, _vp, _i64, _i64, _i64,
+                                      _i32, _vp, _vp, _vp, _i32, _vp]),
     "os_log_softmax_fwd": (_i32, [_vp, _i64, _vp, _i64, _i64, _i64, _i32,
                                   _vp, _vp, _vp, _vp, _sz, _vp]),
     "os_log_softmax_fwd_path": (_i32, [_vp, _i64, _vp, _i64, _i64, _i64,

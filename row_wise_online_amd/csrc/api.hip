@@ -1,5 +1,6 @@
 // C ABI of the row-wise online softmax library: argument validation (on the
 // host, before any HIP call), path selection and launches.
+#include <mutex>
 #include <stdint.h>
 
 #include "../../include/os_softmax.h"
@@ -140,7 +141,74 @@ os_status fwd(os::Mode mode, const void *x, int64_t ld_x, void *y,
 
 }  // namespace
 
+// ---------------------------------------------------------------------------
+// Workspace without allocation, for callers that cannot allocate device
+// memory: a fixed array in device memory that os_softmax_fwd_noalloc uses
+// in place of a caller workspace.  Each device holds its own copy, from
+// the library's first use on it until the process ends.  In host code the
+// array's name is a host-side handle, not a device address: the device
+// address is read once per device with hipGetSymbolAddress (with that
+// device current) and only that address is passed to kernels.
+// ---------------------------------------------------------------------------
+constexpr size_t kScratchBytes = size_t(256) << 10;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+constexpr int kMaxScratchDevices = 64;
+
+struct ScratchEntry {
+    std::once_flag once;
+    void *ptr;
+};
+
+ScratchEntry g_scratch[kMaxScratchDevices];
+
+// The current device's copy of the scratch array, or nullptr if its
+// address cannot be read.
+void *scratch_of_current_device() {
+    int id = -1;
+    if (hipGetDevice(&id) != hipSuccess) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    if (id < 0 || id >= kMaxScratchDevices) return nullptr;
+    ScratchEntry &e = g_scratch[id];
+    std::call_once(e.once, [&e] {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) {
+            (void)hipGetLastError();
+            p = nullptr;
+        }
+        e.ptr = p;
+    });
+    return e.ptr;
+}
+
+}  // namespace
+
 extern "C" {
+
+os_status os_softmax_fwd_noalloc(const void *x, int64_t ld_x, void *y,
+                                 int64_t ld_y, int64_t M, int64_t N,
+                                 os_dtype dt, float *m_out, float *d_out,
+                                 float *lse_out, os_path path,
+                                 hipStream_t stream) {
+    // the arguments first, before any HIP call
+    os_status s = check_shape(M, N, dt);
+    if (s != OS_OK) return s;
+    if (!valid_path(path)) return OS_ERR_PATH;
+    if (ld_x < N || ld_y < N) return OS_ERR_STRIDE;
+    if (M == 0) return OS_OK;
+    if (x == nullptr || y == nullptr) return OS_ERR_NULL;
+    if (path == OS_PATH_RESIDENT && N > os::kResidentMaxN) return OS_ERR_UNSUPPORTED;
+    if (usable_device() == nullptr) return OS_ERR_DEVICE;
+    void *ws = scratch_of_current_device();
+    if (ws == nullptr) return OS_ERR_HIP;
+    // a plan that needs more than the array fails with OS_ERR_WORKSPACE
+    return fwd(os::Mode::Prob, x, ld_x, y, ld_y, M, N, dt, m_out, d_out,
+               lse_out, ws, kScratchBytes, path, stream);
+}
 
 os_status os_softmax_plan(int64_t M, int64_t N, os_dtype dt, os_path path,
                           int read_only, int cu_count, os_plan *out) {

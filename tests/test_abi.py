@@ -89,6 +89,23 @@ def test_fwd_validation(lib, kw, status):
     assert _fwd(lib, **kw) == status
 
 
+def _noalloc(lib, x=FAKE, ldx=8, y=FAKE, ldy=8, M=4, N=8, dt=0, path=0):
+    return lib.os_softmax_fwd_noalloc(x, ldx, y, ldy, M, N, dt, NUL, NUL, NUL,
+                                      path, NUL)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(M=-1), 2), (dict(N=0), 2), (dict(ldx=7), 3), (dict(ldy=7), 3),
+    (dict(dt=2), 4), (dict(x=NUL), 1), (dict(y=NUL), 1), (dict(path=4), 6),
+    (dict(N=40000, ldx=40000, ldy=40000, path=1), 7),
+    (dict(x=NUL, y=NUL, M=0), 0),
+])
+def test_noalloc_validation(lib, kw, status):
+    # the entry point without allocation checks its arguments like the
+    # others, before any HIP call
+    assert _noalloc(lib, **kw) == status
+
+
 def test_device_checked_after_the_arguments(lib):
     # valid arguments: the call reads the current device next; without a
     # gfx950 it fails with OS_ERR_DEVICE and enqueues nothing
@@ -101,6 +118,7 @@ def test_device_checked_after_the_arguments(lib):
     assert _ce(lib) == 9
     assert _ce(lib, x=NUL, labels=NUL, loss=NUL, M=0, mean=FAKE) == 9
     assert _attn(lib) == 9
+    assert _noalloc(lib) == 9
     assert lib.os_softmax_workspace_bytes(16, 1 << 22, 0, 3) == 0
     assert lib.os_softmax_select_path(16, 1 << 22, 0) == 0
     assert lib.os_softmax_stats_select_path(16, 1 << 22, 0) == 0
