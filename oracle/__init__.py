@@ -42,6 +42,9 @@ def _load():
         lib.oracle_merge.restype = i32
         lib.oracle_log_softmax.argtypes = [vp, i64, i64, i64, i32, dp]
         lib.oracle_log_softmax.restype = i32
+        lib.oracle_normalize.argtypes = [vp, i64, i64, i64, i32, dp, dp, i64,
+                                         i32, dp]
+        lib.oracle_normalize.restype = i32
         lib.oracle_cross_entropy.argtypes = [vp, i64, i64, i64, i32, vp, dp,
                                              dp]
         lib.oracle_cross_entropy.restype = i32
@@ -150,6 +153,25 @@ def log_softmax(x):
     rc = _load().oracle_log_softmax(_ptr(x), ld, M, N, code, _ptr(y))
     if rc != 0:
         raise ValueError("oracle_log_softmax rejected its arguments")
+    return y
+
+
+def normalize(x, m, d, log=False):
+    """Pass 2 of every row of ``x`` for the given row states (m, d) [M]
+    (any float dtype, widened to fp64): e^(x - m) / d, or with log=True
+    (x - m) - log d; fp64 [M, N].  The exact value for that state."""
+    x, code = _as_input(x)
+    M, N = x.shape
+    ld = x.strides[0] // x.itemsize
+    m = np.ascontiguousarray(m, dtype=np.float64).reshape(-1)
+    d = np.ascontiguousarray(d, dtype=np.float64).reshape(-1)
+    if m.shape != (M,) or d.shape != (M,):
+        raise ValueError("one state per row")
+    y = np.empty((M, N), np.float64)
+    rc = _load().oracle_normalize(_ptr(x), ld, M, N, code, _ptr(m), _ptr(d),
+                                  1, 1 if log else 0, _ptr(y))
+    if rc != 0:
+        raise ValueError("oracle_normalize rejected its arguments")
     return y
 
 

@@ -79,6 +79,42 @@ static int check_args(const void *x, int64_t ld, int64_t M, int64_t N, int dtype
     return ORACLE_OK;
 }
 
+/* ---- the row's max and normaliser -------------------------------------------
+ * [P1] §1.1 and [P4] §3, passes 1 and 2 over the first n elements of the
+ * row at base: m = max_j x_j (NaN never compares greater, so it is
+ * skipped), d = sum_j e^(x_j - m) (a -inf element has weight 0).
+ * log d ([P3] stable-form section: LSE = m + log d) is evaluated as
+ * log1p(s), s the sum of the terms other than one instance of the max: that
+ * instance's term is exactly e^0 = 1, so d = 1 + s, and s summed apart from
+ * the 1 keeps fp64 relative precision when d lies within rounding of 1 (a
+ * row whose max dominates), where log of a rounded d would lose it.  A row
+ * with no finite max has s = d - 1 taken as is (m = -inf: d = 0, log d =
+ * -inf; m = +inf: its term is NaN). */
+static void row_stats(const void *x, int dtype, int64_t base, int64_t n,
+                      double *m_out, double *d_out, double *logd_out)
+{
+    double m = -INFINITY;
+    for (int64_t j = 0; j < n; ++j) {
+        double v = load_elem(x, dtype, base + j);
+        if (v > m) m = v;
+    }
+    double d = 0.0, s = 0.0;
+    int found = !isfinite(m);  /* no instance to leave out */
+    for (int64_t j = 0; j < n; ++j) {
+        double v = load_elem(x, dtype, base + j);
+        double t = (v == -INFINITY) ? 0.0 : exp(v - m);
+        d = d + t;
+        if (!found && v == m) {
+            found = 1;          /* the max's own 1, left out of s */
+            continue;
+        }
+        s = s + t;
+    }
+    *m_out = m;
+    *d_out = d;
+    *logd_out = isfinite(m) ? log1p(s) : log(d);
+}
+
 /* ---- the definition: three-pass safe softmax ------------------------------
  * [P1] §1.1 and [P4] §3: m = max_j x_j, d = sum_j e^(x_j - m),
  * y_j = e^(x_j - m) / d.  [P3] stable-form section: LSE = m + log d.
@@ -91,20 +127,9 @@ int oracle_softmax(const void *x, int64_t ld, int64_t M, int64_t N, int dtype,
     for (int64_t i = 0; i < M; ++i) {
         const int64_t base = i * ld;
 
-        /* pass 1: the row max (NaN never compares greater, so it is skipped) */
-        double m = -INFINITY;
-        for (int64_t j = 0; j < N; ++j) {
-            double v = load_elem(x, dtype, base + j);
-            if (v > m) m = v;
-        }
-
-        /* pass 2: the sum of e^(x - m); a -inf element has weight 0 */
-        double d = 0.0;
-        for (int64_t j = 0; j < N; ++j) {
-            double v = load_elem(x, dtype, base + j);
-            double t = (v == -INFINITY) ? 0.0 : exp(v - m);
-            d = d + t;
-        }
+        /* passes 1 and 2: the row max and the sum of e^(x - m) */
+        double m, d, logd;
+        row_stats(x, dtype, base, N, &m, &d, &logd);
 
         /* pass 3: normalise with a true division */
         if (y != NULL) {
@@ -116,7 +141,7 @@ int oracle_softmax(const void *x, int64_t ld, int64_t M, int64_t N, int dtype,
         }
         if (m_out) m_out[i] = m;
         if (d_out) d_out[i] = d;
-        if (lse_out) lse_out[i] = m + log(d);
+        if (lse_out) lse_out[i] = m + logd;
     }
     return ORACLE_OK;
 }
@@ -190,8 +215,10 @@ int oracle_merge(const double *m_in, const double *d_in, int64_t ld,
 
 /* ---- log-softmax -----------------------------------------------------------
  * [P3] stable-form section: log p_j = z_j - LSE(z), LSE = m + log d, with m
- * and d from the definition above (oracle_softmax).  y is dense fp64
- * [M][N].  A row of only -inf gives -inf - (-inf) = NaN, as y = 0/0 does. */
+ * and d from the definition above; written (z_j - m) - log d, the same
+ * value with the common m subtracted first, so that a log-probability near
+ * 0 is not the difference of two large numbers.  y is dense fp64 [M][N].
+ * A row of only -inf gives -inf - (-inf) = NaN, as y = 0/0 does. */
 int oracle_log_softmax(const void *x, int64_t ld, int64_t M, int64_t N,
                        int dtype, double *y)
 {
@@ -199,12 +226,37 @@ int oracle_log_softmax(const void *x, int64_t ld, int64_t M, int64_t N,
     if (rc != ORACLE_OK) return rc;
     if (M > 0 && y == NULL) return ORACLE_EINVAL;
     for (int64_t i = 0; i < M; ++i) {
-        double lse;
-        oracle_softmax((const char *)x + (size_t)(i * ld) *
-                           (dtype == ORACLE_F32 ? 4 : 2),
-                       ld, 1, N, dtype, NULL, NULL, NULL, &lse);
+        double m, d, logd;
+        row_stats(x, dtype, i * ld, N, &m, &d, &logd);
         for (int64_t j = 0; j < N; ++j)
-            y[i * N + j] = load_elem(x, dtype, i * ld + j) - lse;
+            y[i * N + j] = (load_elem(x, dtype, i * ld + j) - m) - logd;
+    }
+    return ORACLE_OK;
+}
+
+/* ---- pass 2 with a given state -----------------------------------------------
+ * [P1] §2.2: the second pass writes y_j = e^(x_j - m) / d from the state
+ * (m, d) the first pass left; [P3] stable-form section: its log form is
+ * log p_j = (x_j - m) - log d.  Here the state is an input, (m_in[i*inc],
+ * d_in[i*inc]) for row i, taken as given (fp64; an fp32 state widens
+ * exactly): the exact value of the pass for that state, whatever rounding
+ * the state carries.  log_form != 0 writes the log form.  y is dense fp64
+ * [M][N].  The identity state (-inf, 0) gives NaN (0/0, -inf + inf). */
+int oracle_normalize(const void *x, int64_t ld, int64_t M, int64_t N,
+                     int dtype, const double *m_in, const double *d_in,
+                     int64_t inc, int log_form, double *y)
+{
+    int rc = check_args(x, ld, M, N, dtype);
+    if (rc != ORACLE_OK) return rc;
+    if (M > 0 && (y == NULL || m_in == NULL || d_in == NULL)) return ORACLE_EINVAL;
+    if (inc < 1) return ORACLE_EINVAL;
+    for (int64_t i = 0; i < M; ++i) {
+        const double m = m_in[i * inc];
+        const double d = d_in[i * inc];
+        for (int64_t j = 0; j < N; ++j) {
+            const double v = load_elem(x, dtype, i * ld + j);
+            y[i * N + j] = log_form ? (v - m) - log(d) : exp(v - m) / d;
+        }
     }
     return ORACLE_OK;
 }
@@ -234,11 +286,10 @@ int oracle_cross_entropy(const void *x, int64_t ld, int64_t M, int64_t N,
         if (c >= N) {
             loss[i] = NAN;
         } else {
-            double lse;
-            oracle_softmax((const char *)x + (size_t)(i * ld) *
-                               (dtype == ORACLE_F32 ? 4 : 2),
-                           ld, 1, N, dtype, NULL, NULL, NULL, &lse);
-            loss[i] = lse - load_elem(x, dtype, i * ld + c);
+            /* LSE - z_c = (m - z_c) + log d */
+            double m, d, logd;
+            row_stats(x, dtype, i * ld, N, &m, &d, &logd);
+            loss[i] = (m - load_elem(x, dtype, i * ld + c)) + logd;
         }
         total = total + loss[i];
         count = count + 1;
@@ -257,8 +308,8 @@ int oracle_cross_entropy(const void *x, int64_t ld, int64_t M, int64_t N,
  * -inf reading above then fixes their output): y = 0 for softmax, -inf for
  * log-softmax.  A row with n_i = 0 has m = -inf, d = 0, lse = -inf and a NaN
  * y, as a row of only -inf.
- * The valid columns follow the definition of oracle_softmax, written out
- * again over j < n_i.  log_y (nullable): x - lse on valid columns. */
+ * The valid columns follow the definition of oracle_softmax over j < n_i.
+ * log_y (nullable): (x - m) - log d on valid columns, as oracle_log_softmax. */
 static int64_t valid_cols(int64_t i, int64_t N, const int32_t *row_len,
                           int64_t causal)
 {
@@ -282,24 +333,15 @@ int oracle_softmax_masked(const void *x, int64_t ld, int64_t M, int64_t N,
     for (int64_t i = 0; i < M; ++i) {
         const int64_t base = i * ld;
         const int64_t n = valid_cols(i, N, row_len, causal);
-        double m = -INFINITY;
-        for (int64_t j = 0; j < n; ++j) {
-            double v = load_elem(x, dtype, base + j);
-            if (v > m) m = v;
-        }
-        double d = 0.0;
-        for (int64_t j = 0; j < n; ++j) {
-            double v = load_elem(x, dtype, base + j);
-            double t = (v == -INFINITY) ? 0.0 : exp(v - m);
-            d = d + t;
-        }
-        const double lse = m + log(d);
+        double m, d, logd;
+        row_stats(x, dtype, base, n, &m, &d, &logd);
+        const double lse = m + logd;
         for (int64_t j = 0; j < N; ++j) {
             if (j < n) {
                 double v = load_elem(x, dtype, base + j);
                 double t = (v == -INFINITY) ? 0.0 : exp(v - m);
                 if (y) y[i * N + j] = t / d;
-                if (log_y) log_y[i * N + j] = v - lse;
+                if (log_y) log_y[i * N + j] = (v - m) - logd;
             } else {
                 if (y) y[i * N + j] = (n == 0) ? NAN : 0.0;
                 if (log_y) log_y[i * N + j] = (n == 0) ? NAN : -INFINITY;

@@ -38,6 +38,9 @@ int oracle_log_softmax(const void *x, int64_t ld, int64_t M, int64_t N,
 
 /* Cross-entropy per row from int64 labels; mean (nullable) over the rows
  * whose label is not negative. */
+int oracle_normalize(const void *x, int64_t ld, int64_t M, int64_t N,
+                     int dtype, const double *m_in, const double *d_in,
+                     int64_t inc, int log_form, double *y);
 int oracle_cross_entropy(const void *x, int64_t ld, int64_t M, int64_t N,
                          int dtype, const int64_t *labels, double *loss,
                          double *mean);

@@ -14,6 +14,8 @@
 // (1 KiB contiguous for vectors) and a workgroup sweeps the row front to back.
 #pragma once
 
+#include <type_traits>
+
 #include "merge.hpp"
 
 namespace os {
@@ -120,6 +122,48 @@ __device__ __forceinline__ void write_row_stats(const StatsOut &o, int64_t row,
     }
 }
 
+// The same for a state in r form (r = d - 1): log d is log1p(r), so the
+// log-sum-exp and a cross-entropy near 0 keep full relative precision where
+// d rounds to 1; d is written as 1 + r.  A running state held in m / d
+// (accumulate) enters the merge as r = d - 1.
+template <class Tr, bool CE>
+__device__ __forceinline__ void write_row_stats(const StatsOut &o, int64_t row,
+                                                StateR st, const Target<Tr> &t,
+                                                int N) {
+    const int64_t k = row * o.inc;
+    if (o.accumulate) merge_into_r(st.m, st.r, o.m[k], o.d[k] - 1.0f);
+    const float logd = log1pf(st.r);
+    if (o.m) o.m[k] = st.m;
+    if (o.d) o.d[k] = 1.0f + st.r;
+    if (o.lse) o.lse[k] = st.m + logd;
+    if constexpr (CE) {
+        float l;
+        if (t.c < 0) {
+            l = -0.0f;
+        } else if (t.c >= N) {
+            l = __builtin_nanf("");
+        } else {
+            l = (safe_ref(st.m) - Tr::to_f32(t.raw)) + logd;
+        }
+        o.loss[row] = l;
+    }
+}
+
+// 1/d and log d of a row state in either form.
+__device__ __forceinline__ float inv_d(const State &s) { return 1.0f / s.d; }
+__device__ __forceinline__ float log_d(const State &s) { return __builtin_logf(s.d); }
+__device__ __forceinline__ float inv_d(const StateR &s) { return 1.0f / (1.0f + s.r); }
+__device__ __forceinline__ float log_d(const StateR &s) { return log1pf(s.r); }
+
+// The state form of a pass: log-softmax keeps r = d - 1, whose log1p keeps
+// the log-probabilities near 0; softmax and the read-only passes keep d
+// (softmax divides by d; the statistics and the cross-entropy, fp32 outputs
+// whose bar is absolute, take log d within fp32 rounding of 1, and the
+// extra compare and select per element of the r form would cost them
+// 20-50 % on the short rows, where their VALU work is near the memory time).
+template <Out OUT>
+using StateOf = typename std::conditional<OUT == Out::LogProb, StateR, State>::type;
+
 // ---------------------------------------------------------------------------
 // Resident single-read path ("5.2 CUDA Online Softmax 实现优化" §6: keep the
 // row on chip after pass 1 and normalise from registers; x is read once).
@@ -152,34 +196,41 @@ struct ResidentRow {
         }
     }
 
-    // Pass 1 to the row state; v is left as pass 2 needs it.
-    __device__ __forceinline__ static State reduce(float *v, int wr, int lane,
-                                                   float2 *lds, float &ml) {
+    // Pass 1 to the row state; v is left as pass 2 needs it.  Softmax: the
+    // lane's terms e^(v - m_lane) replace v and the state is (m, d);
+    // otherwise v keeps x and the state is (m, r).
+    __device__ __forceinline__ static StateOf<OUT> reduce(float *v, int wr,
+                                                          int lane, float2 *lds,
+                                                          float &ml) {
         ml = tree_max<EPL>(v);
         const float rl = safe_ref(ml);
-        float dl;
         if constexpr (OUT == Out::Prob) {
 #pragma unroll
             for (int i = 0; i < EPL; ++i) v[i] = (v[i] - rl) * kLog2e;
             exp2_inplace<Tr::kExactTiny, EPL>(v);
-            dl = tree_sum<EPL>(v);
+            const float dl = tree_sum<EPL>(v);
+            State st = wave_merge(ml, dl);
+            return block_merge<WAVES>(st, wr, lane, lds);
+        } else if constexpr (OUT == Out::LogProb) {
+            const StateR st = wave_merge_r(ml, lane_r<EPL>(v, ml));
+            return block_merge_r<WAVES>(st, wr, lane, lds);
         } else {
-            dl = tree_sum_exp<EPL>(v, rl);
+            const float dl = tree_sum_exp<EPL>(v, rl);
+            State st = wave_merge(ml, dl);
+            return block_merge<WAVES>(st, wr, lane, lds);
         }
-        State st = wave_merge(ml, dl);
-        return block_merge<WAVES>(st, wr, lane, lds);
     }
 
     __device__ __forceinline__ static void write(elem_t *yr, int N, int base,
-                                                 const State &st, float ml,
-                                                 float *v) {
+                                                 const StateOf<OUT> &st,
+                                                 float ml, float *v) {
         if constexpr (OUT == Out::Prob) {
             const float scale = exp_shifted(ml - safe_ref(st.m)) * (1.0f / st.d);
 #pragma unroll
             for (int i = 0; i < EPL; ++i) v[i] *= scale;
         } else if constexpr (OUT == Out::LogProb) {
             const float r = safe_ref(st.m);
-            const float logd = __builtin_logf(st.d);
+            const float logd = log_d(st);
 #pragma unroll
             for (int i = 0; i < EPL; ++i) v[i] = (v[i] - r) - logd;
         }
@@ -212,7 +263,7 @@ __global__ __launch_bounds__(kWave *WAVES) void resident_kernel(
     float v[R::EPL];
     R::load(xr, valid_cols<MASKED>(mk, row, N), base, v);
     float ml;
-    const State st = R::reduce(v, wr, lane, lds, ml);
+    const auto st = R::reduce(v, wr, lane, lds, ml);
     R::write(y + row * ldy, N, base, st, ml, v);
     if (threadIdx.x == 0) write_row_stats<Tr, CE>(so, row, st, tg, N);
 }
@@ -247,7 +298,7 @@ __global__ __launch_bounds__(kWave *WAVES) void resident_persistent_kernel(
         const Target<Tr> tg = fetch_target<Tr, CE>(so, row, x + row * ldx, N);
         if (rn < M) R::load(x + rn * ldx, valid_cols<MASKED>(mk, rn, N), base, nxt);
         float ml;
-        const State st = R::reduce(cur, wr, lane, lds[it & 1], ml);
+        const auto st = R::reduce(cur, wr, lane, lds[it & 1], ml);
         R::write(y + row * ldy, N, base, st, ml, cur);
         if (threadIdx.x == 0) write_row_stats<Tr, CE>(so, row, st, tg, N);
 #pragma unroll
@@ -316,6 +367,20 @@ struct Tiles {
         }
     }
 
+    // Pass 1 over [0, n) in r form: fold every element into (m, r).
+    __device__ __forceinline__ static void fold_r(const elem_t *p, int n,
+                                                  int base, float &m, float &r) {
+        const int nt = num_tiles(n);
+        float cur[K], nxt[K];
+        load_tile(p, 0, base, n, tile_full(0, n), cur);
+        for (int t = 0; t < nt; ++t) {
+            if (t + 1 < nt) load_tile(p, t + 1, base, n, tile_full(t + 1, n), nxt);
+            fold_chunk_r<K>(m, r, cur);
+#pragma unroll
+            for (int i = 0; i < K; ++i) cur[i] = nxt[i];
+        }
+    }
+
     // Pass 2 over [0, n) for the row state st: Prob writes e^(x - m) / d,
     // LogProb writes (x - m) - log d.  Only [0, nl) is read (nl <= n; the
     // rest loads as -inf: masked columns).  Tile t+1 is read before tile t
@@ -323,14 +388,14 @@ struct Tiles {
     // REV walks the tiles last to first: after a pass 1 that went first to
     // last, the most recently read lines come first, while they are most
     // likely still in the Infinity Cache.
-    template <Out OUT, bool REV>
+    template <Out OUT, bool REV, class St>
     __device__ __forceinline__ static void normalize(const elem_t *p, elem_t *q,
                                                      int nl, int n, int base,
-                                                     const State &st) {
+                                                     const St &st) {
         static_assert(OUT != Out::None, "pass 2 writes something");
         const float r = safe_ref(st.m);
-        const float inv = 1.0f / st.d;
-        const float logd = __builtin_logf(st.d);
+        const float inv = inv_d(st);
+        const float logd = log_d(st);
         const int nt = num_tiles(n);
         float cur[K], nxt[K];
         const int t0 = REV ? nt - 1 : 0;
@@ -386,10 +451,16 @@ __global__ __launch_bounds__(kWave *WAVES) void stream_kernel(
 
     const Target<Tr> tg = fetch_target<Tr, CE>(so, row, xr, N);
     const int nv = valid_cols<MASKED>(mk, row, N);
-    float m = kNegInf, d = 0.0f;
-    T::fold(xr, nv, base, m, d);
-    State st = wave_merge(m, d);
-    st = block_merge<WAVES>(st, wave, lane, lds);
+    StateOf<OUT> st;
+    if constexpr (OUT == Out::LogProb) {
+        float m = kNegInf, r = -1.0f;
+        T::fold_r(xr, nv, base, m, r);
+        st = block_merge_r<WAVES>(wave_merge_r(m, r), wave, lane, lds);
+    } else {
+        float m = kNegInf, d = 0.0f;
+        T::fold(xr, nv, base, m, d);
+        st = block_merge<WAVES>(wave_merge(m, d), wave, lane, lds);
+    }
 
     if constexpr (OUT != Out::None) {
         T2::template normalize<OUT, Pol::rev>(xr, y + row * ldy, nv, N, base, st);
@@ -403,8 +474,10 @@ __global__ __launch_bounds__(kWave *WAVES) void stream_kernel(
 // partial results).  Row i is cut into P chunks of C elements (the last one
 // shorter); workgroup b handles row b / P, chunk b % P.
 // ---------------------------------------------------------------------------
+// RF: the partial states are written in r form, (m, d - 1), for the pass
+// that keeps r (log-softmax); else (m, d).
 template <class Tr, bool VEC, int WAVES, int U, class Pol = StreamingNT,
-          bool MASKED = false>
+          bool MASKED = false, bool RF = false>
 __global__ __launch_bounds__(kWave *WAVES) void split_partial_kernel(
     const typename Tr::elem_t *x, int64_t ldx, int N, int P, int C,
     float *ws_m, float *ws_d, Mask mk) {
@@ -420,13 +493,24 @@ __global__ __launch_bounds__(kWave *WAVES) void split_partial_kernel(
     // the chunk's state is the identity
     const int n = min(C, valid_cols<MASKED>(mk, row, N) - c0);
 
-    float m = kNegInf, d = 0.0f;
-    T::fold(x + row * ldx + c0, n, wave * kWave + lane, m, d);
-    State st = wave_merge(m, d);
-    st = block_merge<WAVES>(st, wave, lane, lds);
+    float m = kNegInf;
+    float second;
+    if constexpr (RF) {
+        float r = -1.0f;
+        T::fold_r(x + row * ldx + c0, n, wave * kWave + lane, m, r);
+        const StateR st = block_merge_r<WAVES>(wave_merge_r(m, r), wave, lane, lds);
+        m = st.m;
+        second = st.r;
+    } else {
+        float d = 0.0f;
+        T::fold(x + row * ldx + c0, n, wave * kWave + lane, m, d);
+        const State st = block_merge<WAVES>(wave_merge(m, d), wave, lane, lds);
+        m = st.m;
+        second = st.d;
+    }
     if (threadIdx.x == 0) {
-        ws_m[b] = st.m;
-        ws_d[b] = st.d;
+        ws_m[b] = m;
+        ws_d[b] = second;
     }
 }
 
@@ -452,9 +536,16 @@ __global__ __launch_bounds__(kWave *WAVES) void split_normalize_kernel(
     const int c0 = p * C;
     const int n = min(C, N - c0);
     const int nl = min(n, valid_cols<MASKED>(mk, row, N) - c0);
-    float m = kNegInf, d = 0.0f;
-    for (int k = lane; k < P; k += kWave) merge_into(m, d, part_m[row * P + k], part_d[row * P + k]);
-    const State st = wave_merge(m, d);
+    StateOf<OUT> st;
+    if constexpr (OUT == Out::LogProb) {
+        float m = kNegInf, r = -1.0f;
+        for (int k = lane; k < P; k += kWave) merge_into_r(m, r, part_m[row * P + k], part_d[row * P + k]);
+        st = wave_merge_r(m, r);
+    } else {
+        float m = kNegInf, d = 0.0f;
+        for (int k = lane; k < P; k += kWave) merge_into(m, d, part_m[row * P + k], part_d[row * P + k]);
+        st = wave_merge(m, d);
+    }
     if (p == 0 && threadIdx.x == 0)
         write_row_stats<Tr, false>(so, row, st, Target<Tr>{-1, typename Tr::elem_t(0)}, N);
     T::template normalize<OUT, Pol::rev>(x + row * ldx + c0, y + row * ldy + c0,

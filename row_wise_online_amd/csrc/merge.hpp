@@ -199,4 +199,134 @@ __device__ __forceinline__ State block_merge(State s, int wave, int lane,
     }
 }
 
+// ---- the state with r = d - 1 ------------------------------------------------
+// For the outputs that take a logarithm of the normaliser (log-softmax, the
+// log-sum-exp, the cross-entropy) the state carries r = d - 1 in place of d:
+// the row's terms other than one instance of its max, summed apart from
+// that term's 1.  When every other term is below 2^-24 of the max, d rounds
+// to 1 in fp32 and log d to 0, while r keeps the small sum to full relative
+// precision and log1p(r) gives log d to full relative precision.  Then the
+// max element's log-probability, -log1p(r), and a confident row's
+// cross-entropy are exact to fp32 rounding rather than 0.  The identity is
+// (-inf, -1).  Elements equal to the max add exactly 1 each, except the
+// one instance the 1 of d stands for.
+struct StateR {
+    float m;
+    float r;
+};
+
+constexpr float kPosInf = __builtin_huge_valf();
+
+// The sum of e^(v_k - ref) over the v_k other than mn, and the count c of
+// the v_k equal to mn.  Summed in groups of at most 8 (pairwise inside a
+// group, then over the groups), so that few terms are live at once.
+template <int K>
+__device__ __forceinline__ float sum_apart(const float *v, float mn, float ref,
+                                           int &c) {
+    constexpr int G = K < 8 ? K : 8;
+    static_assert(K % G == 0, "whole groups");
+    float part[K / G];
+    c = 0;
+#pragma unroll
+    for (int g = 0; g < K / G; ++g) {
+        float t[G];
+#pragma unroll
+        for (int k = 0; k < G; ++k) {
+            const float x = v[g * G + k];
+            const bool eq = x == mn;
+            t[k] = eq ? 0.0f : exp2_fast((x - ref) * kLog2e);
+            c += eq ? 1 : 0;
+        }
+        part[g] = tree_sum<G>(t);
+    }
+    return tree_sum<K / G>(part);
+}
+
+// r of a lane's K values alone (a fresh lane state, max ml): the values
+// equal to ml are one max and c - 1 further terms of exactly 1.  A lane of
+// only -inf is the identity; a max of +inf makes r NaN (the row is NaN, as
+// a NaN element makes it).
+template <int K>
+__device__ __forceinline__ float lane_r(const float *v, float ml) {
+    int c;
+    const float s = sum_apart<K>(v, ml, safe_ref(ml), c);
+    float r = s + static_cast<float>(c - 1);
+    if (ml == kNegInf) r = -1.0f;
+    if (ml == kPosInf) r = __builtin_nanf("");
+    return r;
+}
+
+// Fold K register values into the lane state (m, r): with mn the new max,
+//   m == mn:  r += sum_k e^(v_k - m), each v_k == m adding exactly 1;
+//   m <  mn:  r = (1 + r) e^(m - mn) + sum_{v_k != mn} e^(v_k - mn) + (c - 1)
+// where c counts the v_k equal to mn (c >= 1: one of them is the new max).
+// Only -inf so far leaves the identity; a max of +inf makes r NaN.
+template <int K>
+__device__ __forceinline__ void fold_chunk_r(float &m, float &r, const float *v) {
+    const float mn = fmaxf(m, tree_max<K>(v));
+    const float ref = safe_ref(mn);
+    int c;
+    const float s = sum_apart<K>(v, mn, ref, c);
+    float rn = (m == mn) ? (r + s) + static_cast<float>(c)
+                         : fmaf(1.0f + r, exp2_fast((m - ref) * kLog2e),
+                                s + static_cast<float>(c - 1));
+    if (mn == kNegInf) rn = r;
+    if (mn == kPosInf) rn = __builtin_nanf("");
+    m = mn;
+    r = rn;
+}
+
+// A state's share of a merged r: its own r if its max is the merged max m
+// (then `first` chooses whether its 1 is the implicit one of the merged d),
+// else all of its d, (1 + r) e^(m_k - m).
+__device__ __forceinline__ float share_r(float mk, float rk, float m, float ref,
+                                         bool first) {
+    if (mk == m && m != kNegInf) return first ? rk : rk + 1.0f;
+    return (1.0f + rk) * exp_shifted(mk - ref);
+}
+
+// Merge one more state (mk, rk) into the lane state (m, r).
+__device__ __forceinline__ void merge_into_r(float &m, float &r, float mk,
+                                             float rk) {
+    const float mn = fmaxf(m, mk);
+    const float ref = safe_ref(mn);
+    const float a = share_r(m, r, mn, ref, true);
+    const float b = share_r(mk, rk, mn, ref, !(m == mn));
+    r = (mn == kNegInf) ? -1.0f : (mn == kPosInf ? __builtin_nanf("") : a + b);
+    m = mn;
+}
+
+// n-ary merge of the 64 lane states in r form.  The lowest lane holding the
+// merged max contributes its r, every other lane its share; a wavefront of
+// identities stays the identity.
+__device__ __forceinline__ StateR wave_merge_r(float m, float r) {
+    const float mw = wave_allreduce(m, OpMax{});
+    const uint64_t at_max = __builtin_amdgcn_ballot_w64(m == mw && mw != kNegInf);
+    const int lane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    const bool first = at_max != 0 && lane == __builtin_ctzll(at_max);
+    const float c = share_r(m, r, mw, safe_ref(mw), first);
+    const float rw = wave_allreduce(c, OpAdd{});
+    return {mw, mw == kNegInf ? -1.0f : (mw == kPosInf ? __builtin_nanf("") : rw)};
+}
+
+// The cross-wave merge of block_merge in r form.
+template <int W>
+__device__ __forceinline__ StateR block_merge_r(StateR s, int wave, int lane,
+                                                float2 *lds) {
+    if constexpr (W == 1) {
+        return s;
+    } else {
+        if (lane == 0) lds[wave] = make_float2(s.m, s.r);
+        __syncthreads();
+        const float2 mine = (lane < W) ? lds[lane] : make_float2(kNegInf, -1.0f);
+        const float m = first_lanes_allreduce<W>(mine.x, OpMax{});
+        const uint64_t at_max =
+            __builtin_amdgcn_ballot_w64(lane < W && mine.x == m && m != kNegInf);
+        const bool first = at_max != 0 && lane == __builtin_ctzll(at_max);
+        const float c = share_r(mine.x, mine.y, m, safe_ref(m), first);
+        const float r = first_lanes_allreduce<W>(c, OpAdd{});
+        return {m, m == kNegInf ? -1.0f : (m == kPosInf ? __builtin_nanf("") : r)};
+    }
+}
+
 }  // namespace os

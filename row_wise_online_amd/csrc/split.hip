@@ -49,8 +49,16 @@ void run(const FwdArgs &a, void *ws) {
     const E *x = static_cast<const E *>(a.x);
 
     const Mask mk{a.row_len, a.causal};
-    split_partial_kernel<Tr, VEC, kSplitWaves, U, Pol, MK><<<grid, block, 0, a.stream>>>(
-        x, a.ldx, a.N, plan.P, plan.C, l.part_m, l.part_d, mk);
+    // log-softmax keeps r = d - 1; softmax, statistics and cross-entropy d
+    if (a.mode != Mode::LogProb) {
+        split_partial_kernel<Tr, VEC, kSplitWaves, U, Pol, MK, false>
+            <<<grid, block, 0, a.stream>>>(x, a.ldx, a.N, plan.P, plan.C,
+                                           l.part_m, l.part_d, mk);
+    } else {
+        split_partial_kernel<Tr, VEC, kSplitWaves, U, Pol, MK, true>
+            <<<grid, block, 0, a.stream>>>(x, a.ldx, a.N, plan.P, plan.C,
+                                           l.part_m, l.part_d, mk);
+    }
 
     const StatsOut so{a.m_out, a.d_out, a.lse_out, a.inc_out, a.labels, a.loss,
                       a.accumulate};

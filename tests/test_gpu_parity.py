@@ -456,6 +456,91 @@ def test_log_softmax_workloads(name):
         check_log(y_h[r0:r1], ref, f"{name} rows {r0}..{r1 - 1}")
 
 
+def _dominant_rows(M, N, seed):
+    """Rows whose max term dominates: every other term below 2^-24 of it for
+    most rows, so d rounds to 1 in fp32 and log d to 0 unless d - 1 is kept
+    apart.  Row 0: others near -20 (d - 1 ~ 1e-5 N); rows 1, 2: near -25
+    and -32; row 3: two maxima (d >= 2); row 4: every other element -inf
+    (d = 1 exactly); row 5 onwards: normals."""
+    rng = np.random.default_rng(seed)
+    v = rng.standard_normal((M, N))
+    for i, off in enumerate([-20.0, -25.0, -32.0, -25.0]):
+        v[i] = v[i] * 0.5 + off
+    v[4, :] = -np.inf
+    cols = rng.integers(0, N, size=M)
+    for i in range(5):
+        v[i, cols[i]] = 0.0
+    v[3, (cols[3] + N // 2) % N] = 0.0
+    return v, cols
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("path", ["resident", "stream", "split"])
+def test_log_probabilities_near_zero(path, dtype):
+    # the max element's log-probability, -log1p(d - 1) ~ -1e-8, and the
+    # log-softmax's log-sum-exp - m keep full relative precision: within
+    # one bf16 step (bf16) and 1e-5 relative (fp32), where log d of a
+    # rounded d would give 0; the cross-entropy and statistics on the same
+    # rows meet their absolute fp32 bar
+    shapes = [(6, 3000), (6, 20000)] if path == "resident" else \
+        [(6, 3000), (6, 70001)]
+    for M, N in shapes:
+        what = f"near 0 {path} {dtype} {M}x{N}"
+        _say(what)
+        v, cols = _dominant_rows(M, N, seed=N)
+        x_h = wl.from_values(v, dtype=dtype)
+        x = to_device(x_h)
+        y = torch.empty_like(x)
+        m = torch.empty(M, device="cuda")
+        lse = torch.empty(M, device="cuda")
+        rw.log_softmax_fwd(x, y, m=m, lse=lse, path=path)
+        labels = torch.from_numpy(cols.astype(np.int64)).cuda()
+        loss = torch.empty(M, device="cuda")
+        lse2 = torch.empty(M, device="cuda")
+        rw.cross_entropy_fwd(x, labels, loss, lse=lse2, path=path)
+        sm, sd, sl = (torch.empty(M, device="cuda") for _ in range(3))
+        rw.softmax_stats(x, sm, sd, sl, path=path)
+        torch.cuda.synchronize()
+        ref = oracle.log_softmax(x_h)
+        y_h = to_host(y)
+        check_log(y_h, ref, what)
+        l_ref, _ = oracle.cross_entropy(x_h, cols)
+        check_log(loss.cpu().numpy(), l_ref, what)
+        # the max element's log-probability in closed form: -log1p(s), s the
+        # sum of every other term e^(x_j - m) taken apart from the max's 1
+        # (fp64, relative error below N 2^-53).  The oracle's d = 1 + s
+        # summed whole carries an absolute error up to N 2^-53, too coarse
+        # for a relative check of values near 1e-11.
+        xf = (x_h.astype(np.float64) if dtype == "f32"
+              else oracle.bf16_bits_to_f64(x_h))
+        mx = xf.max(axis=1)
+        terms = np.exp(xf - mx[:, None])
+        rows = np.arange(5)              # the rows whose max sits at cols
+        mx = mx[rows]
+        terms = terms[rows]
+        terms[rows, cols[rows]] = 0.0
+        s_apart = terms.sum(axis=1)
+        top = -np.log1p(s_apart)
+        assert np.all(mx == 0.0)
+        yf = (y_h.astype(np.float64) if dtype == "f32"
+              else oracle.bf16_bits_to_f64(y_h))
+        got = yf[rows, cols[rows]]
+        if dtype == "f32":
+            assert np.all(np.abs(got - top) <= 1e-5 * np.abs(top)), (got, top)
+        else:
+            want = oracle.round_f64_to_bf16_bits(top)
+            assert np.all(oracle.bf16_ulp_distance(y_h[rows, cols[rows]],
+                                                   want) <= 1), what
+        # log-softmax's lse - m is log1p(s): 1e-5 relative
+        lh = lse.cpu().numpy().astype(np.float64)[rows]
+        assert np.all(np.abs((lh - mx) - (-top)) <= 1e-5 * np.abs(top)), what
+        # the cross-entropy and the statistics keep d: their fp32 bar is
+        # absolute (1e-5 plus fp32 rounding)
+        _, _, _, l2_ref = oracle.softmax(x_h, want_y=False)
+        check_lse(lse2.cpu().numpy(), l2_ref, what)
+        check_lse(sl.cpu().numpy(), l2_ref, what)
+
+
 @pytest.mark.parametrize("path", ["resident", "stream", "split"])
 def test_log_softmax_special_values_and_in_place(path):
     inf, nan = math.inf, math.nan
@@ -780,7 +865,10 @@ def test_windows_normalized_with_the_row_state(M, N, dtype):
     check_m(m[0::inc].cpu().numpy(), m_ref, what)
     check_d(d[0::inc].cpu().numpy(), d_ref, what)
     check_y(to_host(y), y_ref, what)
-    check_log(to_host(ly), oracle.log_softmax(x_h), what)
+    # the log form of pass 2 for the fp32 state it was given: its exact
+    # value for that state (log d of an fp32 d is what a held state fixes)
+    mh, dh = m[0::inc].cpu().numpy(), d[0::inc].cpu().numpy()
+    check_log(to_host(ly), oracle.normalize(x_h, mh, dh, log=True), what)
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])

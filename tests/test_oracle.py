@@ -599,3 +599,106 @@ def test_causal_mask_closed_form():
     # both masks: the smaller length wins
     y2, *_ = oracle.softmax_masked(x, np.full(M, 3, np.int32), causal=off)
     assert np.all(y2[0, :2] == 0.5) and np.all(y2[5, :3] == 1.0 / 3)
+
+
+# ---------------------------------------------------------------------------
+# Pass 2 with a given state (oracle.normalize)
+# ---------------------------------------------------------------------------
+
+def test_normalize_worked_example():
+    # "从原始Softmax到在线Softmax": for [2, 1, 0.1] the max is 2 and the sum of
+    # e^(z - 2) is 1.5174; pass 2 with that state gives the printed
+    # probabilities [0.6590, 0.2424, 0.0986] (4 decimals)
+    x = wl.from_values([2.0, 1.0, 0.1])
+    y = oracle.normalize(x, [2.0], [1.5174])
+    assert np.max(np.abs(y[0] - np.array([0.6590, 0.2424, 0.0986]))) <= 5e-5
+    ly = oracle.normalize(x, [2.0], [1.5174], log=True)
+    assert np.max(np.abs(np.exp(ly[0]) - y[0])) <= 1e-15
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_normalize_with_the_row_state_is_the_softmax(dtype):
+    x = wl.normal(5, 777, scale=3.0, seed=81, dtype=dtype)
+    y_ref, m, d, _ = oracle.softmax(x)
+    np.testing.assert_allclose(oracle.normalize(x, m, d), y_ref, rtol=1e-15,
+                               atol=0)
+    np.testing.assert_allclose(oracle.normalize(x, m, d, log=True),
+                               oracle.log_softmax(x), rtol=1e-13, atol=1e-13)
+
+
+def test_normalize_equivalent_states_agree():
+    # (m + c, d e^-c) is the same state: the same outputs, so m enters as
+    # x - m and d as a divisor (a swapped sign or role fails this)
+    x = wl.normal(4, 300, scale=2.0, seed=82)
+    _, m, d, _ = oracle.softmax(x, want_y=False)
+    for c in (-3.0, 0.5, 7.25):
+        np.testing.assert_allclose(oracle.normalize(x, m + c, d * np.exp(-c)),
+                                   oracle.normalize(x, m, d), rtol=1e-13)
+        np.testing.assert_allclose(
+            oracle.normalize(x, m + c, d * np.exp(-c), log=True),
+            oracle.normalize(x, m, d, log=True), rtol=1e-12, atol=1e-12)
+
+
+def test_normalize_window_of_a_row_and_strides():
+    # the state of the whole row applied to a column window gives that
+    # window of the row's softmax; padded rows are read at their pitch
+    full = wl.normal(3, 1000, scale=2.0, seed=83, ld=1024)
+    y_ref, m, d, _ = oracle.softmax(full)
+    win = full[:, 300:700]
+    np.testing.assert_allclose(oracle.normalize(win, m, d), y_ref[:, 300:700],
+                               rtol=1e-15)
+    # a rounded state: the exact value for that state, not for the exact one
+    d32 = d.astype(np.float32).astype(np.float64) * (1 + 2.0 ** -20)
+    got = oracle.normalize(full, m, d32, log=True)
+    want = (full.astype(np.float64) - m[:, None]) - np.log(d32)[:, None]
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-14)
+
+
+def test_normalize_identity_state_gives_nan():
+    # a row of only -inf has the identity state (-inf, 0); pass 2 with it
+    # gives NaN in both forms, as the three-pass definition does
+    x = wl.from_values(np.full((1, 10), -np.inf))
+    _, m, d, _ = oracle.softmax(x, want_y=False)
+    assert m[0] == -np.inf and d[0] == 0.0
+    assert np.all(np.isnan(oracle.normalize(x, m, d)))
+    assert np.all(np.isnan(oracle.normalize(x, m, d, log=True)))
+
+
+# ---------------------------------------------------------------------------
+# log d near 0: a row whose max dominates
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("gap,N", [(20.0, 3000), (32.0, 3000), (36.0, 100),
+                                   (25.0, 70001)])
+def test_log_probabilities_near_zero_high_precision(gap, N):
+    # one element at 0, the rest near -gap: d = 1 + s with s as small as
+    # 1e-14, below fp64's rounding of 1 for the largest gaps.  The max
+    # element's log-probability -log(1 + s), the LSE - m and the
+    # cross-entropy on the max are checked against mpmath at 40 digits to
+    # 1e-12 relative: the rounded d's log would be off by up to 100 %.
+    mpmath = pytest.importorskip("mpmath")
+    mpmath.mp.dps = 40
+    rng = np.random.default_rng(int(gap) * 7 + N)
+    v = rng.standard_normal((1, N)) * 0.5 - gap
+    c = int(rng.integers(0, N))
+    v[0, c] = 0.0
+    x = wl.from_values(v)
+    xs = [mpmath.mpf(float(t)) for t in x[0]]
+    s_exact = mpmath.fsum(mpmath.exp(t) for j, t in enumerate(xs) if j != c)
+    want = -mpmath.log1p(s_exact)
+    lp = oracle.log_softmax(x)[0, c]
+    assert abs(lp - float(want)) <= 1e-12 * abs(float(want))
+    _, m, d, lse = oracle.softmax(x, want_y=False)
+    assert m[0] == 0.0
+    assert abs(lse[0] + float(want)) <= 1e-12 * abs(float(want))
+    loss, _ = oracle.cross_entropy(x, np.array([c]))
+    assert abs(loss[0] + float(want)) <= 1e-12 * abs(float(want))
+    # two instances of the max: log 2 + s, every other term counted once
+    v[0, (c + 1) % N] = 0.0
+    x2 = wl.from_values(v)
+    s2 = mpmath.fsum(mpmath.exp(mpmath.mpf(float(t))) for j, t in
+                     enumerate(x2[0]) if j != c)
+    assert abs(oracle.log_softmax(x2)[0, c] + float(mpmath.log1p(s2))) <= \
+        1e-14 * float(mpmath.log1p(s2))
+    masked = oracle.softmax_masked(x, None, -1)
+    assert abs(masked[1][0, c] - float(want)) <= 1e-12 * abs(float(want))

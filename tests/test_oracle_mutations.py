@@ -27,20 +27,29 @@ MUTATIONS = {
         ("*d_out = da * exp(ma - m) + db * exp(mb - m);",
          "*d_out = da * exp(ma - m) + db;"),
     "lse without m":
-        ("if (lse_out) lse_out[i] = m + log(d);",
-         "if (lse_out) lse_out[i] = log(d);"),
-    "log-softmax without lse":
-        ("y[i * N + j] = load_elem(x, dtype, i * ld + j) - lse;",
-         "y[i * N + j] = load_elem(x, dtype, i * ld + j);"),
+        ("if (lse_out) lse_out[i] = m + logd;",
+         "if (lse_out) lse_out[i] = logd;"),
+    "log-softmax without log d":
+        ("y[i * N + j] = (load_elem(x, dtype, i * ld + j) - m) - logd;",
+         "y[i * N + j] = (load_elem(x, dtype, i * ld + j) - m);"),
+    "log-softmax without m":
+        ("y[i * N + j] = (load_elem(x, dtype, i * ld + j) - m) - logd;",
+         "y[i * N + j] = load_elem(x, dtype, i * ld + j) - logd;"),
     "cross-entropy sign of the label term":
-        ("loss[i] = lse - load_elem(x, dtype, i * ld + c);",
-         "loss[i] = lse + load_elem(x, dtype, i * ld + c);"),
+        ("loss[i] = (m - load_elem(x, dtype, i * ld + c)) + logd;",
+         "loss[i] = (m + load_elem(x, dtype, i * ld + c)) + logd;"),
+    "log d takes the max's own term":
+        ("*logd_out = isfinite(m) ? log1p(s) : log(d);",
+         "*logd_out = isfinite(m) ? log1p(d) : log(d);"),
+    "log d keeps every instance of the max":
+        ("            found = 1;          /* the max's own 1, left out of s */\n            continue;",
+         "            found = 1;          /* the max's own 1, left out of s */"),
     "cross-entropy mean counts ignored rows":
         ("            loss[i] = 0.0;\n            continue;",
          "            loss[i] = 0.0;\n            count = count + 1;\n            continue;"),
     "masked columns read":
-        ("        for (int64_t j = 0; j < n; ++j) {\n            double v = load_elem(x, dtype, base + j);\n            if (v > m) m = v;",
-         "        for (int64_t j = 0; j < N; ++j) {\n            double v = load_elem(x, dtype, base + j);\n            if (v > m) m = v;"),
+        ("row_stats(x, dtype, base, n, &m, &d, &logd);",
+         "row_stats(x, dtype, base, N, &m, &d, &logd);"),
     "causal offset off by one":
         ("if (causal >= 0 && i + causal + 1 < n) n = i + causal + 1;",
          "if (causal >= 0 && i + causal < n) n = i + causal;"),
@@ -61,6 +70,12 @@ MUTATIONS = {
     "online output rescale dropped":
         ("for (int64_t c = 0; c < D; ++c) acc[c] = alpha * acc[c];",
          "for (int64_t c = 0; c < D; ++c) acc[c] = acc[c];"),
+    "pass 2 with a state: exponent sign flipped":
+        ("log_form ? (v - m) - log(d) : exp(v - m) / d;",
+         "log_form ? (v - m) - log(d) : exp(m - v) / d;"),
+    "pass 2 with a state: log form without log d":
+        ("log_form ? (v - m) - log(d) : exp(v - m) / d;",
+         "log_form ? (v - m) : exp(v - m) / d;"),
     "online normaliser rescale dropped":
         ("            l = alpha * l;", "            l = l;"),
 }
