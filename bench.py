@@ -352,13 +352,22 @@ def copy_gbps(nbytes, steps=50):
     return round(2 * rows * rb / (mean * 1e-6) / 1e9, 1)
 
 
-def ceilings(w, steps=200, warmup=400, trials=20):
+# Launch shapes (waves per workgroup, 16-byte vectors per lane) the copy
+# sweep tries on the workload's bytes: one workgroup per 1 KiB to 128 KiB.
+COPY_SHAPES = [(1, 1), (1, 2), (1, 4), (1, 8), (1, 16), (4, 1), (4, 2), (4, 4),
+               (4, 8), (8, 1), (8, 2), (8, 4), (8, 8), (8, 16)]
+
+
+def ceilings(w, steps=200, warmup=400, trials=20, full=True):
     """What this device reaches on the bytes of one softmax launch of
     workload w, cold (buffer sets rotating over >= 1 GiB), with no
     arithmetic: the in-tree copy, read-only and write-only kernels in the
-    resident kernel's launch shape (ceiling/ceiling.hip), the runtime's
-    device-to-device copy, torch's copy, and the launch floor (an empty
-    kernel back to back, one workgroup and the workload's grid)."""
+    resident kernel's launch shape (ceiling/ceiling.hip), the same copy in
+    every shape of COPY_SHAPES (the best one-launch copy of these bytes),
+    the runtime's device-to-device copy, torch's copy, and the launch floor
+    (an empty kernel back to back, one workgroup and the workload's grid).
+    full=False: the same-shape copy alone (the counters' calibration
+    kernel in profiler runs)."""
     import torch
     import ceiling
     lib = ceiling.load()
@@ -390,9 +399,30 @@ def ceilings(w, steps=200, warmup=400, trials=20):
                 "ceil_write"), nbytes),
         }
         for k, (fn, nb) in kern.items():
+            if not full and k != "copy":
+                continue
             mean, dist = _time_launches(fn, R, steps, warmup, trials)
             out[k] = {"GBps": rate(nb, mean), "us": round(mean, 3),
                       "bytes": nb, **dist}
+    if not full:
+        del src, dst, sink
+        torch.cuda.empty_cache()
+        return out
+    sweep = {}
+    for waves, spl in COPY_SHAPES:
+        rb = 16 * 64 * waves * spl
+        if nbytes % rb:
+            continue
+        rows = nbytes // rb
+        mean, _ = _time_launches(lambda i: ceiling.check(lib.ceil_copy(
+            src[i].data_ptr(), dst[i].data_ptr(), rows, rb, rb, waves, spl,
+            strm), "ceil_copy"), R, steps, warmup, 0)
+        sweep[f"{rows}x{64 * waves}x{spl}"] = round(mean, 3)
+    if sweep:
+        best = min(sweep, key=sweep.get)
+        out["copy_shapes_us"] = sweep
+        out["best_copy"] = {"shape": best, "us": sweep[best],
+                            "GBps": rate(2 * nbytes, sweep[best])}
     mean, dist = _time_launches(lambda i: ceiling.check(lib.ceil_memcpy(
         dst[i].data_ptr(), src[i].data_ptr(), nbytes, strm), "ceil_memcpy"),
         R, min(steps, 50), 10, trials)
@@ -611,7 +641,7 @@ def run_workload(name, steps, warmup, path="auto", want_cpu=True,
         raise ValueError("the causal mask applies to softmax / log-softmax")
     # the ceilings first: they also bring the clocks up from idle before
     # the timed steps
-    ceil = ceilings(w) if extras else None
+    ceil = ceilings(w) if extras else ceilings(w, 50, 10, 0, full=False)
     ms, R, host_us, dist, outs = measure(w, steps, warmup, path, op=op,
                                          causal=causal,
                                          trials=20 if extras else 0,
@@ -701,16 +731,19 @@ def run_workload(name, steps, warmup, path="auto", want_cpu=True,
                 "ms_per_step": round(ms2, 6),
                 "note": "independent steps alternate over two streams (y "
                         "only); not the headline"}
-    if ceil is not None:
-        if "copy" in ceil:
-            # the in-tree copy kernel in this launch shape: x read, y written
-            rec["copy_ceiling_GBps"] = ceil["copy"]["GBps"]
-            rec["roofline"]["frac_of_copy_ceiling"] = round(
-                ceil["copy"]["us"] / (ms * 1e3) *
-                nbytes / ceil["copy"]["bytes"], 4)
+    if "copy" in ceil:
+        # the in-tree copy kernel in this launch shape: x read, y written
+        rec["copy_ceiling_GBps"] = ceil["copy"]["GBps"]
+        rec["roofline"]["frac_of_copy_ceiling"] = round(
+            ceil["copy"]["us"] / (ms * 1e3) * nbytes / ceil["copy"]["bytes"], 4)
+    if "best_copy" in ceil:
+        # the fastest one-launch copy of these bytes over the shapes tried
+        rec["roofline"]["frac_of_best_copy"] = round(
+            ceil["best_copy"]["us"] / (ms * 1e3) * nbytes / (2 * w.M * w.N * w.esize), 4)
+    if "launch_floor" in ceil:
         rec["launch_floor_us"] = {k: v["us"] for k, v in
                                   ceil["launch_floor"].items()}
-        rec["ceilings"] = ceil
+    rec["ceilings"] = ceil
     rec["git_sha"] = git_sha()
     if want_cpu:
         base, ref = cpu_baseline(w, n_stats, cpu_budget, op, causal)
@@ -913,8 +946,8 @@ def main():
                     help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--no-extras", action="store_true",
-                    help="time only the headline loop and the copy "
-                         "calibration (for profiler runs)")
+                    help="time only the headline loop and the same-shape "
+                         "copy (the counters' calibration; profiler runs)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:

@@ -74,3 +74,9 @@ def test_launch_shapes_of_the_workloads():
         rows, rb, waves, spl = bench.ceiling_shape(W[name])
         assert rb == 16 * 64 * waves * spl
         assert rows * rb == W[name].M * W[name].N * W[name].esize
+
+
+def test_sweep_shapes_are_built():
+    # every shape bench.py's copy sweep asks for has an instantiation
+    for waves, spl in bench.COPY_SHAPES:
+        assert waves in ceiling.WAVES and spl in ceiling.VECTORS_PER_LANE
