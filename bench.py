@@ -109,15 +109,13 @@ def algorithmic_bytes(w, path, n_stats, op="softmax", causal=None, cus=None):
 
 
 def measure(w, steps, warmup, path="auto", rotate=True, graph=False,
-            op="softmax", causal=None, streams=1, trials=0, keep=False):
+            op="softmax", causal=None, trials=0, keep=False):
     """Average device time per step (ms), the rotation depth, the host time
-    per launch (us), and the spread of the launch time (or None).  Steps
-    cycle over R buffer sets; with graph=True the launches are captured
-    once in a HIP graph and replayed.  With streams=2 consecutive steps
-    alternate between two default-priority streams, so one step's launch
-    can start while the previous one drains.  With trials > 0 (plain
-    launches on one stream) that many further runs of up to 50 launches,
-    each between its own pair of events, follow the timed steps; their
+    per launch (us), the spread of the launch time (or None) and the kept
+    outputs (or None).  Steps cycle over R buffer sets; with graph=True the
+    launches are captured once in a HIP graph and replayed.  With trials > 0
+    (plain launches) that many further runs of up to 50 launches, each
+    between its own pair of events, follow the timed steps; their
     per-launch times give the p10 / p50 / p90 spread.  With keep=True the
     outputs of the last step on buffer set 0 (every set holds the same x)
     are copied to the host and returned last, else None."""
@@ -161,18 +159,10 @@ def measure(w, steps, warmup, path="auto", rotate=True, graph=False,
         rw.softmax_stats(x0, m_st, d_st)
         m = d = lse = None
 
-    extra_streams = []
-    if streams == 2:
-        if R % 2 or ws_bytes or m is not None or d is not None or \
-                lse is not None or ce:
-            raise ValueError("two streams need an even rotation and no "
-                             "outputs shared between steps")
-        extra_streams.append(torch.cuda.Stream())
-
     def prepared():
-        # the launch streams are taken here, so that under graph capture the
+        # the launch stream is taken here, so that under graph capture the
         # calls bind to the capturing stream
-        strm = [torch.cuda.current_stream()] + extra_streams
+        strm = torch.cuda.current_stream()
         if op == "stats":
             return [rw.prepare_stats(xs[i], m, d, lse, ws=ws, path=path)
                     for i in range(R)]
@@ -185,45 +175,39 @@ def measure(w, steps, warmup, path="auto", rotate=True, graph=False,
                     for i in range(R)]
         return [rw.prepare_fwd(xs[i], ys[i], m=m, d=d, lse=lse, ws=ws,
                                path=path, log=(op == "log_softmax"),
-                               causal=causal, stream=strm[i % len(strm)])
+                               causal=causal, stream=strm)
                 for i in range(R)]
 
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
-    strm = [torch.cuda.current_stream()] + extra_streams
+    strm = torch.cuda.current_stream()   # the stream the calls launch on
     dist = None
     if not graph:
         calls = prepared()
         for i in range(warmup):
             calls[i % R]()
         torch.cuda.synchronize()
-        start.record(strm[0])
-        for s2 in strm[1:]:
-            s2.wait_event(start)
+        start.record(strm)
         t0 = time.perf_counter()
         for i in range(steps):
             calls[i % R]()
         host_us = (time.perf_counter() - t0) / steps * 1e6
-        for s2 in strm[1:]:
-            done = torch.cuda.Event()
-            done.record(s2)
-            strm[0].wait_event(done)
-        end.record(strm[0])
+        end.record(strm)
         end.synchronize()
         torch.cuda.synchronize()
         ms = start.elapsed_time(end) / steps
-        if trials and len(strm) == 1:
+        if trials:
             per = max(1, min(steps, 50))
             evs = [(torch.cuda.Event(enable_timing=True),
                     torch.cuda.Event(enable_timing=True))
                    for _ in range(trials)]
             k = 0
             for a, b in evs:
-                a.record(strm[0])
+                a.record(strm)
                 for _ in range(per):
                     calls[k % R]()
                     k += 1
-                b.record(strm[0])
+                b.record(strm)
             torch.cuda.synchronize()
             us = sorted(a.elapsed_time(b) / per * 1e3 for a, b in evs)
             q = lambda f: round(us[int(f * (len(us) - 1) + 0.5)], 3)
@@ -691,6 +675,17 @@ def run_workload(name, steps, warmup, path="auto", want_cpu=True,
         "pct_of_peak": round(100.0 * gbs / PEAK_GBS, 2),
         "rows_per_s": round(w.M / (ms * 1e-3), 1),
         "effective_single_read_GBps": round(eff, 1),
+        "effective_single_read_pct_of_peak": round(100.0 * eff / PEAK_GBS, 2),
+        "bytes_counted": ("x read once, y written once, row statistics"
+                          if resolved == "resident" or op in (
+                              "stats", "cross_entropy", "normalize")
+                          else "x read twice (pass 1 and pass 2; the second "
+                               "read may be served by the Infinity Cache, so "
+                               "value is not HBM bandwidth: the effective "
+                               "single-read rate is), y written once, row "
+                               "statistics" +
+                               (", partial states" if resolved == "split"
+                                else "")),
         "host_us_per_launch": round(host_us, 2),
         "roofline": {
             "bound": "hbm",
@@ -714,23 +709,6 @@ def run_workload(name, steps, warmup, path="auto", want_cpu=True,
             rec["per_launch_us"] = dist
         rec["warm_cache_GBps"] = round(nbytes / (warm_ms * 1e-3) / 1e9, 1)
         rec["graph_replay_GBps"] = round(nbytes / (graph_ms * 1e-3) / 1e9, 1)
-        if op in ("softmax", "log_softmax") and causal is None and \
-                resolved != "split":
-            # the same steps alternating over two streams: kernel launch
-            # boundaries (about 2 us each on this part) may overlap, which
-            # shows the kernel's sustained rate rather than a single launch's
-            w2 = wl.WORKLOADS[name]
-            w2 = type(w2)(w2.name, w2.M, w2.N, w2.dtype, w2.seed, ("y",),
-                          w2.desc)
-            ms2 = measure(w2, steps, warmup, path, op=op, streams=2)[0]
-            b2 = algorithmic_bytes(w2, resolved, 0, op)
-            rec["two_stream"] = {
-                "GBps": round(b2 / (ms2 * 1e-3) / 1e9, 1),
-                "pct_of_peak": round(100.0 * b2 / (ms2 * 1e-3) / 1e9 /
-                                     PEAK_GBS, 2),
-                "ms_per_step": round(ms2, 6),
-                "note": "independent steps alternate over two streams (y "
-                        "only); not the headline"}
     if "copy" in ceil:
         # the in-tree copy kernel in this launch shape: x read, y written
         rec["copy_ceiling_GBps"] = ceil["copy"]["GBps"]

@@ -114,7 +114,10 @@ typedef enum {
     OS_PATH_SPLIT = 3
 } os_path;
 
-/* Softmax forward.
+/* Softmax forward: both passes of "5.2 CUDA Online Softmax 实现优化" §2.2
+ * (pass 1 folds each row into its running state (m, d) by the recurrence of
+ * §2.1, partial states combining by the merge of §4.1; pass 2 writes
+ * y = e^(x - m) / d), on the path os_softmax_select_path picks.
  *  x        [M, ld_x] input, dtype dt (read only).
  *  y        [M, ld_y] output, dtype dt.
  *  m_out, d_out, lse_out  nullable fp32 [M]: the row's (m, d) as defined
