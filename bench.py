@@ -637,7 +637,11 @@ def run_workload(name, steps, warmup, path="auto", want_cpu=True,
                           op=op, causal=causal)[0]
     nbytes = algorithmic_bytes(w, resolved, n_stats, op, causal)
     gbs = nbytes / (ms * 1e-3) / 1e9
-    eff = (2 * w.M * w.N * w.esize + 4 * w.M * n_stats) / (ms * 1e-3) / 1e9
+    # the single-read minimum: x once and y once (x once for the read-only
+    # passes), and the row statistics
+    read_only = op in ("stats", "cross_entropy")
+    eff = ((1 if read_only else 2) * w.M * w.N * w.esize + 4 * w.M * n_stats) \
+        / (ms * 1e-3) / 1e9
     opname = {"softmax": "softmax", "log_softmax": "log-softmax",
               "cross_entropy": "cross-entropy",
               "stats": "row statistics (m, d, lse)",
@@ -709,13 +713,16 @@ def run_workload(name, steps, warmup, path="auto", want_cpu=True,
             rec["per_launch_us"] = dist
         rec["warm_cache_GBps"] = round(nbytes / (warm_ms * 1e-3) / 1e9, 1)
         rec["graph_replay_GBps"] = round(nbytes / (graph_ms * 1e-3) / 1e9, 1)
-    if "copy" in ceil:
-        # the in-tree copy kernel in this launch shape: x read, y written
-        rec["copy_ceiling_GBps"] = ceil["copy"]["GBps"]
+    # the ceiling kernel of the same bytes: the copy (x read, y written), or
+    # for the read-only passes the read-only kernel, in the resident
+    # kernel's launch shape; and the best copy over the shapes tried
+    ck = "read" if read_only else "copy"
+    if ck in ceil:
+        rec["copy_ceiling_GBps"] = ceil[ck]["GBps"]
+        rec["roofline"]["ceiling_kernel"] = ck
         rec["roofline"]["frac_of_copy_ceiling"] = round(
-            ceil["copy"]["us"] / (ms * 1e3) * nbytes / ceil["copy"]["bytes"], 4)
-    if "best_copy" in ceil:
-        # the fastest one-launch copy of these bytes over the shapes tried
+            ceil[ck]["us"] / (ms * 1e3) * nbytes / ceil[ck]["bytes"], 4)
+    if "best_copy" in ceil and not read_only:
         rec["roofline"]["frac_of_best_copy"] = round(
             ceil["best_copy"]["us"] / (ms * 1e3) * nbytes / (2 * w.M * w.N * w.esize), 4)
     if "launch_floor" in ceil:

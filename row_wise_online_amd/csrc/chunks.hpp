@@ -8,9 +8,9 @@
 
 namespace os {
 
-// Row kernels use at most 512 threads per row (the split path 256 per chunk
-// of a row, P chunks only when rows are few), so 2^22 rows per launch stay
-// under 2^31 work-items.
+// Row kernels use at most 512 threads per row (the split path 512 per chunk
+// of a row, P > 1 chunks only when rows are fewer than 2 per CU), so 2^22
+// rows per launch keep a launch within 2^31 work-items.
 constexpr int64_t kMaxRowsPerLaunch = int64_t(1) << 22;
 
 // Attention workgroups have 512 threads: at most 2^22 per launch.

@@ -7,7 +7,11 @@
 namespace os {
 namespace {
 
-constexpr int kSplitWaves = 4;
+// 8 waves per chunk workgroup (a 128 KiB fp32 chunk is two 64 KiB tiles):
+// fp32 16 x 4194304 softmax 119.0 us and statistics 43.7 us, against 123.1
+// and 44.6 us with 4 waves (MI355X, 8 rotating buffer sets); a plan of 4x
+// the workgroups, or tiles of a whole chunk, were slower.
+constexpr int kSplitWaves = 8;
 constexpr int kMergeRows = 4;          // rows (wavefronts) per merge workgroup
 
 // Temporal pass-1 loads leave x in the Infinity Cache for the normalise
