@@ -44,7 +44,11 @@ void run_persistent(const FwdArgs &a) {
 // medians on cold buffers): one 64-thread workgroup per row up to 1024
 // columns (bf16 32768 x 1024: 5.87 TB/s); 8 waves x 8 values per lane for
 // 4096 columns (fp32: 5.9 TB/s, ahead of 4 x 16 and 2 x 32); 8 waves x 64
-// values per lane, persistent, for 32768 columns (fp32: 6.07 TB/s).
+// values per lane, persistent, for 32768 columns (fp32: 6.07 TB/s).  Shapes
+// with more waves and fewer values per lane were slower for log-softmax
+// too (fp32 4096 columns: 16 x 4 32.5 us, 4 x 16 24.1 us against 23.9 us;
+// bf16 1024 columns: 2 x 8 30.5 us against 23.6 us), except the longest
+// rows (below).
 template <class Tr, bool VEC, Out OUT, bool CE = false, bool MK = false>
 void dispatch(const FwdArgs &a) {
     const int N = a.N;
@@ -63,6 +67,11 @@ void dispatch(const FwdArgs &a) {
         run<Tr, VEC, 8, 16, OUT, CE, MK>(a);
     } else if (N <= 16384) {
         run<Tr, VEC, 8, 32, OUT, CE, MK>(a);
+    } else if constexpr (OUT == Out::LogProb) {
+        // the r-form fold keeps x and more temporaries live: 16 waves of 32
+        // values per lane (fp32 1024 x 32768 log-softmax 44.2 us against
+        // 46.1 us with 8 waves of 64; softmax is 2 us slower this way)
+        run_persistent<Tr, VEC, 16, 32, OUT, CE, MK>(a);
     } else {
         run_persistent<Tr, VEC, 8, 64, OUT, CE, MK>(a);
     }
