@@ -57,8 +57,8 @@ def kernel_source_hash(family="softmax"):
         is_attn = name.startswith("attention")
         if family == "softmax" and is_attn:
             continue
-        if family == "attention" and not (is_attn or name in ("common.hpp",
-                                                              "chunks.hpp")):
+        if family == "attention" and not (is_attn or name in (
+                "common.hpp", "chunks.hpp", "launch.hpp", "plan.hpp")):
             continue
         with open(p, "rb") as f:
             h.update(name.encode())
