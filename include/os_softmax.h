@@ -69,11 +69,22 @@
 
 #include <hip/hip_runtime_api.h>
 
+/* In C++ the enums below take int, the type of a C enum's values, as their
+ * fixed underlying type: then every int a C caller passes is a value of the
+ * enum type, which the library checks and rejects with a status when it is
+ * not one of the enumerators (without a fixed type, C++ leaves values
+ * outside the enumerators' bit range undefined). */
+#ifdef __cplusplus
+#define OS_ENUM_BASE : int
+#else
+#define OS_ENUM_BASE
+#endif
+
 #ifdef __cplusplus
 extern "C" {
 #endif
 
-typedef enum {
+typedef enum OS_ENUM_BASE {
     OS_OK = 0,
     OS_ERR_NULL = 1,        /* a required pointer is NULL */
     OS_ERR_SHAPE = 2,       /* M < 0 or M > 2^31-1, N < 1 or N > 2^30, K < 1 */
@@ -88,7 +99,7 @@ typedef enum {
                                os_softmax_plan: cu_count < 1 */
 } os_status;
 
-typedef enum { OS_F32 = 0, OS_BF16 = 1 } os_dtype;
+typedef enum OS_ENUM_BASE { OS_F32 = 0, OS_BF16 = 1 } os_dtype;
 
 /* Execution paths.
  *  RESIDENT: each row is loaded once into registers, reduced, and
@@ -107,7 +118,7 @@ typedef enum { OS_F32 = 0, OS_BF16 = 1 } os_dtype;
  *  AUTO:     choose by shape: os_softmax_select_path for the softmax and
  *            log-softmax entry points, os_softmax_stats_select_path for
  *            the statistics and cross-entropy ones. */
-typedef enum {
+typedef enum OS_ENUM_BASE {
     OS_PATH_AUTO = 0,
     OS_PATH_RESIDENT = 1,
     OS_PATH_STREAM = 2,
