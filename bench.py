@@ -254,13 +254,15 @@ def measure(w, steps, warmup, path="auto", rotate=True, graph=False,
     return ms, R, host_us, dist, outs
 
 
-def resident_shape(w):
+def resident_shape(w, read_only=False):
     """(waves, 16-byte vectors per lane) of the resident kernel the library
     launches for this row length and dtype (one workgroup per row), if the
-    row is a whole number of its tiles; else None."""
+    row is a whole number of its tiles; else None.  read_only: the shape of
+    the statistics / cross-entropy pass (2 waves x 32 at 4096 columns)."""
     E = 4 if w.dtype == "f32" else 8          # elements per 16-byte vector
     ladder = [(256, 1, 4), (512, 1, 8), (1024, 1, 16), (2048, 4, 8),
-              (4096, 8, 8), (8192, 8, 16), (16384, 8, 32), (32768, 8, 64)]
+              (4096, 2 if read_only else 8, 32 if read_only else 8),
+              (8192, 8, 16), (16384, 8, 32), (32768, 8, 64)]
     for n_max, waves, epl in ladder:
         if w.N <= n_max:
             if epl % E or w.N * w.esize != 16 * 64 * waves * (epl // E):
@@ -269,11 +271,12 @@ def resident_shape(w):
     return None
 
 
-def ceiling_shape(w):
+def ceiling_shape(w, read_only=False):
     """Rows, row bytes, waves and vectors per lane of the ceiling kernels for
-    workload w: the resident kernel's launch shape when it tiles the row
-    exactly, else x cut into 128 KiB rows (512 lanes x 16 vectors)."""
-    rs = resident_shape(w)
+    workload w: the resident kernel's launch shape (of the read-only passes
+    with read_only) when it tiles the row exactly, else x cut into 128 KiB
+    rows (512 lanes x 16 vectors)."""
+    rs = resident_shape(w, read_only)
     nbytes = w.M * w.N * w.esize
     if rs is not None:
         waves, spl = rs
@@ -342,7 +345,7 @@ COPY_SHAPES = [(1, 1), (1, 2), (1, 4), (1, 8), (1, 16), (4, 1), (4, 2), (4, 4),
                (4, 8), (8, 1), (8, 2), (8, 4), (8, 8), (8, 16)]
 
 
-def ceilings(w, steps=200, warmup=400, trials=20, full=True):
+def ceilings(w, steps=200, warmup=400, trials=20, full=True, read_only=False):
     """What this device reaches on the bytes of one softmax launch of
     workload w, cold (buffer sets rotating over >= 1 GiB), with no
     arithmetic: the in-tree copy, read-only and write-only kernels in the
@@ -351,11 +354,12 @@ def ceilings(w, steps=200, warmup=400, trials=20, full=True):
     the runtime's device-to-device copy, torch's copy, and the launch floor
     (an empty kernel back to back, one workgroup and the workload's grid).
     full=False: the same-shape copy alone (the counters' calibration
-    kernel in profiler runs)."""
+    kernel in profiler runs).  read_only: the launch shape of the
+    statistics / cross-entropy pass in place of the softmax's."""
     import torch
     import ceiling
     lib = ceiling.load()
-    shape = ceiling_shape(w)
+    shape = ceiling_shape(w, read_only)
     nbytes = w.M * w.N * w.esize
     R = max(2, -(-ROTATE_BYTES // (2 * nbytes)))
     src = [torch.full((nbytes // 4,), 1.0, device="cuda") for _ in range(R)]
@@ -625,7 +629,9 @@ def run_workload(name, steps, warmup, path="auto", want_cpu=True,
         raise ValueError("the causal mask applies to softmax / log-softmax")
     # the ceilings first: they also bring the clocks up from idle before
     # the timed steps
-    ceil = ceilings(w) if extras else ceilings(w, 50, 10, 0, full=False)
+    ro = op in ("stats", "cross_entropy")
+    ceil = (ceilings(w, read_only=ro) if extras
+            else ceilings(w, 50, 10, 0, full=False, read_only=ro))
     ms, R, host_us, dist, outs = measure(w, steps, warmup, path, op=op,
                                          causal=causal,
                                          trials=20 if extras else 0,

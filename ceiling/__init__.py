@@ -12,7 +12,7 @@ LIB_PATH = os.path.join(_HERE, "libos_ceiling.so")
 
 # the launch shapes the kernels are built for (ceiling.hip): waves per
 # workgroup and 16-byte vectors per lane
-WAVES = (1, 4, 8)
+WAVES = (1, 2, 4, 8)
 VECTORS_PER_LANE = (1, 2, 4, 8, 16)
 
 _lib = None

@@ -105,6 +105,7 @@ int run(Op op, const void *src, void *dst, int64_t rows, int64_t row_bytes,
     bool ok;
     switch (waves) {
         case 1: ok = by_spl<1>(op, spl, src, dst, rows, pitch, s); break;
+        case 2: ok = by_spl<2>(op, spl, src, dst, rows, pitch, s); break;
         case 4: ok = by_spl<4>(op, spl, src, dst, rows, pitch, s); break;
         case 8: ok = by_spl<8>(op, spl, src, dst, rows, pitch, s); break;
         default: ok = false;
@@ -118,7 +119,7 @@ int run(Op op, const void *src, void *dst, int64_t rows, int64_t row_bytes,
 extern "C" {
 
 // src and dst: rows x pitch_bytes, row_bytes = 16 * 64 * waves * spl of
-// each row moved; waves in {1, 4, 8}, spl in {1, 2, 4, 8, 16}.
+// each row moved; waves in {1, 2, 4, 8}, spl in {1, 2, 4, 8, 16}.
 int ceil_copy(const void *src, void *dst, int64_t rows, int64_t row_bytes,
               int64_t pitch_bytes, int waves, int spl, hipStream_t s) {
     return run(kCopy, src, dst, rows, row_bytes, pitch_bytes, waves, spl, s);

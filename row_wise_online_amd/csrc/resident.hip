@@ -43,7 +43,10 @@ void run_persistent(const FwdArgs &a) {
 // Variant ladder by row length (elements), measured on MI355X (interleaved
 // medians on cold buffers): one 64-thread workgroup per row up to 1024
 // columns (bf16 32768 x 1024: 5.87 TB/s); 8 waves x 8 values per lane for
-// 4096 columns (fp32: 5.9 TB/s, ahead of 4 x 16 and 2 x 32); 8 waves x 64
+// 4096 columns (fp32: 5.9 TB/s, ahead of 4 x 16 and 2 x 32), except for
+// the read-only passes, which write nothing per element and take 2 x 32
+// (fp32 4096 x 4096 statistics 11.8 us against 12.1 us, cross-entropy
+// 14.1 against 14.5 us; 4 x 16 11.9 and 14.1-14.2 us); 8 waves x 64
 // values per lane, persistent, for 32768 columns (fp32: 6.07 TB/s).  Shapes
 // with more waves and fewer values per lane were slower for log-softmax
 // too (fp32 4096 columns: 16 x 4 32.5 us, 4 x 16 24.1 us against 23.9 us;
@@ -62,7 +65,8 @@ void dispatch(const FwdArgs &a) {
     } else if (N <= 2048) {
         run<Tr, VEC, 4, 8, OUT, CE, MK>(a);
     } else if (N <= 4096) {
-        run<Tr, VEC, 8, 8, OUT, CE, MK>(a);
+        if constexpr (OUT == Out::None) run<Tr, VEC, 2, 32, OUT, CE, MK>(a);
+        else run<Tr, VEC, 8, 8, OUT, CE, MK>(a);
     } else if (N <= 8192) {
         run<Tr, VEC, 8, 16, OUT, CE, MK>(a);
     } else if (N <= 16384) {

@@ -68,12 +68,18 @@ def test_launch_shapes_of_the_workloads():
     assert bench.resident_shape(W["c5"]) is None
     assert bench.ceiling_shape(W["c2"]) == (4096, 16384, 8, 2)
     assert bench.ceiling_shape(W["c3"]) == (32768, 2048, 1, 2)
+    # the read-only passes take 2 waves x 8 vectors at 4096 fp32 columns
+    assert bench.resident_shape(W["c2"], read_only=True) == (2, 8)
+    assert bench.ceiling_shape(W["c2"], read_only=True) == (4096, 16384, 2, 8)
+    assert bench.resident_shape(W["c3"], read_only=True) == (1, 2)
     # long rows: x cut into 128 KiB rows
     assert bench.ceiling_shape(W["c5"]) == (2048, 131072, 8, 16)
     for name in ("c2", "c3", "c4", "c5"):
-        rows, rb, waves, spl = bench.ceiling_shape(W[name])
-        assert rb == 16 * 64 * waves * spl
-        assert rows * rb == W[name].M * W[name].N * W[name].esize
+        for ro in (False, True):
+            rows, rb, waves, spl = bench.ceiling_shape(W[name], read_only=ro)
+            assert rb == 16 * 64 * waves * spl
+            assert rows * rb == W[name].M * W[name].N * W[name].esize
+            assert waves in ceiling.WAVES and spl in ceiling.VECTORS_PER_LANE
 
 
 def test_sweep_shapes_are_built():
