@@ -36,6 +36,33 @@ def lib():
     return _lib.load()
 
 
+@pytest.mark.parametrize("lang", ["c", "c++"])
+def test_headers_compile_as_c_and_cxx(tmp_path, lang):
+    # the ABI is for C callers as well as C++: both headers, every type and
+    # enumerator, compile warning-free in either language
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc" if lang == "c" else "g++")
+    if cc is None or not os.path.isdir("/opt/rocm/include"):
+        pytest.skip("no host compiler or ROCm headers")
+    src = tmp_path / ("abi.c" if lang == "c" else "abi.cpp")
+    src.write_text(
+        '#include "os_softmax.h"\n#include "os_attention.h"\n'
+        "int main(void) {\n"
+        "    os_dtype d = OS_BF16; os_path p = OS_PATH_SPLIT;\n"
+        "    os_status s = OS_ERR_DEVICE; os_plan pl;\n"
+        "    pl.path = p; pl.chunks_per_row = 1; pl.chunk_len = 1;\n"
+        "    pl.workspace_bytes = 0;\n"
+        "    return (int)d + (int)p + (int)s + (int)pl.chunk_len - 16;\n"
+        "}\n")
+    std = "-std=c11" if lang == "c" else "-std=c++17"
+    r = subprocess.run([cc, std, "-Wall", "-Wextra", "-Werror", "-fsyntax-only",
+                        "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include",
+                        "-I" + os.path.join(ROOT, "include"), str(src)],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+
+
 def test_exports_every_declared_symbol(lib):
     declared = _declared_functions()
     assert declared, "no declarations found"
