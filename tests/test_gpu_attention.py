@@ -321,6 +321,18 @@ def _sample_rows(Sq, seed):
     return sorted(set(fixed) | set(rng.integers(0, Sq, 14).tolist()))
 
 
+@pytest.mark.parametrize("D,causal", [(32, -1), (64, -1), (128, -1), (128, 0),
+                                      (64, 1000)])
+def test_4096_square_every_row(D, causal):
+    # one head of 4096 queries x 4096 keys: 16 query blocks (8 workgroups
+    # under the causal pairing) over 64 key tiles (32 at d = 32), every row
+    # and every output element against the fp64 oracle, bf16 O
+    q, k, v = wl.attention_inputs(1, 1, 4096, 4096, D, seed=4096 + D + causal)
+    print(f"4096^2 every row D={D} causal={causal}", flush=True)
+    o, lse = run(q, k, v, causal=causal)
+    check(q, k, v, o, lse, causal=causal, what=f"4096^2 D{D} c{causal}")
+
+
 @pytest.mark.parametrize("D", [32, 64, 128])
 @pytest.mark.parametrize("causal", [-1, 0, 700])
 def test_many_heads_medium_sampled(D, causal):
