@@ -267,3 +267,44 @@ def test_most_rows():
     assert bool((bits[::3] == -(1 << 31)).all())        # -0.0
     assert bool((bits[1::3] == 0).all()) and bool((bits[2::3] == 0).all())
     assert mean.item() == 0.0
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_row_stride_beyond_32_bits(dtype):
+    # three rows 2^31 + 16 elements apart (the last one starts 2^32 + 32
+    # elements, 16 or 8 GiB, into the buffer): every row offset must be
+    # formed in 64 bits, on every path and entry point.  Only the rows'
+    # first N columns are written; the rest of the buffer is never read.
+    M3, N3, ld = 3, 1000, (1 << 31) + 16
+    x_h = wl.normal(M3, N3, scale=3.0, seed=903, dtype=dtype)
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    print(f"row stride {ld} {dtype}: {M3} rows of {N3}", flush=True)
+    buf = torch.empty(M3 * ld, dtype=tdt, device="cuda")
+    x = buf.view(M3, ld)[:, :N3]
+    x.copy_(to_device(x_h))
+    try:
+        _, m_ref, d_ref, l_ref = oracle.softmax(x_h, want_y=False)
+        y_ref = oracle.softmax(x_h)[0]
+        for path in ("resident", "stream", "split"):
+            what = f"stride {ld} {dtype} {path}"
+            m, d, lse = (torch.empty(M3, device="cuda") for _ in range(3))
+            y = rw.softmax_fwd(x, m=m, d=d, lse=lse, path=path)
+            ly = rw.log_softmax_fwd(x, path=path)
+            torch.cuda.synchronize()
+            check_y(to_host(y), y_ref, what)
+            check_log(to_host(ly), oracle.log_softmax(x_h), what)
+            check_m(m.cpu().numpy(), m_ref, what)
+            check_d(d.cpu().numpy(), d_ref, what)
+            check_lse(lse.cpu().numpy(), l_ref, what)
+            m2, d2 = (torch.empty(M3, device="cuda") for _ in range(2))
+            rw.softmax_stats(x, m2, d2, path=path)
+            torch.cuda.synchronize()
+            check_m(m2.cpu().numpy(), m_ref, what + " stats")
+            check_d(d2.cpu().numpy(), d_ref, what + " stats")
+        # pass 2 alone, in place, on the strided rows
+        rw.softmax_normalize(x, m2, d2, x)
+        torch.cuda.synchronize()
+        check_y(to_host(x), y_ref, f"stride {ld} {dtype} normalize in place")
+    finally:
+        del x, buf
+        torch.cuda.empty_cache()
