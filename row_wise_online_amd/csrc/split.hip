@@ -10,7 +10,9 @@ namespace {
 // 8 waves per chunk workgroup (a 128 KiB fp32 chunk is two 64 KiB tiles):
 // fp32 16 x 4194304 softmax 119.0 us and statistics 43.7 us, against 123.1
 // and 44.6 us with 4 waves (MI355X, 8 rotating buffer sets); a plan of 4x
-// the workgroups, or tiles of a whole chunk, were slower.
+// the workgroups, or tiles of a whole chunk, were slower.  Chunks shorter
+// than one such tile (rows of a few thousand elements on a forced split
+// path) take 4 waves or 1, so that a tile is not mostly past the chunk's end.
 constexpr int kSplitWaves = 8;
 constexpr int kMergeRows = 4;          // rows (wavefronts) per merge workgroup
 
@@ -42,24 +44,23 @@ WsLayout layout(void *ws, int64_t M, int P) {
     return l;
 }
 
-template <class Tr, bool VEC, class Pol, bool MK>
-void run(const FwdArgs &a, void *ws) {
+template <class Tr, bool VEC, class Pol, bool MK, int WAVES>
+void run(const FwdArgs &a, void *ws, const SplitPlan &plan) {
     using E = typename Tr::elem_t;
     constexpr int U = tile_slots<Tr, VEC>();
-    const SplitPlan plan = split_plan(a.M, a.N, a.cus);
     const WsLayout l = layout(ws, a.M, plan.P);
     const dim3 grid(static_cast<unsigned>(a.M * plan.P));
-    const dim3 block(kWave * kSplitWaves);
+    const dim3 block(kWave * WAVES);
     const E *x = static_cast<const E *>(a.x);
 
     const Mask mk{a.row_len, a.causal};
     // log-softmax keeps r = d - 1; softmax, statistics and cross-entropy d
     if (a.mode != Mode::LogProb) {
-        split_partial_kernel<Tr, VEC, kSplitWaves, U, Pol, MK, false>
+        split_partial_kernel<Tr, VEC, WAVES, U, Pol, MK, false>
             <<<grid, block, 0, a.stream>>>(x, a.ldx, a.N, plan.P, plan.C,
                                            l.part_m, l.part_d, mk);
     } else {
-        split_partial_kernel<Tr, VEC, kSplitWaves, U, Pol, MK, true>
+        split_partial_kernel<Tr, VEC, WAVES, U, Pol, MK, true>
             <<<grid, block, 0, a.stream>>>(x, a.ldx, a.N, plan.P, plan.C,
                                            l.part_m, l.part_d, mk);
     }
@@ -87,21 +88,34 @@ void run(const FwdArgs &a, void *ws) {
     // itself and writes the requested statistics
     E *y = static_cast<E *>(a.y);
     if (a.mode == Mode::Prob) {
-        split_normalize_kernel<Tr, VEC, kSplitWaves, U, Out::Prob, Pol, MK>
+        split_normalize_kernel<Tr, VEC, WAVES, U, Out::Prob, Pol, MK>
             <<<grid, block, 0, a.stream>>>(x, a.ldx, y, a.ldy, a.N, plan.P, plan.C,
                                            l.part_m, l.part_d, so, mk);
     } else {
-        split_normalize_kernel<Tr, VEC, kSplitWaves, U, Out::LogProb, Pol, MK>
+        split_normalize_kernel<Tr, VEC, WAVES, U, Out::LogProb, Pol, MK>
             <<<grid, block, 0, a.stream>>>(x, a.ldx, y, a.ldy, a.N, plan.P, plan.C,
                                            l.part_m, l.part_d, so, mk);
     }
 }
 
+// Waves per chunk workgroup: kSplitWaves, unless the chunk (at most the
+// row) is shorter than such a workgroup's tile of 64 lanes x U slots per
+// wave.
+template <class Tr, bool VEC, class Pol, bool MK>
+void by_waves(const FwdArgs &a, void *ws) {
+    const SplitPlan plan = split_plan(a.M, a.N, a.cus);
+    const int64_t len = plan.C < a.N ? plan.C : a.N;
+    const int64_t tile = int64_t(kWave) * tile_slots<Tr, VEC>() * (VEC ? Tr::E : 1);
+    if (len >= kSplitWaves * tile) run<Tr, VEC, Pol, MK, kSplitWaves>(a, ws, plan);
+    else if (len >= 4 * tile) run<Tr, VEC, Pol, MK, 4>(a, ws, plan);
+    else run<Tr, VEC, Pol, MK, 1>(a, ws, plan);
+}
+
 template <class Tr, bool VEC>
 void by_mode(const FwdArgs &a, void *ws) {
-    if (a.mode == Mode::Stats) run<Tr, VEC, StatsPolicy, false>(a, ws);
-    else if (a.masked()) run<Tr, VEC, SplitPolicy, true>(a, ws);
-    else run<Tr, VEC, SplitPolicy, false>(a, ws);
+    if (a.mode == Mode::Stats) by_waves<Tr, VEC, StatsPolicy, false>(a, ws);
+    else if (a.masked()) by_waves<Tr, VEC, SplitPolicy, true>(a, ws);
+    else by_waves<Tr, VEC, SplitPolicy, false>(a, ws);
 }
 
 }  // namespace
