@@ -27,18 +27,28 @@ constexpr int tile_slots() {
     return VEC ? 32 / Tr::E : 16;
 }
 
-template <class Tr, bool VEC, Out OUT, class Pol, bool CE = false,
-          bool MK = false>
-void run(const FwdArgs &a) {
+template <class Tr, bool VEC, Out OUT, class Pol, bool CE, bool MK, int WAVES>
+void launch_waves(const FwdArgs &a) {
     using E = typename Tr::elem_t;
     constexpr int U = tile_slots<Tr, VEC>();
-    constexpr int WAVES = OUT == Out::None ? kStatsWaves : kStreamWaves;
     const StatsOut so{a.m_out, a.d_out, a.lse_out, a.inc_out, a.labels, a.loss,
                       a.accumulate};
     stream_kernel<Tr, VEC, WAVES, U, OUT, Pol, CE, MK>
         <<<dim3(static_cast<unsigned>(a.M)), dim3(kWave * WAVES), 0, a.stream>>>(
             static_cast<const E *>(a.x), a.ldx, static_cast<E *>(a.y), a.ldy,
             a.N, so, Mask{a.row_len, a.causal});
+}
+
+// Rows shorter than one tile of the full workgroup (only on a stream path
+// forced onto short rows; AUTO streams rows of more than 16384 elements)
+// take a single wavefront, so that a tile is not mostly past the row's end.
+template <class Tr, bool VEC, Out OUT, class Pol, bool CE = false,
+          bool MK = false>
+void run(const FwdArgs &a) {
+    constexpr int WAVES = OUT == Out::None ? kStatsWaves : kStreamWaves;
+    constexpr int64_t kTile = int64_t(kWave) * WAVES * tile_slots<Tr, VEC>() * (VEC ? Tr::E : 1);
+    if (a.N >= kTile) launch_waves<Tr, VEC, OUT, Pol, CE, MK, WAVES>(a);
+    else launch_waves<Tr, VEC, OUT, Pol, CE, MK, 1>(a);
 }
 
 template <class Tr, bool VEC>
