@@ -2,7 +2,8 @@
 the C ABI), against os_softmax_fwd_path with a caller-allocated workspace
 on the same inputs: the same kernels and plan, so the results must be
 bit-identical, and both within the oracle's bar.  Two calls in a row, the
-second on a smaller input, reuse the device's fixed array."""
+second on a smaller input, reuse the device's fixed array; a HIP graph that
+captures the call replays it on new inputs."""
 import numpy as np
 import pytest
 
@@ -93,3 +94,47 @@ def test_plan_beyond_the_array_is_refused():
     rw.softmax_fwd_noalloc(x, y)
     torch.cuda.synchronize()
     assert bool((y == 1.0 / N).all())
+
+
+def test_graph_capture_and_replay():
+    # the callers this entry point is for: a HIP graph captures the call
+    # (it allocates nothing, and the split path's scratch is the fixed
+    # array), and each replay on new inputs gives the bits of the eager call
+    # with a caller workspace
+    M, N = 8, 300001
+    assert rw.select_path(M, N, "f32") == "split"
+    x = torch.empty(M, N, device="cuda")
+    y = torch.empty_like(x)
+    st = [torch.empty(M, device="cuda") for _ in range(3)]
+
+    def fill(seed):
+        x.copy_(torch.from_numpy(wl.normal(M, N, scale=3.0, seed=seed)))
+
+    fill(80)
+    # one eager call first, as a caller warms up before capturing: the
+    # device's array address is read on the first call on a device
+    rw.softmax_fwd_noalloc(x, y, m=st[0], d=st[1], lse=st[2])
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        rw.softmax_fwd_noalloc(x, y, m=st[0], d=st[1], lse=st[2])
+    for i, seed in enumerate((81, 82, 83)):
+        fill(seed)
+        eager = _pair(x, "auto")[1]
+        want_y, want = eager[0], eager[1:]
+        for t in (y, *st):
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, want_y), f"replay {i}: y differs from the eager call"
+        for a, b in zip(st, want):
+            assert torch.equal(a, b), f"replay {i}: a row statistic differs"
+        if i == 0:
+            x_h = wl.normal(M, N, scale=3.0, seed=seed)
+            y_ref, m_ref, d_ref, l_ref = oracle.softmax(x_h)
+            check_y(to_host(y), y_ref, "graph replay")
+            check_m(st[0].cpu().numpy(), m_ref, "graph replay")
+            check_d(st[1].cpu().numpy(), d_ref, "graph replay")
+            check_lse(st[2].cpu().numpy(), l_ref, "graph replay")
